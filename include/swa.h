@@ -1,0 +1,181 @@
+/*
+ * swa.h — C ABI of libswa: causal sliding-window attention (SWA) with
+ * grouped-query heads (GQA), a rolling-buffer KV cache, chunked prefill and
+ * single-token decode, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of Mistral 7B as described by the pages
+ *   "Mistral 7B — 슬라이딩 윈도우 어텐션 중심 정리"            (digest)
+ *   "[arXiv 2310.06825] Mistral 7B: 슬라이딩 윈도우 어텐션과 ..." (essay)
+ *   "Mistral 7B: Engineering Extreme Efficiency in LLMs"         (explainer)
+ *   "LLM 추론용 SWA는 ... 캐시를 무한히 키우지 않는 기술에 가깝다" (sinks)
+ *
+ * WINDOW CONVENTION (fixed).  A query at absolute position i attends the key
+ * at absolute position j iff
+ *       0 <= j <= i   and   ( i - window < j   or   j < n_sink )
+ * i.e. `window` keys including itself, plus the first n_sink positions
+ * (attention sinks).  Digest "핵심 구성요소" / explainer How It Works 2 give
+ * the SWA mask; this is its reading that matches a window-slot buffer that is
+ * written before it is read (digest "Rolling Buffer KV Cache 동작 설명":
+ * the query at p reads p-W+1 .. p).  The sink prefix follows the sinks page,
+ * "왜 단순 sliding window만으로는 부족한가".
+ *
+ * CACHE SLOT of position p (digest "쓰기(write) 단계"; explainer How It
+ * Works 3: slot = p mod W):
+ *       slot(p) = p < n_sink ? p : n_sink + (p - n_sink) % window
+ * A cache holds S = n_sink + window slots per sequence.
+ *
+ * GQA: query head h uses KV head h / (n_q_heads / n_kv_heads) (explainer
+ * How It Works 1: subsets of query heads share one K/V head; contiguous
+ * subsets).
+ *
+ * RoPE (digest "Methods": theta = 10000): element pair (2k, 2k+1) of a head
+ * vector at position p is rotated counter-clockwise by p * theta^(-2k/D).
+ * Queries are rotated at their position, keys at their original position.
+ * rope_theta == 0 disables it.  Angles are formed in double precision and
+ * reduced to [-pi, pi] before a float sine/cosine; the rotation is float.
+ *
+ * LAYOUTS (row-major, contiguous, element type = params.dtype):
+ *   q, out   : [batch][n_tok][n_q_heads][head_dim]     (prefill)
+ *              [batch][n_q_heads][head_dim]            (decode)
+ *   k, v     : [batch][n_tok][n_kv_heads][head_dim]    (raw, un-rotated)
+ *   k_cache, v_cache : [batch][n_sink + window][n_kv_heads][head_dim]
+ *              k_cache holds rotated keys, v_cache the values verbatim.
+ *   lse      : float32 [batch][n_q_heads][n_tok] (prefill), [batch][n_q_heads]
+ *              (decode): natural-log sum of exp of the scaled scores.
+ *   start_pos / pos : int32 [batch], device memory.
+ * All pointers are DEVICE pointers except `params`, which is host memory.
+ *
+ * OWNERSHIP: the caller allocates and owns every buffer, including the
+ * workspaces whose sizes the *_workspace_bytes functions return.  The library
+ * keeps no state between calls and allocates nothing; calls on different
+ * streams with disjoint buffers may run concurrently.
+ *
+ * ERRORS: arguments are checked on the host before any HIP call; a bad
+ * argument returns a negative swa_status and launches nothing.  A failed
+ * launch returns SWA_ERR_LAUNCH.  Work is asynchronous on `stream`; kernel
+ * faults surface on the stream like any HIP error.  Position values are
+ * device data and are trusted: a negative position, or one >= 2^30, is
+ * undefined behaviour.
+ *
+ * PRECISION: bf16 inputs are multiplied on the matrix cores with float32
+ * accumulation; softmax statistics are float32; outputs are rounded once to
+ * the output type.  The float32 dtype runs float32 arithmetic throughout.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swa_status {
+  SWA_OK = 0,
+  SWA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  SWA_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes                */
+  SWA_ERR_DTYPE = -3,       /* unknown dtype                                     */
+  SWA_ERR_UNSUPPORTED = -4, /* valid request this build does not implement        */
+  SWA_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required   */
+  SWA_ERR_LAUNCH = -6       /* a kernel launch failed (hipGetLastError)          */
+} swa_status;
+
+typedef enum swa_dtype { SWA_BF16 = 0, SWA_F32 = 1 } swa_dtype;
+
+typedef struct swa_params {
+  int32_t batch;       /* sequences, >= 1                                       */
+  int32_t n_q_heads;   /* query heads, multiple of n_kv_heads                   */
+  int32_t n_kv_heads;  /* key/value heads, >= 1                                 */
+  int32_t head_dim;    /* 64 or 128                                             */
+  int32_t window;      /* W >= 1: rolling slots; keys i-W < j <= i              */
+  int32_t n_sink;      /* 0 <= n_sink <= 64 sink positions with fixed slots     */
+  float scale;         /* softmax scale; 0 means 1/sqrt(head_dim)               */
+  float rope_theta;    /* RoPE base; 0 disables RoPE                            */
+  int32_t dtype;       /* swa_dtype of q, k, v, out and the caches              */
+} swa_params;
+
+/*
+ * swa_cache_write — rotate keys and scatter a run of tokens into the
+ * rolling buffer.  Digest "쓰기(write) 단계" (slot = p % W; K_buf[slot] = k_p;
+ * V_buf[slot] = v_p), explainer How It Works 3.
+ *   k, v      : [batch][n_tok][n_kv_heads][head_dim] raw keys and values.
+ *   start_pos : device int32[batch]; token t of sequence b has position
+ *               start_pos[b] + t.
+ *   n_tok     : >= 1.
+ *   k_cache, v_cache : caches, updated in place.
+ * Equivalent to writing the tokens one by one in order: when n_tok exceeds
+ * the window, only positions that survive (p >= start+n_tok-window, or sinks)
+ * are written, so every slot has exactly one writer and the result is
+ * deterministic.
+ */
+int swa_cache_write(const swa_params* params, const void* k, const void* v,
+                    const int32_t* start_pos, int32_t n_tok, void* k_cache, void* v_cache,
+                    hipStream_t stream);
+
+/* Bytes of workspace swa_prefill_chunk needs for a chunk of `chunk_len`
+ * tokens (the chunk's rotated keys).  0 on a bad argument. */
+size_t swa_prefill_workspace_bytes(const swa_params* params, int32_t chunk_len);
+
+/*
+ * swa_prefill_chunk — attention of one prefill chunk.  Essay §4.1 and
+ * Figure 3, explainer How It Works 4: the chunk's queries attend causally to
+ * the chunk and, within the window, to what the cache held before the chunk.
+ *   q         : [batch][chunk_len][n_q_heads][head_dim] raw queries.
+ *   k, v      : [batch][chunk_len][n_kv_heads][head_dim] raw keys, values.
+ *   k_cache, v_cache : the caches as they stand before the chunk (positions
+ *               < start_pos[b]); may both be NULL when every start_pos is 0.
+ *   start_pos : device int32[batch], position of the chunk's first token.
+ *   out       : [batch][chunk_len][n_q_heads][head_dim].
+ *   lse       : float32 [batch][n_q_heads][chunk_len], or NULL.
+ *   workspace : >= swa_prefill_workspace_bytes(params, chunk_len) bytes.
+ * Does NOT write the cache: call swa_cache_write(k, v, start_pos, chunk_len)
+ * afterwards on the same stream (digest "Pre-fill과의 상호작용": after each
+ * chunk the buffer holds the last W entries).
+ */
+int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, const void* v,
+                      const void* k_cache, const void* v_cache, const int32_t* start_pos,
+                      int32_t chunk_len, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace swa_decode needs (split-K partial results). */
+size_t swa_decode_workspace_bytes(const swa_params* params);
+
+/*
+ * swa_decode — one decode step per sequence against the rolling buffer.
+ * Digest "읽기(read) 단계": the query at p reads the buffer entries of
+ * positions p-W+1 .. p (plus sinks); digest "Pre-fill과의 상호작용": same
+ * cache convention as prefill.
+ *   q         : [batch][n_q_heads][head_dim] raw queries (rotated at pos[b]).
+ *   k_cache, v_cache : caches that already hold position pos[b] (call
+ *               swa_cache_write with n_tok = 1 first).
+ *   pos       : device int32[batch], position of the token being decoded.
+ *   out       : [batch][n_q_heads][head_dim];  lse: float32 [batch][n_q_heads]
+ *               or NULL.
+ *   workspace : >= swa_decode_workspace_bytes(params) bytes.
+ * Slots whose implied position is negative (fewer than W tokens so far) are
+ * never read.  Deterministic: no atomics.
+ */
+int swa_decode(const swa_params* params, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/* Human-readable name of a swa_status value. */
+const char* swa_status_string(int status);
+
+/* Test hooks: run the same device index functions the kernels use.
+ * swa_debug_slots: slots[t] = slot(positions[t]) for t < n (device arrays).
+ * swa_debug_mask : mask[t] = 1 iff key position k_pos[t] is in the key set of
+ *                  query position q_pos (device arrays). */
+int swa_debug_slots(const swa_params* params, const int32_t* positions, int32_t n,
+                    int32_t* slots, hipStream_t stream);
+int swa_debug_mask(const swa_params* params, int32_t q_pos, const int32_t* k_pos, int32_t n,
+                   uint8_t* mask, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

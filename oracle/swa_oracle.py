@@ -218,7 +218,7 @@ def kv_cache_bytes(n_positions_kept, n_layers, n_kv_heads, head_dim, bytes_per_e
 # ---------------------------------------------------------------------------
 # Schedules: one prefill chunk, one decode step
 # ---------------------------------------------------------------------------
-def prefill_chunk(cache, q, k, v, start, theta=10000.0, scale=None):
+def prefill_chunk(cache, q, k, v, start, theta=10000.0, scale=None, rows=None):
     """One chunk of chunked prefill for one sequence.
 
     q [C, Hq, D], k and v [C, Hkv, D] are the raw (un-rotated) projections of
@@ -227,16 +227,21 @@ def prefill_chunk(cache, q, k, v, start, theta=10000.0, scale=None):
     (essay §4.1 and Figure 3; explainer How It Works 4).  The chunk is written
     to the cache afterwards, so after the call the cache holds the last W
     positions (digest "Pre-fill과의 상호작용").  Returns (out, lse).
+
+    ``rows`` (chunk-relative indices) restricts the attention to those query
+    rows; every query row is independent, so each returned row is the same as
+    in the full evaluation.
     """
     C = q.shape[0]
     pos = np.arange(start, start + C, dtype=np.int64)
-    q_rot = rope(q, pos, theta)
     k_rot = rope(k, pos, theta)
     ck, cv, cpos = cache.entries(below=start)
     keys = np.concatenate([ck, k_rot], axis=0)
     vals = np.concatenate([cv, np.asarray(v, dtype=np.float64)], axis=0)
     kpos = np.concatenate([cpos, pos])
-    out, lse = swa_attention(q_rot, keys, vals, pos, kpos, cache.window, cache.n_sink, scale)
+    sel = np.arange(C) if rows is None else np.asarray(rows, dtype=np.int64)
+    q_rot = rope(np.asarray(q)[sel], pos[sel], theta)
+    out, lse = swa_attention(q_rot, keys, vals, pos[sel], kpos, cache.window, cache.n_sink, scale)
     cache.write(k_rot, np.asarray(v, dtype=np.float64), pos)
     return out, lse
 

@@ -1,0 +1,173 @@
+// swa_api.cpp — the C ABI of libswa (declared in include/swa.h): argument
+// validation on the host, then kernel launches on the caller's stream.  No
+// HIP call is made before every argument has been checked.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/swa.h"
+#include "swa_device.hpp"
+#include "swa_launch.hpp"
+
+namespace {
+
+using swa::RopeTab;
+using swa::Shape;
+
+size_t elem_size(int dtype) { return dtype == SWA_F32 ? 4 : 2; }
+
+// Checks shared by every entry point; fills the kernel-side shape.
+int check_params(const swa_params* p, Shape* sh) {
+  if (!p) return SWA_ERR_NULL;
+  if (p->dtype != SWA_BF16 && p->dtype != SWA_F32) return SWA_ERR_DTYPE;
+  if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1) return SWA_ERR_SHAPE;
+  if (p->n_q_heads % p->n_kv_heads != 0) return SWA_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return SWA_ERR_SHAPE;
+  if (p->window < 1 || p->n_sink < 0 || p->n_sink > 64) return SWA_ERR_SHAPE;
+  if ((long long)p->n_sink + p->window > (1LL << 30)) return SWA_ERR_SHAPE;
+  if (!(p->scale >= 0.f) || !isfinite(p->scale)) return SWA_ERR_SHAPE;
+  if (!(p->rope_theta >= 0.f) || !isfinite(p->rope_theta)) return SWA_ERR_SHAPE;
+  if (sh) {
+    sh->B = p->batch;
+    sh->Hq = p->n_q_heads;
+    sh->Hkv = p->n_kv_heads;
+    sh->D = p->head_dim;
+    sh->W = p->window;
+    sh->n_sink = p->n_sink;
+    sh->S = p->n_sink + p->window;
+    sh->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->head_dim));
+    sh->scale_log2 = (float)((double)sh->scale * 1.4426950408889634);
+    sh->rope = p->rope_theta > 0.f ? 1 : 0;
+  }
+  return SWA_OK;
+}
+
+RopeTab rope_table(const swa_params* p) {
+  RopeTab rt;
+  for (int k = 0; k < swa::kMaxPairs; ++k) rt.freq[k] = 0.0;
+  if (p->rope_theta > 0.f)
+    for (int k = 0; k < p->head_dim / 2; ++k)
+      rt.freq[k] = pow((double)p->rope_theta, -2.0 * k / p->head_dim);
+  return rt;
+}
+
+bool fast_path(const swa_params* p) {
+  return p->dtype == SWA_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int swa_cache_write(const swa_params* params, const void* k, const void* v,
+                    const int32_t* start_pos, int32_t n_tok, void* k_cache, void* v_cache,
+                    hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k || !v || !start_pos || !k_cache || !v_cache) return SWA_ERR_NULL;
+  if (n_tok < 1) return SWA_ERR_SHAPE;
+  if ((long long)sh.B * n_tok * sh.Hkv * (sh.D / 8) >= (1LL << 40)) return SWA_ERR_SHAPE;
+  return launched(swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k, v,
+                                          start_pos, n_tok, k_cache, v_cache, swa::kToCache,
+                                          stream));
+}
+
+size_t swa_prefill_workspace_bytes(const swa_params* params, int32_t chunk_len) {
+  if (check_params(params, nullptr) != SWA_OK || chunk_len < 1) return 0;
+  return (size_t)params->batch * chunk_len * params->n_kv_heads * params->head_dim *
+         elem_size(params->dtype);
+}
+
+int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, const void* v,
+                      const void* k_cache, const void* v_cache, const int32_t* start_pos,
+                      int32_t chunk_len, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k || !v || !start_pos || !out) return SWA_ERR_NULL;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return SWA_ERR_NULL;
+  if (chunk_len < 1 || chunk_len > (1 << 24)) return SWA_ERR_SHAPE;
+  const size_t need = swa_prefill_workspace_bytes(params, chunk_len);
+  if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  const RopeTab rt = rope_table(params);
+  const bool f32 = params->dtype == SWA_F32;
+  // rotated chunk keys -> workspace (values are read as given)
+  hipError_t e = swa::launch_cache_write(sh, rt, f32, k, v, start_pos, chunk_len, workspace,
+                                         nullptr, swa::kToDense, stream);
+  if (e != hipSuccess) return SWA_ERR_LAUNCH;
+  if (fast_path(params))
+    e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, workspace, v, k_cache, v_cache, start_pos,
+                                         chunk_len, out, lse, stream);
+  else
+    e = swa::launch_prefill_generic(sh, rt, f32, q, workspace, v, k_cache, v_cache, start_pos,
+                                    chunk_len, out, lse, stream);
+  return launched(e);
+}
+
+size_t swa_decode_workspace_bytes(const swa_params* params) {
+  Shape sh;
+  if (check_params(params, &sh) != SWA_OK) return 0;
+  const int n = swa::decode_splits(sh);
+  return (size_t)sh.B * sh.Hq * n * (sh.D + 2) * sizeof(float);
+}
+
+int swa_decode(const swa_params* params, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k_cache || !v_cache || !pos || !out) return SWA_ERR_NULL;
+  const size_t need = swa_decode_workspace_bytes(params);
+  if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  const int n = swa::decode_splits(sh);
+  const RopeTab rt = rope_table(params);
+  const bool f32 = params->dtype == SWA_F32;
+  float* part = static_cast<float*>(workspace);
+  hipError_t e;
+  if (fast_path(params))
+    e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, stream);
+  else
+    e = swa::launch_decode_generic(sh, rt, f32, q, k_cache, v_cache, pos, part, n, stream);
+  if (e != hipSuccess) return SWA_ERR_LAUNCH;
+  return launched(swa::launch_decode_combine(sh, f32, part, n, out, lse, stream));
+}
+
+const char* swa_status_string(int status) {
+  switch (status) {
+    case SWA_OK: return "SWA_OK";
+    case SWA_ERR_NULL: return "SWA_ERR_NULL: a required pointer is NULL";
+    case SWA_ERR_SHAPE: return "SWA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case SWA_ERR_DTYPE: return "SWA_ERR_DTYPE: unknown dtype";
+    case SWA_ERR_UNSUPPORTED: return "SWA_ERR_UNSUPPORTED: not implemented for these arguments";
+    case SWA_ERR_WORKSPACE: return "SWA_ERR_WORKSPACE: workspace missing or too small";
+    case SWA_ERR_LAUNCH: return "SWA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown swa_status";
+  }
+}
+
+int swa_debug_slots(const swa_params* params, const int32_t* positions, int32_t n, int32_t* slots,
+                    hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!positions || !slots) return SWA_ERR_NULL;
+  if (n < 1) return SWA_ERR_SHAPE;
+  return launched(swa::launch_debug_slots(sh, positions, n, slots, stream));
+}
+
+int swa_debug_mask(const swa_params* params, int32_t q_pos, const int32_t* k_pos, int32_t n,
+                   uint8_t* mask, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k_pos || !mask) return SWA_ERR_NULL;
+  if (n < 1 || q_pos < 0) return SWA_ERR_SHAPE;
+  return launched(swa::launch_debug_mask(sh, q_pos, k_pos, n, mask, stream));
+}
+
+}  // extern "C"

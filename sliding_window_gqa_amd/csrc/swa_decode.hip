@@ -1,0 +1,397 @@
+// swa_decode.hip — single-token decode against the rolling buffer.
+//
+// Digest page "Rolling Buffer KV Cache 동작 설명", 읽기(read) 단계: the query at
+// position p reads the buffer entries of positions p-W+1 .. p, which sit in
+// at most two contiguous runs of physical slots; the buffer is read in slot
+// order and the position each slot holds is recovered from the slot index and
+// p (slot_position), so slots not yet written (p < W-1) are never used.
+// Reads per token are bounded by the window (essay §3.2, §3.4: decode is
+// bound by cache reads; GQA cuts them 4x).
+//
+// Split-K: the S = n_sink + W slots of a sequence are cut into n_splits
+// ranges; each (sequence, KV head, range) is one work-group that streams its
+// K/V rows from HBM and leaves an unnormalised partial (m, l, o[D]); a
+// combine pass merges the partials of each (sequence, query head):
+//   m* = max m_s,  l* = sum l_s 2^(m_s - m*),  o = sum o_s 2^(m_s - m*) / l*.
+//
+// Fast kernel (bf16, head_dim 128, GQA group 4):
+//  * A wave takes 32 slots at a time.  K is loaded straight from global
+//    memory in the A-operand layout of v_mfma_f32_16x16x32_bf16 (lane = slot,
+//    8 consecutive head-dim elements), S^T = K Q^T with the 4 query heads of
+//    the group as the B columns (the other 12 columns are zero).
+//  * Each lane loads 8 V rows (16 bytes at one head-dim offset) and
+//    transposes them in registers into the A operand of O^T += V^T P^T, so V
+//    needs no LDS round trip.  The score accumulator is the B operand.
+//  * The 4 waves of a work-group interleave over the range and merge through
+//    LDS, so one partial per (sequence, query head, range) reaches memory.
+#include <math.h>
+
+#include "swa_device.hpp"
+#include "swa_launch.hpp"
+
+namespace swa {
+namespace {
+
+constexpr int HD = 128;
+constexpr int kChunk = 32;     // slots per wave step
+constexpr float kTau = 8.0f;
+
+__device__ inline float xg_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float xg_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+struct DecodeArgs {
+  Shape sh;
+  RopeTab rt;
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* pos;
+  float* part;
+  int n_splits;
+  int split_len;
+};
+
+__global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) {
+  __shared__ float sm_m[4][4], sm_l[4][4];
+  __shared__ float sm_o[4][4][HD];
+
+  const Shape& sh = a.sh;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, i = lane & 15, g = lane >> 4;
+  const int p = a.pos[b];
+  const int S = sh.S;
+  // slots [0, min(S, p+1)) hold live positions; the others are never read
+  const int n_live = min(S, p + 1);
+  const int sp0 = split * a.split_len;
+  const int vend = min(min(S, sp0 + a.split_len), n_live);
+  const int h0 = kvh * 4;
+
+  // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
+  bf16x8 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    u32x4 wv = {0u, 0u, 0u, 0u};
+    if (i < 4) wv = *reinterpret_cast<const u32x4*>(a.q + ((long long)b * sh.Hq + h0 + i) * HD + 8 * (4 * kk + g));
+    u32x4 r;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
+      if (sh.rope) {
+        float cs, sn;
+        rope_cs(p, a.rt.freq[4 * (4 * kk + g) + jj], cs, sn);
+        rotate(x0, x1, cs, sn);
+      }
+      r[jj] = pack_bf16(x0, x1);
+    }
+    qf[kk] = __builtin_bit_cast(bf16x8, r);
+  }
+
+  const long long row_stride = (long long)sh.Hkv * HD;       // elements between slots
+  const uint16_t* kbase = a.kc + ((long long)b * S * sh.Hkv + kvh) * HD;
+  const uint16_t* vbase = a.vc + ((long long)b * S * sh.Hkv + kvh) * HD;
+  const float c2 = sh.scale_log2;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = sp0 + kChunk * w; c0 < vend; c0 += 4 * kChunk) {
+    // K: A operand rows = slots c0+16kb+i, d = 8*(4kk+g) .. +7
+    u32x4 kr[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int slot = c0 + 16 * kb + i;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kr[kb][kk] = slot < vend ? *reinterpret_cast<const u32x4*>(kbase + slot * row_stride + 8 * (4 * kk + g))
+                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+    // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
+    u32x4 vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int slot = c0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+      vr[e] = slot < vend ? *reinterpret_cast<const u32x4*>(vbase + slot * row_stride + 8 * i)
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
+    floatx4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kb][kk]), qf[kk], s[kb], 0, 0, 0);
+    }
+    // mask slots past the live range
+    if (c0 + kChunk > vend) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (c0 + 16 * kb + 4 * g + r >= vend) s[kb][r] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xg_max(mx) * c2;
+    const bool need = mx > m_run + kTau;
+    const float alpha = need ? exp2f(m_run - mx) : 1.f;
+    if (need) m_run = mx;
+    if (__any(need)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+    float pv[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[kb][r] = exp2f(fmaf(s[kb][r], c2, -msub));
+        l_run += pv[kb][r];
+      }
+    u32x4 pk;
+    pk[0] = pack_bf16(pv[0][0], pv[0][1]);
+    pk[1] = pack_bf16(pv[0][2], pv[0][3]);
+    pk[2] = pack_bf16(pv[1][0], pv[1][1]);
+    pk[3] = pack_bf16(pv[1][2], pv[1][3]);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+    // transpose: A operand of d-block db holds, for d = 8i+db, the 8 slots kappa(g, e)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int wd = db >> 1;
+      u32x4 va;
+#pragma unroll
+      for (int m2 = 0; m2 < 4; ++m2) {
+        const uint32_t x0 = vr[2 * m2][wd], x1 = vr[2 * m2 + 1][wd];
+        va[m2] = (db & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      }
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[db], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the 4 waves through LDS ----
+  const float lt = xg_sum(l_run);
+  if (i < 4) {
+    if (g == 0) {
+      sm_m[w][i] = m_run;
+      sm_l[w][i] = lt;
+    }
+    // o[db][r]: head i, d = 8*(4g+r) + db
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm_o[w][i][8 * (4 * g + r) + db] = o[db][r];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 4 * HD; idx += 256) {
+    const int hh = idx / HD, d = idx - hh * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float Lsum = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      Lsum += sm_l[ww][hh] * f;
+      O += sm_o[ww][hh][d] * f;
+    }
+    float* dst = a.part + (((long long)b * sh.Hq + h0 + hh) * a.n_splits + split) * (HD + 2);
+    dst[d] = O;
+    if (d == 0) {
+      dst[HD] = M;
+      dst[HD + 1] = Lsum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic decode: one wave per (split, query head, sequence).  Lanes score 64
+// slots at a time, then accumulate O over those slots with lane = head dim.
+// ---------------------------------------------------------------------------
+template <bool F32>
+__device__ inline float ldv(const void* base, long long off) {
+  if (F32) return static_cast<const float*>(base)[off];
+  return __uint_as_float(((uint32_t) static_cast<const uint16_t*>(base)[off]) << 16);
+}
+
+template <bool F32, int D>
+__global__ void __launch_bounds__(64) decode_generic_kernel(Shape sh, RopeTab rt, const void* q,
+                                                            const void* kc, const void* vc,
+                                                            const int32_t* pos, float* part,
+                                                            int n_splits, int split_len) {
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int kvh = h / (sh.Hq / sh.Hkv);
+  const int p = pos[b];
+  float qv[D];
+  const long long qoff = ((long long)b * sh.Hq + h) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) qv[d] = ldv<F32>(q, qoff + d);
+  if (sh.rope) {
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) {
+      float cs, sn;
+      rope_cs(p, rt.freq[kk], cs, sn);
+      rotate(qv[2 * kk], qv[2 * kk + 1], cs, sn);
+    }
+  }
+  if (!F32) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) qv[d] = __uint_as_float(((uint32_t)to_bf16_bits(qv[d])) << 16);
+  }
+  constexpr int E = D / 64;
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int sp0 = split * split_len;
+  const int sp1 = min(sh.S, sp0 + split_len);
+  for (int c0 = sp0; c0 < sp1; c0 += 64) {
+    const int slot = c0 + lane;
+    int P = -1;
+    if (slot < sp1) P = slot_position(slot, p, sh.W, sh.n_sink);
+    float sc = -INFINITY;
+    const long long roff = (((long long)b * sh.S + slot) * sh.Hkv + kvh) * D;
+    if (P >= 0) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc = fmaf(qv[d], ldv<F32>(kc, roff + d), acc);
+      sc = acc * sh.scale_log2;
+    }
+    float cm = sc;
+    for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float mn = fmaxf(m, cm);
+    if (mn == -INFINITY) continue;
+    const float al = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    const float pj = (P >= 0) ? exp2f(sc - mn) : 0.f;
+    float ps = pj;
+    for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    l = l * al + ps;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= al;
+    for (int jj = 0; jj < 64; ++jj) {
+      const float pjj = __shfl(pj, jj);
+      if (pjj != 0.f) {
+        const long long voff = (((long long)b * sh.S + (c0 + jj)) * sh.Hkv + kvh) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(pjj, ldv<F32>(vc, voff + lane + 64 * e), o[e]);
+      }
+    }
+    m = mn;
+  }
+  float* dst = part + (((long long)b * sh.Hq + h) * n_splits + split) * (D + 2);
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[lane + 64 * e] = o[e];
+  if (lane == 0) {
+    dst[D] = m;
+    dst[D + 1] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one work-group per (query head, sequence), one thread per head dim.
+// ---------------------------------------------------------------------------
+template <bool F32>
+__global__ void decode_combine_kernel(Shape sh, const float* part, int n_splits, void* out,
+                                      float* lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int D = sh.D;
+  const float* src = part + ((long long)b * sh.Hq + h) * n_splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, src[s * (D + 2) + D]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    const float ms = src[s * (D + 2) + D];
+    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    L += src[s * (D + 2) + D + 1] * f;
+    O += src[s * (D + 2) + d] * f;
+  }
+  const float val = O / L;
+  const long long off = ((long long)b * sh.Hq + h) * D + d;
+  if (F32)
+    static_cast<float*>(out)[off] = val;
+  else
+    static_cast<uint16_t*>(out)[off] = to_bf16_bits(val);
+  if (lse && d == 0) lse[(long long)b * sh.Hq + h] = (M + log2f(L)) * 0.69314718055994531f;
+}
+
+}  // namespace
+
+// Splits: enough work-groups to cover the 256 CUs several times over, each
+// range a multiple of the 128 slots one work-group step covers.
+int decode_splits(const Shape& sh) {
+  const int units = sh.B * sh.Hkv;
+  int n = (2048 + units - 1) / units;
+  const int max_n = (sh.S + 4 * kChunk - 1) / (4 * kChunk);
+  if (n > max_n) n = max_n;
+  if (n < 1) n = 1;
+  return n;
+}
+
+static int split_len_of(const Shape& sh, int n_splits) {
+  int len = (sh.S + n_splits - 1) / n_splits;
+  len = (len + 4 * kChunk - 1) / (4 * kChunk) * (4 * kChunk);
+  return len;
+}
+
+hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
+                                      const void* kc, const void* vc, const int32_t* pos,
+                                      float* partial, int n_splits, hipStream_t st) {
+  DecodeArgs a;
+  a.sh = sh;
+  a.rt = rt;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(kc);
+  a.vc = static_cast<const uint16_t*>(vc);
+  a.pos = pos;
+  a.part = partial;
+  a.n_splits = n_splits;
+  a.split_len = split_len_of(sh, n_splits);
+  decode_bf16_d128_g4_kernel<<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
+                                 const void* kc, const void* vc, const int32_t* pos,
+                                 float* partial, int n_splits, hipStream_t st) {
+  const int split_len = split_len_of(sh, n_splits);
+  dim3 grid(n_splits, sh.Hq, sh.B);
+  if (f32) {
+    if (sh.D == 64)
+      decode_generic_kernel<true, 64><<<grid, 64, 0, st>>>(sh, rt, q, kc, vc, pos, partial, n_splits, split_len);
+    else
+      decode_generic_kernel<true, 128><<<grid, 64, 0, st>>>(sh, rt, q, kc, vc, pos, partial, n_splits, split_len);
+  } else {
+    if (sh.D == 64)
+      decode_generic_kernel<false, 64><<<grid, 64, 0, st>>>(sh, rt, q, kc, vc, pos, partial, n_splits, split_len);
+    else
+      decode_generic_kernel<false, 128><<<grid, 64, 0, st>>>(sh, rt, q, kc, vc, pos, partial, n_splits, split_len);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const Shape& sh, bool f32, const float* partial, int n_splits,
+                                 void* out, float* lse, hipStream_t st) {
+  dim3 grid(sh.Hq, sh.B);
+  if (f32)
+    decode_combine_kernel<true><<<grid, sh.D, 0, st>>>(sh, partial, n_splits, out, lse);
+  else
+    decode_combine_kernel<false><<<grid, sh.D, 0, st>>>(sh, partial, n_splits, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace swa

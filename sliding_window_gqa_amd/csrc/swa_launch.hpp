@@ -1,0 +1,50 @@
+// swa_launch.hpp — host-side launchers implemented next to their kernels and
+// called by the C ABI in swa_api.cpp after it has validated the arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swa_device.hpp"
+
+namespace swa {
+
+// Destination of a rotate-and-store launch.
+enum WriteMode {
+  kToCache = 0,  // rolling-buffer slots of k_cache / v_cache (survivors only)
+  kToDense = 1,  // rotated K into a dense [B][n_tok][Hkv][D] buffer (V untouched)
+};
+
+hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
+                              const void* v, const int32_t* start, int n_tok, void* kdst,
+                              void* vdst, WriteMode mode, hipStream_t st);
+
+// Fast bf16 prefill: head_dim 128, group size 4, n_sink <= 64.
+hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
+                                       const void* k_rot, const void* v, const void* kc,
+                                       const void* vc, const int32_t* start, int C, void* out,
+                                       float* lse, hipStream_t st);
+
+// Generic prefill (float32 or bf16, head_dim 64 or 128, any group size).
+hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
+                                  const void* k_rot, const void* v, const void* kc,
+                                  const void* vc, const int32_t* start, int C, void* out,
+                                  float* lse, hipStream_t st);
+
+// Split-K decode.  Partials: [B][Hq][n_splits][D + 2] float.
+int decode_splits(const Shape& sh);
+hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
+                                      const void* kc, const void* vc, const int32_t* pos,
+                                      float* partial, int n_splits, hipStream_t st);
+hipError_t launch_decode_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
+                                 const void* kc, const void* vc, const int32_t* pos,
+                                 float* partial, int n_splits, hipStream_t st);
+hipError_t launch_decode_combine(const Shape& sh, bool f32, const float* partial, int n_splits,
+                                 void* out, float* lse, hipStream_t st);
+
+hipError_t launch_debug_slots(const Shape& sh, const int32_t* pos, int n, int32_t* slots,
+                              hipStream_t st);
+hipError_t launch_debug_mask(const Shape& sh, int q_pos, const int32_t* k_pos, int n,
+                             uint8_t* mask, hipStream_t st);
+
+}  // namespace swa

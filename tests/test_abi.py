@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every symbol
+include/swa.h declares, and rejects bad arguments on the host before any HIP
+call (no kernel is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_gqa_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(swa.LIB_PATH),
+                                reason="libswa.so not built (run __graft_entry__.build())")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(swa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"swa_cache_write", "swa_prefill_chunk", "swa_decode", "swa_decode_workspace_bytes",
+            "swa_prefill_workspace_bytes", "swa_status_string", "swa_debug_slots",
+            "swa_debug_mask"} <= set(names)
+    lib = ctypes.CDLL(swa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def P(**kw):
+    base = dict(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128, window=4096, n_sink=0,
+                scale=0.0, rope_theta=10000.0, dtype=swa.SWA_BF16)
+    base.update(kw)
+    return swa.make_params(**base)
+
+
+BAD_PARAMS = [
+    (dict(n_q_heads=30), swa.SWA_ERR_SHAPE),        # Hq % Hkv != 0
+    (dict(head_dim=96), swa.SWA_ERR_SHAPE),
+    (dict(window=0), swa.SWA_ERR_SHAPE),
+    (dict(n_sink=-1), swa.SWA_ERR_SHAPE),
+    (dict(n_sink=65), swa.SWA_ERR_SHAPE),
+    (dict(batch=0), swa.SWA_ERR_SHAPE),
+    (dict(scale=-1.0), swa.SWA_ERR_SHAPE),
+    (dict(scale=float("nan")), swa.SWA_ERR_SHAPE),
+    (dict(rope_theta=-5.0), swa.SWA_ERR_SHAPE),
+    (dict(dtype=7), swa.SWA_ERR_DTYPE),
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_PARAMS)
+def test_bad_params_rejected_everywhere(bad, code):
+    lib = swa.library()
+    p = P(**bad)
+    bp = ctypes.byref(p)
+    assert lib.swa_cache_write(bp, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == code
+    assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == code
+    assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
+    assert lib.swa_debug_slots(bp, FAKE, 4, FAKE, None) == code
+    assert lib.swa_decode_workspace_bytes(bp) == 0
+    assert lib.swa_prefill_workspace_bytes(bp, 16) == 0
+
+
+def test_null_pointers_rejected():
+    lib = swa.library()
+    bp = ctypes.byref(P())
+    assert lib.swa_cache_write(None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == swa.SWA_ERR_NULL
+    assert lib.swa_cache_write(bp, None, FAKE, FAKE, 4, FAKE, FAKE, None) == swa.SWA_ERR_NULL
+    assert lib.swa_cache_write(bp, FAKE, FAKE, None, 4, FAKE, FAKE, None) == swa.SWA_ERR_NULL
+    assert lib.swa_cache_write(bp, FAKE, FAKE, FAKE, 4, FAKE, None, None) == swa.SWA_ERR_NULL
+    assert lib.swa_prefill_chunk(bp, None, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
+    # exactly one cache pointer given
+    assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
+    assert lib.swa_decode(bp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
+    assert lib.swa_debug_mask(bp, 5, None, 4, FAKE, None) == swa.SWA_ERR_NULL
+
+
+def test_sizes_and_workspace_rejected():
+    lib = swa.library()
+    p = P()
+    bp = ctypes.byref(p)
+    assert lib.swa_cache_write(bp, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == swa.SWA_ERR_SHAPE
+    assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 0, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_SHAPE
+    need = lib.swa_prefill_workspace_bytes(bp, 16)
+    assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, need - 1, None) == swa.SWA_ERR_WORKSPACE
+    assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None, need, None) == swa.SWA_ERR_WORKSPACE
+    dneed = lib.swa_decode_workspace_bytes(bp)
+    assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE
+    assert lib.swa_debug_slots(bp, FAKE, 0, FAKE, None) == swa.SWA_ERR_SHAPE
+    assert lib.swa_debug_mask(bp, -1, FAKE, 4, FAKE, None) == swa.SWA_ERR_SHAPE
+
+
+def test_workspace_sizes():
+    lib = swa.library()
+    # prefill: the chunk's rotated keys, one element per (b, token, kv head, dim)
+    for dt, es in ((swa.SWA_BF16, 2), (swa.SWA_F32, 4)):
+        p = P(dtype=dt)
+        assert lib.swa_prefill_workspace_bytes(ctypes.byref(p), 4096) == 2 * 4096 * 8 * 128 * es
+    # decode: B*Hq partials of (D + 2) floats per split; splits cover the slots
+    for B, W, S in ((64, 4096, 0), (16, 4092, 4), (1, 64, 0), (3, 100, 2)):
+        p = P(batch=B, window=W, n_sink=S)
+        nbytes = lib.swa_decode_workspace_bytes(ctypes.byref(p))
+        per_split = B * 32 * (128 + 2) * 4
+        assert nbytes % per_split == 0
+        n_splits = nbytes // per_split
+        assert 1 <= n_splits <= -(-(W + S) // 128)
+        assert B * 8 * n_splits >= min(2048, B * 8 * -(-(W + S) // 128))
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = swa.swa_status_string(code)
+        assert s.startswith("SWA_")
+    assert "unknown" in swa.swa_status_string(42)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(swa, "_lib", None)
+    monkeypatch.setattr(swa, "LIB_PATH", str(tmp_path / "libswa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        swa.library()

@@ -1,0 +1,260 @@
+"""GPU parity on small inputs that still span several tiles and ragged tails:
+the HIP library (through the C ABI) against the fp64 oracle, element by
+element.  Index work (slots, masks, cache placement) is compared bit-exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.swa_oracle as so
+import sliding_window_gqa_amd as swa
+from sliding_window_gqa_amd import synth
+from tests.common import BF16_LSE_ATOL, assert_close, assert_lse, tol
+from tests.gpu_harness import DEV, GpuSide, OracleSide, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def rnd(shape, tag, seq=0, dtype=torch.bfloat16, index=90):
+    return synth.normal(shape, index, tag, seq, dtype)
+
+
+# ---------------------------------------------------------------------------
+# integer index work, bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W,S", [(4096, 0), (4092, 4), (100, 3), (4, 0), (1, 0), (64, 64)])
+def test_debug_slots_and_mask_bit_exact(W, S):
+    print(f"debug slots/mask W={W} n_sink={S}", flush=True)
+    p = swa.make_params(1, 4, 1, 128, W, S)
+    g = torch.Generator().manual_seed(W + S)
+    pos = torch.cat([torch.arange(0, 300), torch.randint(0, 1 << 24, (500,), generator=g)]).to(torch.int32)
+    slots = swa.swa_debug_slots(p, pos.to(DEV)).cpu().numpy()
+    cache = so.RollingCache(1, 1, W, S)
+    np.testing.assert_array_equal(slots, [cache.slot(int(x)) for x in pos])
+    for qp in [0, 1, 3, W - 1, W, W + 1, S + W + 5, 70000]:
+        kp = torch.arange(max(0, qp - W - 70), qp + 70, dtype=torch.int32)
+        kp = torch.cat([torch.arange(0, S + 3, dtype=torch.int32), kp])
+        m = swa.swa_debug_mask(p, qp, kp.to(DEV)).cpu().numpy().astype(bool)
+        np.testing.assert_array_equal(m, so.key_mask([qp], kp.numpy(), W, S)[0])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("theta", [0.0, 10000.0])
+@pytest.mark.parametrize("S", [0, 3])
+def test_cache_write_placement(dtype, theta, S):
+    """Slots written must hold exactly the oracle's entries (V verbatim, K
+    rotated); slots never written keep their old bytes."""
+    print(f"cache write dtype={dtype} theta={theta} n_sink={S}", flush=True)
+    B, Hkv, D, W = 3, 2, 128, 20
+    gpu = GpuSide(B, 4 * Hkv, Hkv, D, W, S, theta, dtype, fill=7.0)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta)
+    ops = [(7, [0, 5, 33]), (45, [7, 12, 40]), (1, [52, 57, 85]), (19, [53, 58, 86]), (2, [200, 300, 1000])]
+    for n, start in ops:
+        k = rnd((B, n, Hkv, D), "k", n, dtype)
+        v = rnd((B, n, Hkv, D), "v", n, dtype)
+        gpu.write(k, v, start)
+        orc.write(k, v, start)
+    kc, vc = np64(gpu.kc), np64(gpu.vc)
+    for b in range(B):
+        c = orc.caches[b]
+        held = c.tag >= 0
+        np.testing.assert_array_equal(vc[b][held], c.v[held])
+        assert (vc[b][~held] == 7.0).all() and (kc[b][~held] == 7.0).all()
+        if theta == 0:
+            np.testing.assert_array_equal(kc[b][held], c.k[held])
+        else:
+            err = np.abs(kc[b][held] - c.k[held])
+            ulp = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -23
+            assert (err <= ulp * np.abs(c.k[held]) + 1e-6).all(), err.max()
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [64, 256])
+def test_prefill_tiny_fp32(W):
+    """Tiny float32 SWA prefill: batch 1, N=256, 4/1 heads, head_dim 64, no
+    RoPE, scale 1/8; W=256 is full causal attention."""
+    print(f"tiny fp32 prefill W={W}", flush=True)
+    wl = synth.workload(1)
+    N, Hq, Hkv, D = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    q = synth.normal((1, N, Hq, D), 1, "q", dtype=torch.float32)
+    k = synth.normal((1, N, Hkv, D), 1, "k", dtype=torch.float32)
+    v = synth.normal((1, N, Hkv, D), 1, "v", dtype=torch.float32)
+    gpu = GpuSide(1, Hq, Hkv, D, W, 0, 0.0, torch.float32, scale=wl.scale)
+    orc = OracleSide([0], Hkv, D, W, 0, 0.0, scale=wl.scale)
+    out, lse = gpu.prefill(q, k, v, [0])
+    ref = orc.prefill(q, k, v, [0])[0]
+    atol, rrms, latol = tol(torch.float32)
+    assert_close(out[0], ref[0], atol, rrms, "out")
+    assert_lse(lse[0], ref[1], latol, "lse")
+
+
+PREFILL_CASES = [
+    # (B, Hq, Hkv, D, W, n_sink, dtype, chunks)  -- fast path: bf16, D=128, G=4
+    (2, 8, 2, 128, 100, 0, torch.bfloat16, [130, 1, 3, 64, 100, 52]),
+    (2, 8, 2, 128, 100, 4, torch.bfloat16, [130, 1, 3, 64, 100, 52]),
+    (1, 4, 1, 128, 64, 0, torch.bfloat16, [200, 64, 65]),
+    (1, 4, 1, 128, 1, 0, torch.bfloat16, [70, 5]),
+    (2, 4, 1, 128, 300, 2, torch.bfloat16, [500, 77]),
+    # generic path
+    (2, 4, 2, 64, 100, 0, torch.bfloat16, [130, 1, 70]),
+    (1, 6, 2, 128, 50, 3, torch.float32, [90, 7, 40]),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}{str(c[6])[6:]}" for c in PREFILL_CASES])
+def test_prefill_chunks(case):
+    B, Hq, Hkv, D, W, S, dtype, chunks = case
+    print(f"prefill chunks {case}", flush=True)
+    theta = 10000.0
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta)
+    # sequence b > 0 starts after a prefix of 237*b tokens already in the cache
+    offs = [237 * b for b in range(B)]
+    if max(offs) > 0:
+        for b in range(1, B):
+            pre = 237 * b
+            kp = rnd((1, pre, Hkv, D), "hist_k", b, dtype)
+            vp = rnd((1, pre, Hkv, D), "hist_v", b, dtype)
+            sub = GpuSide(1, Hq, Hkv, D, W, S, theta, dtype)
+            sub.write(kp, vp, [0])
+            gpu.kc[b] = sub.kc[0]
+            gpu.vc[b] = sub.vc[0]
+            orc.caches[b].write(so.rope(np64(kp[0]), np.arange(pre), theta), np64(vp[0]), np.arange(pre))
+        gpu.has_cache = True
+    atol, rrms, latol = tol(dtype)
+    t = 0
+    for ci, C in enumerate(chunks):
+        q = rnd((B, C, Hq, D), "q", ci, dtype)
+        k = rnd((B, C, Hkv, D), "k", ci, dtype)
+        v = rnd((B, C, Hkv, D), "v", ci, dtype)
+        start = [offs[b] + t for b in range(B)]
+        out, lse = gpu.prefill(q, k, v, start)
+        ref = orc.prefill(q, k, v, start)
+        for b in range(B):
+            assert_close(out[b], ref[b][0], atol, rrms, f"chunk {ci} seq {b} out")
+            assert_lse(lse[b], ref[b][1], latol, f"chunk {ci} seq {b} lse")
+        t += C
+
+
+def test_prefill_key_counts_exact():
+    """A (near) zero softmax scale makes every weight exactly 1, so exp(lse)
+    counts the keys each query attended: an end-to-end integer check of the
+    masks, the window edge, the sinks and the cache/chunk split."""
+    print("prefill key counts", flush=True)
+    B, Hq, Hkv, D, W, S = 2, 8, 2, 128, 100, 4
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, 10000.0, torch.bfloat16, scale=1e-30)
+    t = 0
+    for ci, C in enumerate([150, 70, 1, 130]):
+        q = rnd((B, C, Hq, D), "q", ci)
+        k = rnd((B, C, Hkv, D), "k", ci)
+        v = rnd((B, C, Hkv, D), "v", ci)
+        start = [t, t + 1000 * 0]
+        _, lse = gpu.prefill(q, k, v, start)
+        lse = lse.cpu().numpy()
+        for b in range(B):
+            for tt in range(C):
+                I = start[b] + tt
+                count = int(so.key_mask([I], np.arange(I + 1), W, S)[0].sum())
+                got = np.rint(np.exp(lse[b, :, tt].astype(np.float64)))
+                assert (got == count).all(), (ci, b, tt, got[:4], count)
+        t += C
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+DECODE_CASES = [
+    (3, 8, 2, 128, 100, 0, torch.bfloat16),
+    (3, 8, 2, 128, 100, 3, torch.bfloat16),
+    (2, 4, 1, 128, 4092, 4, torch.bfloat16),
+    (3, 4, 2, 64, 100, 0, torch.bfloat16),   # generic path
+    (2, 4, 1, 64, 100, 2, torch.float32),    # generic path
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}{str(c[6])[6:]}" for c in DECODE_CASES])
+def test_decode_steps(case):
+    B, Hq, Hkv, D, W, S, dtype = case
+    print(f"decode steps {case}", flush=True)
+    theta = 10000.0
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta)
+    p0 = [0, 57, 250][:B] if W < 1000 else [3, 5000][:B]
+    # history: positions max(0, p0 - W - S) .. p0 - 1, one write per sequence
+    for b in range(B):
+        lo = max(0, p0[b] - W - S)
+        n = p0[b] - lo
+        if n == 0:
+            continue
+        kh = rnd((1, n, Hkv, D), "hist_k", b, dtype)
+        vh = rnd((1, n, Hkv, D), "hist_v", b, dtype)
+        sub = GpuSide(1, Hq, Hkv, D, W, S, theta, dtype)
+        sub.write(kh, vh, [lo])
+        orc.caches[b].write(so.rope(np64(kh[0]), np.arange(lo, p0[b]), theta), np64(vh[0]), np.arange(lo, p0[b]))
+        if S > 0 and lo > 0:  # sinks of this sequence, written after the history on both sides
+            ks = rnd((1, S, Hkv, D), "sink_k", b, dtype)
+            vs = rnd((1, S, Hkv, D), "sink_v", b, dtype)
+            sub.write(ks, vs, [0])
+            orc.caches[b].write(so.rope(np64(ks[0]), np.arange(S), theta), np64(vs[0]), np.arange(S))
+        gpu.kc[b] = sub.kc[0]
+        gpu.vc[b] = sub.vc[0]
+    atol, rrms, latol = tol(dtype)
+    steps = 130 if W < 1000 else 40
+    for st in range(steps):
+        q = rnd((B, Hq, D), "step_q", st, dtype)
+        k = rnd((B, Hkv, D), "step_k", st, dtype)
+        v = rnd((B, Hkv, D), "step_v", st, dtype)
+        pos = [p0[b] + st for b in range(B)]
+        out, lse = gpu.decode(q, k, v, pos)
+        ref = orc.decode(q, k, v, pos)
+        for b in range(B):
+            assert_close(out[b], ref[b][0], atol, rrms, f"step {st} seq {b} out")
+            assert_lse(lse[b], ref[b][1], latol, f"step {st} seq {b} lse")
+
+
+def test_decode_key_counts_exact():
+    print("decode key counts", flush=True)
+    B, Hq, Hkv, D, W, S = 3, 8, 2, 128, 100, 3
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, 10000.0, torch.bfloat16, scale=1e-30)
+    for st in range(0, 230):
+        q = rnd((B, Hq, D), "step_q", st)
+        k = rnd((B, Hkv, D), "step_k", st)
+        v = rnd((B, Hkv, D), "step_v", st)
+        pos = [st, st, st]
+        _, lse = gpu.decode(q, k, v, pos)
+        count = int(so.key_mask([st], np.arange(st + 1), W, S)[0].sum())
+        got = np.rint(np.exp(lse.cpu().numpy().astype(np.float64)))
+        assert (got == count).all(), (st, got.ravel()[:4], count)
+
+
+# ---------------------------------------------------------------------------
+# determinism and resume
+# ---------------------------------------------------------------------------
+def test_bitwise_determinism_and_resume():
+    print("determinism and resume", flush=True)
+    B, Hq, Hkv, D, W, S = 2, 8, 2, 128, 100, 2
+    gpu = GpuSide(B, Hq, Hkv, D, W, S)
+    q = rnd((B, 300, Hq, D), "q", 1)
+    k = rnd((B, 300, Hkv, D), "k", 1)
+    v = rnd((B, 300, Hkv, D), "v", 1)
+    st = torch.tensor([0, 0], dtype=torch.int32, device=DEV)
+    o1, l1 = swa.swa_prefill_chunk(gpu.p, q.to(DEV), k.to(DEV), v.to(DEV), None, None, st)
+    o2, l2 = swa.swa_prefill_chunk(gpu.p, q.to(DEV), k.to(DEV), v.to(DEV), None, None, st)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    gpu.write(k, v, [0, 0])
+    steps = []
+    for s in range(20):
+        steps.append((rnd((B, Hq, D), "step_q", s), rnd((B, Hkv, D), "step_k", s), rnd((B, Hkv, D), "step_v", s)))
+    for s in range(10):
+        gpu.decode(*steps[s], [300 + s] * B)
+    snap = (gpu.kc.clone(), gpu.vc.clone())
+    first = [gpu.decode(*steps[s], [300 + s] * B) for s in range(10, 20)]
+    gpu.kc.copy_(snap[0])
+    gpu.vc.copy_(snap[1])
+    second = [gpu.decode(*steps[s], [300 + s] * B) for s in range(10, 20)]
+    for (a, la), (b, lb) in zip(first, second):
+        assert torch.equal(a, b) and torch.equal(la, lb)

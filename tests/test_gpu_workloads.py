@@ -1,0 +1,167 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times.  The oracle evaluates sampled query rows / decode steps one
+by one (rows are independent), while it follows every cache write exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.swa_oracle as so
+import sliding_window_gqa_amd as swa
+from sliding_window_gqa_amd import synth
+from tests.common import assert_close, assert_lse, tol
+from tests.gpu_harness import DEV, GpuSide, OracleSide, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(C, n_random, seed, fixed):
+    g = np.random.default_rng(seed)
+    rows = set(int(r) for r in fixed if 0 <= r < C)
+    rows |= set(int(x) for x in g.choice(C, size=min(n_random, C), replace=False))
+    return np.array(sorted(rows))
+
+
+def check_rows(out, lse, ref, rows, dtype, what):
+    atol, rrms, latol = tol(dtype)
+    assert_close(out[rows.tolist()], ref[0], atol, rrms, what + " out")
+    assert_lse(lse[:, rows.tolist()], ref[1], latol, what + " lse")
+
+
+def test_workload2_prefill_n8192():
+    wl = synth.workload(2)
+    print(f"workload {wl.name}", flush=True)
+    N, Hq, Hkv, D, W = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    q = synth.normal((1, N, Hq, D), 2, "q")
+    k = synth.normal((1, N, Hkv, D), 2, "k")
+    v = synth.normal((1, N, Hkv, D), 2, "v")
+    gpu = GpuSide(1, Hq, Hkv, D, W)
+    out, lse = gpu.prefill(q, k, v, [0], use_cache=False)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 24, 2, [0, 1, 63, 64, 127, 4095, 4096, 4097, 6000, 8191])
+    orc = OracleSide([0], Hkv, D, W)
+    ref = orc.prefill(q, k, v, [0], rows=rows)[0]
+    check_rows(out[0].cpu(), lse[0].cpu(), ref, rows, torch.bfloat16, "prefill n8192")
+    # the cache afterwards holds the last W positions
+    pos = np.arange(N - W, N)
+    np.testing.assert_array_equal(np64(gpu.vc[0])[pos % W], np64(v[0])[pos])
+
+
+def test_workload3_chunked_prefill_and_full_causal():
+    wl = synth.workload(3)
+    print(f"workload {wl.name}", flush=True)
+    N, Hq, Hkv, D, W, C = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.chunk
+    q = synth.normal((1, N, Hq, D), 3, "q")
+    k = synth.normal((1, N, Hkv, D), 3, "k")
+    v = synth.normal((1, N, Hkv, D), 3, "v")
+    gpu = GpuSide(1, Hq, Hkv, D, W)
+    orc = OracleSide([0], Hkv, D, W)
+    for c in range(N // C):
+        s = c * C
+        print(f"  chunk {c}", flush=True)
+        out, lse = gpu.prefill(q[:, s:s + C], k[:, s:s + C], v[:, s:s + C], [s])
+        rows = sample_rows(C, 12, 30 + c, [0, 1, 2, 63, 64, 2047, 4094, 4095])
+        ref = orc.prefill(q[:, s:s + C], k[:, s:s + C], v[:, s:s + C], [s], rows=rows)[0]
+        check_rows(out[0].cpu(), lse[0].cpu(), ref, rows, torch.bfloat16, f"chunk {c}")
+        np.testing.assert_array_equal(np.sort(orc.caches[0].positions()), np.arange(s + C - W, s + C))
+    # full causal attention at N = 16384 (window >= N), one pass
+    Wf = wl.extra["full_window"]
+    print("  full causal", flush=True)
+    gfull = GpuSide(1, Hq, Hkv, D, Wf)
+    out, lse = gfull.prefill(q, k, v, [0], use_cache=False)
+    rows = sample_rows(N, 12, 39, [0, 1, 8191, 16383])
+    ref = OracleSide([0], Hkv, D, Wf).prefill(q, k, v, [0], rows=rows)[0]
+    check_rows(out[0].cpu(), lse[0].cpu(), ref, rows, torch.bfloat16, "full causal")
+
+
+def _decode_setup(wl, n_oracle_seqs, seed):
+    B, Hq, Hkv, D, W, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.n_sink
+    p0 = synth.positions(wl.index, B, wl.pos_lo, wl.pos_hi).numpy().astype(np.int64)
+    gpu = GpuSide(B, Hq, Hkv, D, W, S)
+    # the buffers start out holding N(0,1) values in every slot
+    for b in range(B):
+        gpu.kc[b] = synth.normal(gpu.kc.shape[1:], wl.index, "garbage_k", b).to(DEV)
+        gpu.vc[b] = synth.normal(gpu.vc.shape[1:], wl.index, "garbage_v", b).to(DEV)
+    order = np.argsort(p0)
+    g = np.random.default_rng(seed)
+    seqs = sorted(set(order[:4].tolist()) | set(g.choice(B, size=n_oracle_seqs - 4, replace=False).tolist()))
+    orc = OracleSide(seqs, Hkv, D, W, S)
+    return p0, gpu, orc
+
+
+def test_workload4_batched_decode():
+    wl = synth.workload(4)
+    print(f"workload {wl.name}", flush=True)
+    B, Hq, Hkv, D, W = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    p0, gpu, orc = _decode_setup(wl, 16, 4)
+    # history: positions max(0, p0-W) .. p0-1 hold N(0,1) keys taken as already rotated
+    p_one = swa.make_params(1, Hq, Hkv, D, W, 0, 0.0, 0.0)
+    for b in range(B):
+        lo = max(0, int(p0[b]) - W)
+        n = int(p0[b]) - lo
+        if n == 0:
+            continue
+        kh = synth.normal((1, n, Hkv, D), 4, "hist_k", b)
+        vh = synth.normal((1, n, Hkv, D), 4, "hist_v", b)
+        swa.swa_cache_write(p_one, kh.to(DEV), vh.to(DEV), torch.tensor([lo], dtype=torch.int32, device=DEV),
+                            gpu.kc[b:b + 1], gpu.vc[b:b + 1])
+        if b in orc.caches:
+            orc.caches[b].write(np64(kh[0]), np64(vh[0]), np.arange(lo, int(p0[b])))
+    qs = synth.normal((wl.steps, B, Hq, D), 4, "step_q")
+    ks = synth.normal((wl.steps, B, Hkv, D), 4, "step_k")
+    vs = synth.normal((wl.steps, B, Hkv, D), 4, "step_v")
+    check_at = {0, 1, 2, 127, 254, 255}
+    atol, rrms, latol = tol(torch.bfloat16)
+    for s in range(wl.steps):
+        pos = p0 + s
+        out, lse = gpu.decode(qs[s], ks[s], vs[s], pos)
+        ref = orc.decode(qs[s], ks[s], vs[s], pos, compute=s in check_at)
+        if s in check_at:
+            o, l = out.cpu(), lse.cpu()
+            for b, (ro, rl) in ref.items():
+                assert_close(o[b], ro, atol, rrms, f"step {s} seq {b} (p={pos[b]})")
+                assert_lse(l[b], rl, latol, f"step {s} seq {b} lse")
+
+
+def test_workload5_sink_streaming():
+    wl = synth.workload(5)
+    print(f"workload {wl.name}", flush=True)
+    B, Hq, Hkv, D, W, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.n_sink
+    p0, gpu, orc = _decode_setup(wl, 8, 5)
+    ksk = synth.normal((B, S, Hkv, D), 5, "sink_k")
+    vsk = synth.normal((B, S, Hkv, D), 5, "sink_v")
+    gpu.write(ksk, vsk, [0] * B)
+    orc.write(ksk, vsk, [0] * B)
+    kh = synth.normal((B, W, Hkv, D), 5, "hist_k")
+    vh = synth.normal((B, W, Hkv, D), 5, "hist_v")
+    gpu.write(kh, vh, p0 - W)
+    orc.write(kh, vh, p0 - W)
+    atol, rrms, latol = tol(torch.bfloat16)
+    p = p0.copy()
+    for phase in range(2):
+        qs = synth.normal((wl.steps, B, Hq, D), 5, "step_q", phase)
+        ks = synth.normal((wl.steps, B, Hkv, D), 5, "step_k", phase)
+        vs = synth.normal((wl.steps, B, Hkv, D), 5, "step_v", phase)
+        for s in range(wl.steps):
+            check = s in (0, wl.steps - 1)
+            out, lse = gpu.decode(qs[s], ks[s], vs[s], p)
+            ref = orc.decode(qs[s], ks[s], vs[s], p, compute=check)
+            if check:
+                o, l = out.cpu(), lse.cpu()
+                for b, (ro, rl) in ref.items():
+                    assert_close(o[b], ro, atol, rrms, f"phase {phase} step {s} seq {b}")
+                    assert_lse(l[b], rl, latol, f"phase {phase} step {s} seq {b} lse")
+            p = p + 1
+        if phase == 0:
+            print("  chunk", flush=True)
+            C = wl.chunk
+            qc = synth.normal((B, C, Hq, D), 5, "chunk_q")
+            kc = synth.normal((B, C, Hkv, D), 5, "chunk_k")
+            vc = synth.normal((B, C, Hkv, D), 5, "chunk_v")
+            out, lse = gpu.prefill(qc, kc, vc, p)
+            rows = sample_rows(C, 6, 55, [0, 1, 4095])
+            ref = orc.prefill(qc, kc, vc, p, rows=rows)
+            o, l = out.cpu(), lse.cpu()
+            for b, r in ref.items():
+                check_rows(o[b], l[b], r, rows, torch.bfloat16, f"chunk seq {b}")
+            p = p + C
