@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the sliding-window GQA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the prefill hot path over the 8192-token Mistral-7B
+attention layer (batch 1, 32 query / 8 KV heads, head_dim 128, W = 4096,
+bf16, RoPE theta 10000): key rotation, the band-restricted attention, and the
+rolling-buffer write of the chunk's keys and values.  `value` is the
+algorithmic prefill FLOP rate of that step (4*D*Hq*sum_i |A(i)|).  The decode
+half of the metric is measured on the batched-decode workload (64 sequences,
+256 steps of cache write + decode) and reported under "decode".
+
+Inputs are synthetic (seeded N(0,1), bf16) and resident in HBM before timing.
+Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SWA prefill TFLOP/s + decode HBM GB/s, W=4096 GQA 32/8 hd128 bf16"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak (published)
+
+
+def band_pairs(N, W, start=0, n_sink=0):
+    """sum over queries i in [start, start+N) of |A(i)| (all earlier keys exist)."""
+    tot = 0
+    for i in range(start, start + N):
+        lo = max(0, i - W + 1)
+        tot += i - lo + 1 + min(n_sink, lo)
+    return tot
+
+
+def attn_flops(pairs, D=128, Hq=32):
+    return 4 * D * Hq * pairs
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the chunked / full-causal / sink timings")
+    ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all",
+                    help="restrict the GPU work (for profiler runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sliding_window_gqa_amd as swa
+    from sliding_window_gqa_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    result = {"metric": METRIC}
+
+    # ------------------------------------------------------------------
+    # prefill: N=8192, W=4096 (the headline workload)
+    # ------------------------------------------------------------------
+    wl = synth.workload(2)
+    N, Hq, Hkv, D, W = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    p = swa.make_params(1, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+    q = synth.normal((1, N, Hq, D), 2, "q").to(dev)
+    k = synth.normal((1, N, Hkv, D), 2, "k").to(dev)
+    v = synth.normal((1, N, Hkv, D), 2, "v").to(dev)
+    kc = torch.zeros((1, W, Hkv, D), dtype=bf, device=dev)
+    vc = torch.zeros_like(kc)
+    start = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((1, N, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((1, Hq, N), dtype=torch.float32, device=dev)
+    k_rot = torch.empty_like(k)
+    pairs2 = band_pairs(N, W)
+    flops2 = attn_flops(pairs2)
+
+    def prefill_step(ev=None):
+        swa.swa_rope_keys(p, k, start, k_rot)
+        if ev is not None:
+            ev[0].record()
+        swa.swa_prefill_attention(p, q, k_rot, v, None, None, start, out, lse)
+        if ev is not None:
+            ev[1].record()
+        swa.swa_cache_write(p, k, v, start, kc, vc)
+
+    if args.only in ("prefill", "all"):
+        for _ in range(args.warmup):
+            prefill_step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for s in range(args.steps):
+            prefill_step(evs[s])
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = t0.elapsed_time(t1) / args.steps
+        attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        achieved = flops2 / (attn_ms * 1e-3) / 1e12
+        result.update({
+            "value": round(flops2 / (ms_step * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": wl.name, "batch": 1, "seq_len": N, "window": W,
+                       "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "rope_theta": wl.rope_theta,
+                       "step": "rope_keys + prefill_attention + cache_write",
+                       "algorithmic_flops_per_step": flops2, "key_pairs": pairs2},
+            "roofline": {"bound": "mfma", "kernel": "prefill_bf16_d128_g4_kernel",
+                         "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "avg_kernel_ms": round(attn_ms, 4),
+                         "timing": "HIP events around each attention launch in the timed region"},
+            "wall_s_timed_region": round(wall, 4),
+        })
+
+    # ------------------------------------------------------------------
+    # decode: 64 sequences, positions U[1, 32768], 256 steps
+    # ------------------------------------------------------------------
+    if args.only in ("decode", "all"):
+        wl4 = synth.workload(4)
+        B4, S4 = wl4.batch, wl4.n_slots
+        p4 = swa.make_params(B4, Hq, Hkv, D, wl4.window, 0, 0.0, wl4.rope_theta, bf)
+        g = torch.Generator(device=dev).manual_seed(4004)
+        kc4 = torch.randn((B4, S4, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        vc4 = torch.randn((B4, S4, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        T = args.decode_steps
+        qs = torch.randn((T, B4, Hq, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        ks = torch.randn((T, B4, 1, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        vs = torch.randn((T, B4, 1, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        p0 = synth.positions(4, B4, wl4.pos_lo, wl4.pos_hi).to(torch.int64)
+        pos = (p0[None, :] + torch.arange(T)[:, None]).to(torch.int32).to(dev)    # [T][B]
+        o4 = torch.empty((B4, Hq, D), dtype=bf, device=dev)
+        l4 = torch.empty((B4, Hq), dtype=torch.float32, device=dev)
+        ws4 = torch.empty(swa.swa_decode_workspace_bytes(p4), dtype=torch.uint8, device=dev)
+        row_bytes = Hkv * D * 2 * 2                       # K and V of one slot
+        kv_bytes = sum(int(min(int(pp) + 1, S4)) * row_bytes for pp in pos.cpu().flatten())
+        qo_bytes = T * B4 * Hq * D * 2 * 2
+        write_bytes = T * B4 * Hkv * D * 2 * 2 * 2        # read k,v + write k,v
+        dec_bytes = kv_bytes + qo_bytes
+
+        def dstep(s, ev=None):
+            swa.swa_cache_write(p4, ks[s], vs[s], pos[s], kc4, vc4)
+            if ev is not None:
+                ev[0].record()
+            swa.swa_decode(p4, qs[s], kc4, vc4, pos[s], o4, l4, ws4)
+            if ev is not None:
+                ev[1].record()
+
+        for s in range(min(8, T)):
+            dstep(s)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for s in range(T):
+            dstep(s, evs[s])
+        t1.record()
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        dec_ms = sum(a.elapsed_time(b) for a, b in evs)
+        dec_achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": wl4.name, "batch": B4, "steps": T, "window": wl4.window,
+            "value": round((dec_bytes + write_bytes) / (total_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(total_ms / T, 4),
+            "step": "cache_write + decode (split + combine)",
+            "algorithmic_bytes_per_step": round((dec_bytes + write_bytes) / T),
+            "roofline": {"bound": "hbm", "kernel": "decode_bf16_d128_g4_kernel + decode_combine_kernel",
+                         "achieved": round(dec_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(dec_achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                         "avg_call_ms": round(dec_ms / T, 4),
+                         "bytes": "valid K/V slots read once + Q + O"},
+        }
+        del kc4, vc4, qs, ks, vs
+
+    # ------------------------------------------------------------------
+    # context: chunked SWA vs full causal at 16K, sink streaming decode
+    # ------------------------------------------------------------------
+    if not args.no_context and args.only == "all":
+        result["context"] = context_timings(swa, synth, torch, dev)
+
+    # ------------------------------------------------------------------
+    # CPU baseline: the oracle on a bounded sample of the prefill workload
+    # ------------------------------------------------------------------
+    if not args.no_cpu_baseline and args.only in ("prefill", "all"):
+        result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), W, wl.rope_theta, args.cpu_seconds)
+
+    result["host"] = {"cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
+    print(json.dumps(result), flush=True)
+
+
+def context_timings(swa, synth, torch, dev):
+    """Chunked SWA prefill (4 x 4096 into a 4096-slot buffer) vs one full
+    causal pass at N = 16384, and the sink-streaming decode rate."""
+    bf = torch.bfloat16
+    wl = synth.workload(3)
+    N, Hq, Hkv, D, W, C = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.chunk
+    g = torch.Generator(device=dev).manual_seed(3003)
+    q = torch.randn((1, N, Hq, D), generator=g, device=dev).to(bf)
+    k = torch.randn((1, N, Hkv, D), generator=g, device=dev).to(bf)
+    v = torch.randn((1, N, Hkv, D), generator=g, device=dev).to(bf)
+    p = swa.make_params(1, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+    kc = torch.zeros((1, W, Hkv, D), dtype=bf, device=dev)
+    vc = torch.zeros_like(kc)
+    ws = torch.empty(swa.swa_prefill_workspace_bytes(p, C), dtype=torch.uint8, device=dev)
+    outc = torch.empty((1, C, Hq, D), dtype=bf, device=dev)
+    lsec = torch.empty((1, Hq, C), dtype=torch.float32, device=dev)
+    starts = [torch.tensor([c * C], dtype=torch.int32, device=dev) for c in range(N // C)]
+
+    qs = [q[:, c * C:(c + 1) * C].contiguous() for c in range(N // C)]
+    ks_ = [k[:, c * C:(c + 1) * C].contiguous() for c in range(N // C)]
+    vs_ = [v[:, c * C:(c + 1) * C].contiguous() for c in range(N // C)]
+
+    def chunked2():
+        for c in range(N // C):
+            swa.swa_prefill_chunk(p, qs[c], ks_[c], vs_[c], kc if c else None, vc if c else None,
+                                  starts[c], outc, lsec, ws)
+            swa.swa_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc)
+
+    pf = swa.make_params(1, Hq, Hkv, D, N, 0, 0.0, wl.rope_theta, bf)
+    wsf = torch.empty(swa.swa_prefill_workspace_bytes(pf, N), dtype=torch.uint8, device=dev)
+    outf = torch.empty((1, N, Hq, D), dtype=bf, device=dev)
+    lsef = torch.empty((1, Hq, N), dtype=torch.float32, device=dev)
+    z = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def full():
+        swa.swa_prefill_chunk(pf, q, k, v, None, None, z, outf, lsef, wsf)
+
+    def timeit(fn, reps=5):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    swa_ms = timeit(chunked2)
+    full_ms = timeit(full)
+    swa_flops = attn_flops(band_pairs(N, W))
+    full_flops = attn_flops(band_pairs(N, N))
+    ctx = {
+        "chunked_swa_prefill": {"workload": wl.name, "ms": round(swa_ms, 4),
+                                "tflops": round(swa_flops / (swa_ms * 1e-3) / 1e12, 1),
+                                "step": "4 x (prefill_chunk + cache_write)"},
+        "full_causal_prefill": {"seq_len": N, "ms": round(full_ms, 4),
+                                "tflops": round(full_flops / (full_ms * 1e-3) / 1e12, 1)},
+        "full_over_swa_time": round(full_ms / swa_ms, 3),
+        "pages_claim": "about 2x faster than vanilla attention at 16K tokens, W=4096 (no hardware stated)",
+    }
+    del q, k, v, outf, wsf
+
+    # sink streaming decode (B=16, 4 sinks + 4092 window): 256 steps
+    wl5 = synth.workload(5)
+    B, S = wl5.batch, wl5.n_slots
+    p5 = swa.make_params(B, Hq, Hkv, D, wl5.window, wl5.n_sink, 0.0, wl5.rope_theta, bf)
+    kc5 = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(bf)
+    vc5 = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(bf)
+    T = 256
+    qs5 = torch.randn((T, B, Hq, D), generator=g, device=dev).to(bf)
+    ks5 = torch.randn((T, B, 1, Hkv, D), generator=g, device=dev).to(bf)
+    vs5 = torch.randn((T, B, 1, Hkv, D), generator=g, device=dev).to(bf)
+    p0 = synth.positions(5, B, wl5.pos_lo, wl5.pos_hi).to(torch.int64)
+    pos = (p0[None, :] + torch.arange(T)[:, None]).to(torch.int32).to(dev)
+    o5 = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    l5 = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws5 = torch.empty(swa.swa_decode_workspace_bytes(p5), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+
+    def run5(flush_each):
+        tot = 0.0
+        for s in range(T):
+            if flush_each:
+                flush.fill_(s & 255)
+            swa.swa_cache_write(p5, ks5[s], vs5[s], pos[s], kc5, vc5)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            swa.swa_decode(p5, qs5[s], kc5, vc5, pos[s], o5, l5, ws5)
+            b.record()
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        return tot / T
+
+    run5(False)
+    ms_flushed = run5(True)
+    ms_warm = run5(False)
+    bytes5 = B * S * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2
+    ctx["sink_decode"] = {
+        "workload": wl5.name, "bytes_per_step": bytes5,
+        "ms_per_decode_mall_flushed": round(ms_flushed, 4),
+        "gbps_mall_flushed": round(bytes5 / (ms_flushed * 1e-3) / 1e9, 1),
+        "ms_per_decode_warm": round(ms_warm, 4),
+        "gbps_warm_cache_resident": round(bytes5 / (ms_warm * 1e-3) / 1e9, 1),
+        "note": "working set 256 MiB fits the 256 MB Infinity Cache; the flushed figure writes 512 MiB before each step",
+    }
+    return ctx
+
+
+def cpu_baseline(q, k, v, W, theta, target_s):
+    """The fp64 oracle, untuned, on a bounded sample of query rows of the
+    prefill workload; reported as algorithmic TFLOP/s on the host cores."""
+    import numpy as np
+    import oracle.swa_oracle as so
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except Exception:  # pragma: no cover
+        blas_threads = 0
+    q64 = q[0].to(dtype=__import__("torch").float64).numpy()
+    k64 = k[0].to(dtype=__import__("torch").float64).numpy()
+    v64 = v[0].to(dtype=__import__("torch").float64).numpy()
+    N = q64.shape[0]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(N)
+    done = 0
+    pairs = 0
+    t0 = time.perf_counter()
+    block = 128
+    while done < N:
+        rows = np.sort(order[done:done + block])
+        cache = so.RollingCache(k64.shape[1], k64.shape[2], W)
+        so.prefill_chunk(cache, q64, k64, v64, 0, theta, rows=rows)
+        pairs += sum(min(int(r) + 1, W) for r in rows)
+        done += len(rows)
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    flops = attn_flops(pairs)
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{done} of {N} query rows (random) of the n8192 w4096 prefill, fp64 NumPy, {el:.1f} s",
+            "seconds": round(el, 2), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -140,6 +140,26 @@ int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, co
                       int32_t chunk_len, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * swa_rope_keys — the key-rotation pass of swa_prefill_chunk on its own:
+ * k_rot[b][t] = RoPE(k[b][t], start_pos[b] + t) (digest "Methods": RoPE,
+ * theta from the architecture table), same layout as k.  With rope_theta == 0
+ * it is a copy.  For callers that keep rotated keys themselves.
+ */
+int swa_rope_keys(const swa_params* params, const void* k, const int32_t* start_pos,
+                  int32_t n_tok, void* k_rot, hipStream_t stream);
+
+/*
+ * swa_prefill_attention — the attention pass of swa_prefill_chunk on keys
+ * that are already rotated (k_rot from swa_rope_keys); queries are rotated on
+ * load.  Arguments and semantics otherwise as swa_prefill_chunk; it needs no
+ * workspace.  swa_prefill_chunk == swa_rope_keys + swa_prefill_attention.
+ */
+int swa_prefill_attention(const swa_params* params, const void* q, const void* k_rot,
+                          const void* v, const void* k_cache, const void* v_cache,
+                          const int32_t* start_pos, int32_t chunk_len, void* out, float* lse,
+                          hipStream_t stream);
+
 /* Bytes of workspace swa_decode needs (split-K partial results). */
 size_t swa_decode_workspace_bytes(const swa_params* params);
 

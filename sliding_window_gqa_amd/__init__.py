@@ -15,6 +15,7 @@ __all__ = [
     "SwaError", "swa_params", "make_params", "library", "LIB_PATH",
     "swa_cache_write", "swa_prefill_chunk", "swa_prefill_workspace_bytes",
     "swa_decode", "swa_decode_workspace_bytes", "swa_status_string",
+    "swa_rope_keys", "swa_prefill_attention",
     "swa_debug_slots", "swa_debug_mask",
     "SWA_OK", "SWA_ERR_NULL", "SWA_ERR_SHAPE", "SWA_ERR_DTYPE", "SWA_ERR_UNSUPPORTED",
     "SWA_ERR_WORKSPACE", "SWA_ERR_LAUNCH", "SWA_BF16", "SWA_F32",
@@ -56,6 +57,8 @@ _SIGNATURES = {
     "swa_cache_write": (ctypes.c_int, [_P, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "swa_prefill_workspace_bytes": (_sz, [_P, _i32]),
     "swa_prefill_chunk": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "swa_rope_keys": (ctypes.c_int, [_P, _vp, _vp, _i32, _vp, _vp]),
+    "swa_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "swa_decode_workspace_bytes": (_sz, [_P]),
     "swa_decode": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "swa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -190,6 +193,42 @@ def swa_prefill_chunk(params, q, k, v, k_cache, v_cache, start_pos, out=None, ls
         _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads, C)),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "swa_prefill_chunk")
+    return out, lse
+
+
+def swa_rope_keys(params, k, start_pos, k_rot=None, stream=None):
+    """Rotate keys k [B][n_tok][Hkv][D] at positions start_pos[b] + t; returns k_rot."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    shp = (params.batch, k.shape[1], params.n_kv_heads, params.head_dim)
+    if k_rot is None:
+        k_rot = torch.empty(shp, dtype=dt, device=k.device)
+    st = library().swa_rope_keys(ctypes.byref(params), _ptr(k, "k", dt, shp),
+                                 _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), k.shape[1],
+                                 _ptr(k_rot, "k_rot", dt, shp), _stream(stream))
+    _check(st, "swa_rope_keys")
+    return k_rot
+
+
+def swa_prefill_attention(params, q, k_rot, v, k_cache, v_cache, start_pos, out=None, lse=None,
+                          want_lse=True, stream=None):
+    """Attention pass of a prefill chunk over already-rotated keys; returns (out, lse)."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    C = q.shape[1]
+    qshp = (params.batch, C, params.n_q_heads, params.head_dim)
+    kshp = (params.batch, C, params.n_kv_heads, params.head_dim)
+    cshp = (params.batch, params.n_sink + params.window, params.n_kv_heads, params.head_dim)
+    if out is None:
+        out = torch.empty(qshp, dtype=dt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((params.batch, params.n_q_heads, C), dtype=torch.float32, device=q.device)
+    st = library().swa_prefill_attention(
+        ctypes.byref(params), _ptr(q, "q", dt, qshp), _ptr(k_rot, "k_rot", dt, kshp),
+        _ptr(v, "v", dt, kshp), _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp),
+        _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), C, _ptr(out, "out", dt, qshp),
+        _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads, C)), _stream(stream))
+    _check(st, "swa_prefill_attention")
     return out, lse
 
 

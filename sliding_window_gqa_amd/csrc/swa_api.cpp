@@ -81,6 +81,39 @@ size_t swa_prefill_workspace_bytes(const swa_params* params, int32_t chunk_len) 
          elem_size(params->dtype);
 }
 
+int swa_rope_keys(const swa_params* params, const void* k, const int32_t* start_pos,
+                  int32_t n_tok, void* k_rot, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k || !start_pos || !k_rot) return SWA_ERR_NULL;
+  if (n_tok < 1 || n_tok > (1 << 24)) return SWA_ERR_SHAPE;
+  return launched(swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k,
+                                          nullptr, start_pos, n_tok, k_rot, nullptr,
+                                          swa::kToDense, stream));
+}
+
+int swa_prefill_attention(const swa_params* params, const void* q, const void* k_rot,
+                          const void* v, const void* k_cache, const void* v_cache,
+                          const int32_t* start_pos, int32_t chunk_len, void* out, float* lse,
+                          hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k_rot || !v || !start_pos || !out) return SWA_ERR_NULL;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return SWA_ERR_NULL;
+  if (chunk_len < 1 || chunk_len > (1 << 24)) return SWA_ERR_SHAPE;
+  const RopeTab rt = rope_table(params);
+  hipError_t e;
+  if (fast_path(params))
+    e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, k_rot, v, k_cache, v_cache, start_pos,
+                                         chunk_len, out, lse, stream);
+  else
+    e = swa::launch_prefill_generic(sh, rt, params->dtype == SWA_F32, q, k_rot, v, k_cache,
+                                    v_cache, start_pos, chunk_len, out, lse, stream);
+  return launched(e);
+}
+
 int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, const void* v,
                       const void* k_cache, const void* v_cache, const int32_t* start_pos,
                       int32_t chunk_len, void* out, float* lse, void* workspace,
@@ -93,19 +126,11 @@ int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, co
   if (chunk_len < 1 || chunk_len > (1 << 24)) return SWA_ERR_SHAPE;
   const size_t need = swa_prefill_workspace_bytes(params, chunk_len);
   if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
-  const RopeTab rt = rope_table(params);
-  const bool f32 = params->dtype == SWA_F32;
-  // rotated chunk keys -> workspace (values are read as given)
-  hipError_t e = swa::launch_cache_write(sh, rt, f32, k, v, start_pos, chunk_len, workspace,
-                                         nullptr, swa::kToDense, stream);
-  if (e != hipSuccess) return SWA_ERR_LAUNCH;
-  if (fast_path(params))
-    e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, workspace, v, k_cache, v_cache, start_pos,
-                                         chunk_len, out, lse, stream);
-  else
-    e = swa::launch_prefill_generic(sh, rt, f32, q, workspace, v, k_cache, v_cache, start_pos,
-                                    chunk_len, out, lse, stream);
-  return launched(e);
+  // rotated chunk keys -> workspace, then attention over them
+  st = swa_rope_keys(params, k, start_pos, chunk_len, workspace, stream);
+  if (st != SWA_OK) return st;
+  return swa_prefill_attention(params, q, workspace, v, k_cache, v_cache, start_pos, chunk_len,
+                               out, lse, stream);
 }
 
 size_t swa_decode_workspace_bytes(const swa_params* params) {

@@ -27,6 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"swa_cache_write", "swa_prefill_chunk", "swa_decode", "swa_decode_workspace_bytes",
+            "swa_rope_keys", "swa_prefill_attention",
             "swa_prefill_workspace_bytes", "swa_status_string", "swa_debug_slots",
             "swa_debug_mask"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
@@ -64,6 +65,8 @@ def test_bad_params_rejected_everywhere(bad, code):
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_debug_slots(bp, FAKE, 4, FAKE, None) == code
+    assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, FAKE, None) == code
+    assert lib.swa_prefill_attention(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None) == code
     assert lib.swa_decode_workspace_bytes(bp) == 0
     assert lib.swa_prefill_workspace_bytes(bp, 16) == 0
 
@@ -80,6 +83,9 @@ def test_null_pointers_rejected():
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     assert lib.swa_debug_mask(bp, 5, None, 4, FAKE, None) == swa.SWA_ERR_NULL
+    assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, None, None) == swa.SWA_ERR_NULL
+    assert lib.swa_prefill_attention(bp, FAKE, None, FAKE, None, None, FAKE, 16, FAKE, None, None) == swa.SWA_ERR_NULL
+    assert lib.swa_prefill_attention(bp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, None, None) == swa.SWA_ERR_NULL
 
 
 def test_sizes_and_workspace_rejected():
