@@ -10,20 +10,22 @@
 //
 // Fast kernel (bf16, head_dim 128, GQA group 4), MI355X / gfx950:
 //  * One work-group = 64 query positions x the 4 query heads of one KV head
-//    (256 query rows), 4 waves; wave w owns positions t0+16w .. t0+16w+15 for
-//    all 4 heads, so the four 16-row query blocks of a wave share one mask.
+//    (256 query rows), 8 waves, 2 per SIMD so that one wave's softmax runs
+//    while the other's matrix instructions do.  Wave w owns positions
+//    t0+16(w&3) .. +15 for 2 of the 4 heads: 32 query rows, about 190 VGPRs.
 //  * Key tiles of 64 keys.  K and V tiles are staged in LDS once per
 //    work-group and used by all 4 heads (the GQA sharing of explainer How It
-//    Works 1).  Tiles outside the band i-W < j <= i of the work-group are never
-//    visited, so the work is O(N*W); a wave skips the matrix work of tiles
-//    outside its own band and masks only the tiles that cut the diagonal or the
-//    window edge.
+//    Works 1), double-buffered so one barrier per tile suffices.  Tiles outside
+//    the band i-W < j <= i of the work-group are never visited, so the work is
+//    O(N*W); a wave skips the matrix work of tiles outside its own band and
+//    masks only the tiles that cut the diagonal or the window edge.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: in the
 //    transposed form every lane owns one query column, so the softmax row
-//    statistics stay in one lane plus a 4-lane exchange, and the score
-//    accumulator is already the B operand of the PV product.
-//  * V is transposed into LDS when it is stored, so every A operand of the PV
-//    product is one 16-byte LDS read.
+//    statistics stay in one lane plus a 4-lane exchange (permlane swaps), and
+//    the score accumulator is already the B operand of the PV product.
+//  * V stays row-major in LDS; the A operand of the PV product is read with
+//    the transposing LDS load ds_read_b64_tr_b16.  Both tiles use XOR-swizzled
+//    16-byte chunks so the operand reads are free of bank conflicts.
 //  * Online softmax in the log2 domain; the output accumulator is rescaled
 //    only when a running max grows by more than 2^8 (the result is the same:
 //    numerator and denominator carry the same stale max).
@@ -42,22 +44,35 @@
 namespace swa {
 namespace {
 
-constexpr int BM = 64;     // query positions per work-group
-constexpr int BN = 64;     // keys per tile
-constexpr int HD = 128;    // head_dim of the fast kernel
-constexpr int KPITCH = 272;  // bytes per K row in LDS (256 + 16 pad)
-constexpr int VPITCH = 144;  // bytes per V^T row in LDS (128 + 16 pad)
+constexpr int BM = 64;       // query positions per work-group
+constexpr int BN = 64;       // keys per tile
+constexpr int HD = 128;      // head_dim of the fast kernel
+constexpr int ROWB = HD * 2; // bytes of one K or V row
+constexpr int TILEB = BN * ROWB;  // bytes of one K (or V) tile in LDS
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
 
-__device__ inline float wave_max_g(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// XOR swizzles of the 16-byte chunks of a 256-byte LDS row, chosen so that the
+// QK^T operand reads (16 lanes: 16 rows, one chunk) and the transposing PV
+// operand reads (4 consecutive rows, 2 chunks per 16 lanes) hit distinct banks.
+__device__ inline int k_off(int r, int c) { return r * ROWB + ((c ^ (r & 15)) << 4); }
+__device__ inline int v_off(int r, int c) { return r * ROWB + ((c ^ (((r & 7) << 1) | ((r >> 3) & 1))) << 4); }
+
+// max / sum over the 4 lanes l, l^16, l^32, l^48 (one query column)
+__device__ inline float xg_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ inline float wave_sum_g(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ inline float xg_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 struct PrefillArgs {
@@ -92,10 +107,11 @@ __device__ inline const uint16_t* key_row(const PrefillArgs& a, int which, int b
   return base + (((long long)b * a.sh.S + slot) * a.sh.Hkv + kvh) * HD;
 }
 
-__global__ void __launch_bounds__(256, 1) prefill_bf16_d128_g4_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[BN * KPITCH + HD * VPITCH];
-  uint8_t* Ks = smem;
-  uint8_t* Vt = smem + BN * KPITCH;
+// 8 waves: wave w owns positions t0 + 16*(w&3) .. +15 and query heads
+// h0 + 2*(w>>2) + {0,1}; each lane owns one query column of the two 16-row
+// query blocks.  K/V tiles are double-buffered in LDS.
+__global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * TILEB];
 
   const Shape& sh = a.sh;
   // ---- work mapping: XCD-contiguous, longest tiles first ----
@@ -115,45 +131,44 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_d128_g4_kernel(PrefillArg
   const int s0 = a.start[b];
   const int C = a.C;
   const int t0 = qt * BM;
-  const int q0w = t0 + 16 * w;   // first query of this wave (chunk-relative)
-  const int tq = q0w + i;        // this lane's query
-  const int h0 = kvh * 4;
+  const int q0w = t0 + 16 * (w & 3);   // first query of this wave (chunk-relative)
+  const int tq = q0w + i;              // this lane's query
+  const int hw = kvh * 4 + 2 * (w >> 2);  // first query head of this wave
   const int W = sh.W;
 
   // ---- Q prologue: rotated, rounded to bf16, in the B-operand layout ----
-  // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
-  bf16x8 qf[4][4];
+  // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head hw+qb.
+  bf16x8 qf[2][4];
   {
-    float cs[4][4], sn[4][4];
     const int I = s0 + tq;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
+      float cs[4], sn[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         if (sh.rope) {
-          rope_cs(I, a.rt.freq[4 * (4 * kk + g) + jj], cs[kk][jj], sn[kk][jj]);
+          rope_cs(I, a.rt.freq[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
         } else {
-          cs[kk][jj] = 1.f;
-          sn[kk][jj] = 0.f;
+          cs[jj] = 1.f;
+          sn[jj] = 0.f;
         }
       }
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int qb = 0; qb < 2; ++qb) {
         u32x4 wv = {0u, 0u, 0u, 0u};
         if (tq < C)
           wv = *reinterpret_cast<const u32x4*>(
-              a.q + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD + 8 * (4 * kk + g));
+              a.q + (((long long)b * C + tq) * sh.Hq + hw + qb) * HD + 8 * (4 * kk + g));
         u32x4 r;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
-          rotate(x0, x1, cs[kk][jj], sn[kk][jj]);
+          rotate(x0, x1, cs[jj], sn[jj]);
           r[jj] = pack_bf16(x0, x1);
         }
         qf[qb][kk] = __builtin_bit_cast(bf16x8, r);
       }
+    }
   }
 
   // ---- tile list ----
@@ -164,57 +179,38 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_d128_g4_kernel(PrefillArg
   const int kmin = max(k_lo, k_clip);
   const int n_band = 1 - kmin;
   const int n_tiles = n_band + (has_sink_tile ? 1 : 0);
-
-  // tile it -> (is_sink, first key position relative to s0 for band tiles)
   auto tile_u0 = [&](int it) { return t0 + BN * (kmin + it - (has_sink_tile ? 1 : 0)); };
 
-  u32x4 kreg[4], vreg[4];
+  // ---- cooperative tile loads: thread -> rows r, r+32, chunk c, for K and V ----
+  const int lr = tid >> 4, lc = tid & 15;
+  u32x4 stage[4];
   auto load_tile = [&](int it) {
     const bool is_sink = has_sink_tile && it == 0;
     const int base = is_sink ? 0 : s0 + tile_u0(it);   // absolute position of row 0
-    const int c = tid & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = (tid >> 4) + 16 * j;
-      const int P = base + r;
-      const uint16_t* src = (is_sink && P >= sh.n_sink) ? nullptr : key_row(a, 0, b, kvh, s0, P);
-      kreg[j] = src ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * (tid >> 4) + e;
-      const int P = base + r;
-      const uint16_t* src = (is_sink && P >= sh.n_sink) ? nullptr : key_row(a, 1, b, kvh, s0, P);
-      vreg[e] = src ? *reinterpret_cast<const u32x4*>(src + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 2; ++j) {
+      const int P = base + lr + 32 * j;
+      const bool ok = !(is_sink && P >= sh.n_sink);
+      const uint16_t* ks = ok ? key_row(a, 0, b, kvh, s0, P) : nullptr;
+      const uint16_t* vs = ok ? key_row(a, 1, b, kvh, s0, P) : nullptr;
+      stage[j] = ks ? *reinterpret_cast<const u32x4*>(ks + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
+      stage[2 + j] = vs ? *reinterpret_cast<const u32x4*>(vs + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_tile = [&]() {
-    const int c = tid & 15;
+  auto store_tile = [&](int buf) {
+    uint8_t* Kb = smem + buf * 2 * TILEB;
+    uint8_t* Vb = Kb + TILEB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * j) * KPITCH + c * 16) = kreg[j];
-    // V^T: key k of the tile is stored at column pos(k) = 32(k/32) + 8((k%16)/4)
-    // + 4((k%32)/16) + k%4, so that the 8 keys one lane needs for a PV step
-    // (4 from each of two 16-key score blocks) are 16 contiguous bytes.
-    const int quad = tid >> 4;
-    const int pos = 32 * (quad >> 3) + 8 * (quad & 3) + 4 * ((quad >> 2) & 1);
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      const int wd = jd >> 1;
-      const bool hi = jd & 1;
-      uint32_t e0 = hi ? (vreg[0][wd] >> 16) : (vreg[0][wd] & 0xffffu);
-      uint32_t e1 = hi ? (vreg[1][wd] >> 16) : (vreg[1][wd] & 0xffffu);
-      uint32_t e2 = hi ? (vreg[2][wd] >> 16) : (vreg[2][wd] & 0xffffu);
-      uint32_t e3 = hi ? (vreg[3][wd] >> 16) : (vreg[3][wd] & 0xffffu);
-      u32x2 val = {e0 | (e1 << 16), e2 | (e3 << 16)};
-      *reinterpret_cast<u32x2*>(Vt + (8 * c + jd) * VPITCH + pos * 2) = val;
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<u32x4*>(Kb + k_off(lr + 32 * j, lc)) = stage[j];
+      *reinterpret_cast<u32x4*>(Vb + v_off(lr + 32 * j, lc)) = stage[2 + j];
     }
   };
 
-  float m_run[4], l_run[4];
-  floatx4 o[8][4];
+  float m_run[2], l_run[2];
+  floatx4 o[8][2];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < 2; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
@@ -222,16 +218,18 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_d128_g4_kernel(PrefillArg
   }
   const float c2 = sh.scale_log2;
 
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(1);
+  }
   for (int it = 0; it < n_tiles; ++it) {
     __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(it + 1);
+    const uint8_t* Kb = smem + (it & 1) * 2 * TILEB;
+    lds_u8* Vb = (lds_u8*)smem + (it & 1) * 2 * TILEB + TILEB;
 
     const bool is_sink = has_sink_tile && it == 0;
     const int u0 = is_sink ? 0 : tile_u0(it);
-    // classify this tile for this wave (wave-uniform)
     bool any, full;
     if (is_sink) {
       any = (s0 + q0w + 15 - W) >= 0;
@@ -240,110 +238,124 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_d128_g4_kernel(PrefillArg
       any = !(u0 > q0w + 15 || u0 + BN - 1 <= q0w - W || s0 + u0 + BN - 1 < 0);
       full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
     }
-    if (!any) continue;
-
-    // ---- S^T = K Q^T: s[kb][qb] rows = keys 16kb+4g+r, column = query i ----
-    floatx4 s[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 ka[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        ka[kb] = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + i) * KPITCH + (4 * kk + g) * 16);
+    if (any) {
+      // ---- S^T = K Q^T: s[kb][qb] rows = keys 16kb+4g+r, column = query i ----
+      floatx4 s[4][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qf[qb][kk], s[kb][qb], 0, 0, 0);
-    }
-
-    // ---- mask the tiles that cut the diagonal, the window edge or position 0 ----
-    if (!full) {
-      const int I = s0 + tq;
+        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kr_ = 16 * kb + 4 * g + r;
-          bool ok;
-          if (is_sink) {
-            const int P = kr_;
-            ok = P < sh.n_sink && P <= I - W;
-          } else {
-            const int u = u0 + kr_;
-            ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
-          }
-          if (!ok) {
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kb + k_off(16 * kb + i, 4 * kk + g));
 #pragma unroll
-            for (int qb = 0; qb < 4; ++qb) s[kb][qb][r] = -INFINITY;
-          }
+          for (int qb = 0; qb < 2; ++qb)
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][kk], s[kb][qb], 0, 0, 0);
         }
-    }
-
-    // ---- online softmax (log2 domain) ----
-    bf16x8 pb[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = wave_max_g(mx) * c2;
-      const bool need = mx > m_run[qb] + kTau;
-      const float alpha = need ? exp2f(m_run[qb] - mx) : 1.f;
-      if (need) m_run[qb] = mx;
-      if (__any(need)) {
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
       }
-      const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float p[4][4];
-      float ls = 0.f;
+
+      // ---- mask the tiles that cut the diagonal, the window edge or position 0 ----
+      if (!full) {
+        const int I = s0 + tq;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[kb][r] = exp2f(fmaf(s[kb][qb][r], c2, -msub));
-          ls += p[kb][r];
+          for (int r = 0; r < 4; ++r) {
+            const int kr_ = 16 * kb + 4 * g + r;
+            bool ok;
+            if (is_sink) {
+              ok = kr_ < sh.n_sink && kr_ <= I - W;
+            } else {
+              const int u = u0 + kr_;
+              ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
+            }
+            if (!ok) {
+              s[kb][0][r] = -INFINITY;
+              s[kb][1][r] = -INFINITY;
+            }
+          }
+      }
+
+      // ---- online softmax (log2 domain), P -> bf16 B operands ----
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3]));
+#pragma unroll
+        for (int kb = 1; kb < 4; ++kb)
+          mx = fmaxf(mx, fmaxf(fmaxf(s[kb][qb][0], s[kb][qb][1]), fmaxf(s[kb][qb][2], s[kb][qb][3])));
+        mx = xg_max(mx) * c2;
+        const bool need = mx > m_run[qb] + kTau;
+        if (__builtin_expect(__any(need), 0)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.f;
+          if (need) m_run[qb] = mx;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
         }
-      l_run[qb] += ls;
+        const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        float ls = 0.f;
+        float pv[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pv[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -msub));
+            ls += pv[kb][r];
+          }
+        l_run[qb] += ls;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 pk;
+          pk[0] = pack_bf16(pv[2 * s2][0], pv[2 * s2][1]);
+          pk[1] = pack_bf16(pv[2 * s2][2], pv[2 * s2][3]);
+          pk[2] = pack_bf16(pv[2 * s2 + 1][0], pv[2 * s2 + 1][1]);
+          pk[3] = pack_bf16(pv[2 * s2 + 1][2], pv[2 * s2 + 1][3]);
+          pb[s2][qb] = __builtin_bit_cast(bf16x8, pk);
+        }
+      }
+
+      // ---- O^T += V^T P^T: o[db][qb] rows = d 16db+4g+r, column = query i ----
+      // The A operand (16 d x 8 keys per lane) comes from two transposing LDS
+      // reads: lane i of a 16-lane group addresses key base+i/4, d 16db+4(i%4),
+      // and receives V[base+e][16db+i] for e = 0..3.
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pk;
-        pk[0] = pack_bf16(p[2 * s2][0], p[2 * s2][1]);
-        pk[1] = pack_bf16(p[2 * s2][2], p[2 * s2][3]);
-        pk[2] = pack_bf16(p[2 * s2 + 1][0], p[2 * s2 + 1][1]);
-        pk[3] = pack_bf16(p[2 * s2 + 1][2], p[2 * s2 + 1][3]);
-        pb[s2][qb] = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int cidx = 2 * db + ((i & 3) >> 1);
+          const int boff = 8 * (i & 1);
+          const int r0 = 32 * s2 + 4 * g + (i >> 2);
+          const int r1 = r0 + 16;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<lds_v4i16*>(Vb + v_off(r0, cidx) + boff));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<lds_v4i16*>(Vb + v_off(r1, cidx) + boff));
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[s2][qb],
+                                                                o[db][qb], 0, 0, 0);
+        }
       }
     }
-
-    // ---- O^T += V^T P^T: o[db][qb] rows = d 16db+4g+r, column = query i ----
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(Vt + (16 * db + i) * VPITCH + (32 * s2 + 8 * g) * 2);
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[s2][qb], o[db][qb], 0, 0, 0);
-      }
+    // stage the tile after next while this one is being consumed
+    if (it + 1 < n_tiles) {
+      store_tile((it + 1) & 1);
+      if (it + 2 < n_tiles) load_tile(it + 2);
+    }
   }
 
   // ---- epilogue: O / l, LSE ----
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const float lt = wave_sum_g(l_run[qb]);
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = xg_sum(l_run[qb]);
     const float inv = 1.f / lt;
     if (tq < C) {
-      uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD;
+      uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + hw + qb) * HD;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         u32x2 val = {pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv),
@@ -351,7 +363,7 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_d128_g4_kernel(PrefillArg
         *reinterpret_cast<u32x2*>(dst + 16 * db + 4 * g) = val;
       }
       if (a.lse && g == 0)
-        a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (m_run[qb] + log2f(lt)) * 0.69314718055994531f;
+        a.lse[((long long)b * sh.Hq + hw + qb) * C + tq] = (m_run[qb] + log2f(lt)) * 0.69314718055994531f;
     }
   }
 }
@@ -460,7 +472,7 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   const long long nwg = (long long)a.n_qtiles * sh.Hkv * sh.B;
-  prefill_bf16_d128_g4_kernel<<<dim3((unsigned)nwg), dim3(256), 0, st>>>(a);
+  prefill_bf16_d128_g4_kernel<<<dim3((unsigned)nwg), dim3(512), 0, st>>>(a);
   return hipGetLastError();
 }
 
