@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-context", action="store_true", help="skip the chunked / full-causal / sink timings")
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all",
                     help="restrict the GPU work (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (scales HBM byte counters)")
     return ap.parse_args()
 
 
@@ -76,6 +78,15 @@ def main():
     torch.cuda.set_device(dev)
     bf = torch.bfloat16
     result = {"metric": METRIC}
+
+    if args.copy_calibration_mib:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nb
+        del src, dst
 
     # ------------------------------------------------------------------
     # prefill: N=8192, W=4096 (the headline workload)

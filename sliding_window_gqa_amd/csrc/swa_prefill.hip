@@ -38,6 +38,8 @@
 // not cover (e.g. the float32 path).
 #include <math.h>
 
+#include <type_traits>
+
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
 
@@ -75,6 +77,13 @@ __device__ inline float xg_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// max of the 4 lanes of a float4 (NaN-propagating IEEE maximum: no
+// canonicalising moves, v_maximum3_f32 on gfx950)
+__device__ inline float vmax4(floatx4 v) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]),
+                                       __builtin_elementwise_maximum(v[2], v[3]));
+}
+
 struct PrefillArgs {
   Shape sh;
   RopeTab rt;
@@ -90,28 +99,22 @@ struct PrefillArgs {
   float* lse;
 };
 
-// Pointer to row `which` (0 = K, 1 = V) of the key at absolute position P for
-// sequence b / kv head kvh, or null if that key does not exist.
-__device__ inline const uint16_t* key_row(const PrefillArgs& a, int which, int b, int kvh, int s0,
-                                          int P) {
-  if (P < 0) return nullptr;
-  const int u = P - s0;
-  if (u >= 0) {
-    if (u >= a.C) return nullptr;
-    const uint16_t* base = which ? a.v : a.kr;
-    return base + (((long long)b * a.C + u) * a.sh.Hkv + kvh) * HD;
-  }
-  const uint16_t* base = which ? a.vc : a.kc;
-  if (!base) return nullptr;
-  const int slot = slot_of(P, a.sh.W, a.sh.n_sink);
-  return base + (((long long)b * a.sh.S + slot) * a.sh.Hkv + kvh) * HD;
-}
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most n vector-memory operations of this wave
+// are outstanding.
+#define SWA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
-// 8 waves: wave w owns positions t0 + 16*(w&3) .. +15 and query heads
-// h0 + 2*(w>>2) + {0,1}; each lane owns one query column of the two 16-row
-// query blocks.  K/V tiles are double-buffered in LDS.
+constexpr int NBUF = 3;              // LDS ring of K/V tiles (prefetch distance 2)
+constexpr int LOADS_PER_TILE = 4;    // direct-to-LDS loads per wave per tile (2 K, 2 V)
+
+// One work-group: 64 query positions x 4 query heads of one KV head, 8 waves.
+// Wave w owns positions t0 + 16*(w&3) .. +15 and query heads hw, hw+1 with
+// hw = 4*kvh + 2*(w>>2); lane (i, g) owns query column i of both 16-row
+// query blocks.  K/V tiles of 64 keys go global -> LDS directly
+// (global_load_lds_dwordx4, 1 KB per wave instruction) into a 3-deep ring.
 __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * 2 * TILEB];
+  __shared__ double rope_freq[kMaxPairs];
 
   const Shape& sh = a.sh;
   // ---- work mapping: XCD-contiguous, longest tiles first ----
@@ -131,13 +134,111 @@ __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a
   const int s0 = a.start[b];
   const int C = a.C;
   const int t0 = qt * BM;
-  const int q0w = t0 + 16 * (w & 3);   // first query of this wave (chunk-relative)
-  const int tq = q0w + i;              // this lane's query
+  const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
+  const int tq = q0w + i;                 // this lane's query
   const int hw = kvh * 4 + 2 * (w >> 2);  // first query head of this wave
   const int W = sh.W;
+  const int S = sh.S;
+  const int nsink = sh.n_sink;
+
+  // ---- tile list: [sink tile] + band tiles k = kmin..0 (u0 = t0 + 64k) ----
+  const int tq_last = min(t0 + BM, C) - 1;
+  const bool has_sink_tile = nsink > 0 && (s0 + tq_last - W) >= 0;
+  const int k_lo = -((W - 1 + BN - 1) / BN);
+  const int k_clip = -((s0 + t0 + BN - 1) / BN);
+  const int kmin = max(k_lo, k_clip);
+  const int n_tiles = (1 - kmin) + (has_sink_tile ? 1 : 0);
+  const int sink_off = has_sink_tile ? 1 : 0;
+
+  // ---- direct-to-LDS tile loads ----
+  // Wave w fills rows 8w .. 8w+7 of the K and of the V tile, 4 rows per
+  // instruction; lane l lands at row 8w+4j+l/16, stored chunk l%16, and so
+  // fetches the global chunk that the row's XOR swizzle puts there.
+  const long long rowstride_c = (long long)sh.Hkv * HD;                // elements between tokens
+  const uint16_t* kchunk = a.kr + ((long long)b * C * sh.Hkv + kvh) * HD;
+  const uint16_t* vchunk = a.v + ((long long)b * C * sh.Hkv + kvh) * HD;
+  const uint16_t* kcache = a.kc ? a.kc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
+  const uint16_t* vcache = a.vc ? a.vc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
+  // lane-constant byte offsets of this lane's two rows (8w+4j+lane/16) in a
+  // run of consecutive source rows, including the chunk swizzle
+  const int rowstride_b = sh.Hkv * ROWB;
+  int voff_k[2], voff_v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * w + 4 * j + (lane >> 4);
+    const int pos = lane & 15;
+    voff_k[j] = row * rowstride_b + 16 * (pos ^ (row & 15));
+    voff_v[j] = row * rowstride_b + 16 * (pos ^ (((row & 7) << 1) | ((row >> 3) & 1)));
+  }
+  auto issue_tile = [&](int it) {
+    const int buf = it % NBUF;
+    const bool is_sink = has_sink_tile && it == 0;
+    const int u0 = is_sink ? 0 : t0 + BN * (kmin + it - sink_off);
+    // fast path: the 64 rows are 64 consecutive rows of one tensor
+    const uint16_t* kbase = nullptr;
+    const uint16_t* vbase = nullptr;
+    if (!is_sink) {
+      if (u0 >= 0) {
+        if (u0 + BN <= C) {
+          kbase = kchunk + (long long)u0 * rowstride_c;
+          vbase = vchunk + (long long)u0 * rowstride_c;
+        }
+      } else {
+        const int P0 = s0 + u0;
+        if (P0 >= nsink) {
+          const int slot0 = nsink + (P0 - nsink) % W;
+          if (slot0 + BN <= S) {
+            kbase = kcache + (long long)slot0 * rowstride_c;
+            vbase = vcache + (long long)slot0 * rowstride_c;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint8_t* kl = smem + (buf * 2) * TILEB + (8 * w + 4 * j) * ROWB;
+      uint8_t* vl = kl + TILEB;
+      const uint8_t* kp;
+      const uint8_t* vp;
+      if (kbase) {
+        kp = reinterpret_cast<const uint8_t*>(kbase) + voff_k[j];
+        vp = reinterpret_cast<const uint8_t*>(vbase) + voff_v[j];
+      } else {
+        // edge tiles: each row located separately, clamped to a row that
+        // exists (rows that are not keys of any query are masked later)
+        const int row = 8 * w + 4 * j + (lane >> 4);
+        const uint16_t* kb;
+        const uint16_t* vb;
+        int roff;
+        if (is_sink) {
+          const int P = min(row, nsink - 1);
+          if (P < s0 && kcache) {
+            kb = kcache; vb = vcache; roff = P;
+          } else {
+            kb = kchunk; vb = vchunk; roff = min(max(P - s0, 0), C - 1);
+          }
+        } else if (u0 >= 0) {
+          kb = kchunk; vb = vchunk; roff = min(u0 + row, C - 1);
+        } else {
+          const int P = max(s0 + u0 + row, 0);
+          kb = kcache; vb = vcache;
+          roff = P < nsink ? P : nsink + (P - nsink) % W;
+        }
+        const long long rb = (long long)(roff - row) * rowstride_c;   // voff already holds row*stride
+        kp = reinterpret_cast<const uint8_t*>(kb + rb) + voff_k[j];
+        vp = reinterpret_cast<const uint8_t*>(vb + rb) + voff_v[j];
+      }
+      __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)kl, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)vl, 16, 0, 0);
+    }
+  };
+  // kick off the first two tiles before the Q prologue
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
 
   // ---- Q prologue: rotated, rounded to bf16, in the B-operand layout ----
-  // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head hw+qb.
+  if (tid < kMaxPairs) rope_freq[tid] = a.rt.freq[tid];
+  __syncthreads();
   bf16x8 qf[2][4];
   {
     const int I = s0 + tq;
@@ -147,7 +248,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         if (sh.rope) {
-          rope_cs(I, a.rt.freq[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
+          rope_cs(I, rope_freq[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
         } else {
           cs[jj] = 1.f;
           sn[jj] = 0.f;
@@ -171,102 +272,53 @@ __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a
     }
   }
 
-  // ---- tile list ----
-  const int tq_last = min(t0 + BM, C) - 1;
-  const bool has_sink_tile = sh.n_sink > 0 && (s0 + tq_last - W) >= 0;
-  const int k_lo = -((W - 1 + BN - 1) / BN);
-  const int k_clip = -((s0 + t0 + BN - 1) / BN);
-  const int kmin = max(k_lo, k_clip);
-  const int n_band = 1 - kmin;
-  const int n_tiles = n_band + (has_sink_tile ? 1 : 0);
-  auto tile_u0 = [&](int it) { return t0 + BN * (kmin + it - (has_sink_tile ? 1 : 0)); };
-
-  // ---- cooperative tile loads: thread -> rows r, r+32, chunk c, for K and V ----
-  const int lr = tid >> 4, lc = tid & 15;
-  u32x4 stage[4];
-  auto load_tile = [&](int it) {
-    const bool is_sink = has_sink_tile && it == 0;
-    const int base = is_sink ? 0 : s0 + tile_u0(it);   // absolute position of row 0
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int P = base + lr + 32 * j;
-      const bool ok = !(is_sink && P >= sh.n_sink);
-      const uint16_t* ks = ok ? key_row(a, 0, b, kvh, s0, P) : nullptr;
-      const uint16_t* vs = ok ? key_row(a, 1, b, kvh, s0, P) : nullptr;
-      stage[j] = ks ? *reinterpret_cast<const u32x4*>(ks + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
-      stage[2 + j] = vs ? *reinterpret_cast<const u32x4*>(vs + 8 * lc) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* Kb = smem + buf * 2 * TILEB;
-    uint8_t* Vb = Kb + TILEB;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<u32x4*>(Kb + k_off(lr + 32 * j, lc)) = stage[j];
-      *reinterpret_cast<u32x4*>(Vb + v_off(lr + 32 * j, lc)) = stage[2 + j];
-    }
-  };
-
-  float m_run[2], l_run[2];
+  float m_run[2];
   floatx4 o[8][2];
+  // row sums of P accumulate on the matrix core: an all-ones A operand makes
+  // every row of lsum[qb] the sum over keys of P for this lane's query
+  floatx4 lsum[2];
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    lsum[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = sh.scale_log2;
+  const int I = s0 + tq;
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(1);
-  }
-  for (int it = 0; it < n_tiles; ++it) {
-    __syncthreads();
-    const uint8_t* Kb = smem + (it & 1) * 2 * TILEB;
-    lds_u8* Vb = (lds_u8*)smem + (it & 1) * 2 * TILEB + TILEB;
-
-    const bool is_sink = has_sink_tile && it == 0;
-    const int u0 = is_sink ? 0 : tile_u0(it);
-    bool any, full;
-    if (is_sink) {
-      any = (s0 + q0w + 15 - W) >= 0;
-      full = false;
-    } else {
-      any = !(u0 > q0w + 15 || u0 + BN - 1 <= q0w - W || s0 + u0 + BN - 1 < 0);
-      full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
-    }
-    if (any) {
-      // ---- S^T = K Q^T: s[kb][qb] rows = keys 16kb+4g+r, column = query i ----
-      floatx4 s[4][2];
+  // One tile, as two 32-key halves: S^T = K Q^T, mask (MK 1: band edge or
+  // diagonal, 2: sink tile), online softmax, O^T += V^T P^T.
+  auto tile_body = [&](const uint8_t* Kb, lds_u8* Vb, int u0, auto mask_kind) {
+    constexpr int MK = decltype(mask_kind)::value;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int h = 0; h < 2; ++h) {
+      // s[kb][qb]: rows = keys 32h + 16kb + 4g + r, column = query i
+      floatx4 s[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kb + k_off(16 * kb + i, 4 * kk + g));
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kb + k_off(32 * h + 16 * kb + i, 4 * kk + g));
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
             s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][kk], s[kb][qb], 0, 0, 0);
         }
       }
-
-      // ---- mask the tiles that cut the diagonal, the window edge or position 0 ----
-      if (!full) {
-        const int I = s0 + tq;
+      if constexpr (MK != 0) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int kr_ = 16 * kb + 4 * g + r;
+            const int kr_ = 32 * h + 16 * kb + 4 * g + r;
             bool ok;
-            if (is_sink) {
-              ok = kr_ < sh.n_sink && kr_ <= I - W;
+            if constexpr (MK == 2) {
+              ok = kr_ < nsink && kr_ <= I - W;
             } else {
               const int u = u0 + kr_;
               ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
@@ -277,82 +329,80 @@ __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a
             }
           }
       }
-
-      // ---- online softmax (log2 domain), P -> bf16 B operands ----
-      bf16x8 pb[2][2];
+      bf16x8 pb[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3]));
-#pragma unroll
-        for (int kb = 1; kb < 4; ++kb)
-          mx = fmaxf(mx, fmaxf(fmaxf(s[kb][qb][0], s[kb][qb][1]), fmaxf(s[kb][qb][2], s[kb][qb][3])));
+        float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
         mx = xg_max(mx) * c2;
         const bool need = mx > m_run[qb] + kTau;
         if (__builtin_expect(__any(need), 0)) {
           const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.f;
           if (need) m_run[qb] = mx;
-          l_run[qb] *= alpha;
+          lsum[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
         }
         const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-        float ls = 0.f;
-        float pv[4][4];
+        float pv[2][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pv[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -msub));
-            ls += pv[kb][r];
-          }
-        l_run[qb] += ls;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 pk;
-          pk[0] = pack_bf16(pv[2 * s2][0], pv[2 * s2][1]);
-          pk[1] = pack_bf16(pv[2 * s2][2], pv[2 * s2][3]);
-          pk[2] = pack_bf16(pv[2 * s2 + 1][0], pv[2 * s2 + 1][1]);
-          pk[3] = pack_bf16(pv[2 * s2 + 1][2], pv[2 * s2 + 1][3]);
-          pb[s2][qb] = __builtin_bit_cast(bf16x8, pk);
-        }
+          for (int r = 0; r < 4; ++r) pv[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -msub));
+        u32x4 pk;
+        pk[0] = pack_bf16(pv[0][0], pv[0][1]);
+        pk[1] = pack_bf16(pv[0][2], pv[0][3]);
+        pk[2] = pack_bf16(pv[1][0], pv[1][1]);
+        pk[3] = pack_bf16(pv[1][2], pv[1][3]);
+        pb[qb] = __builtin_bit_cast(bf16x8, pk);
       }
+      // A operand of the PV product from two transposing LDS reads: lane i of
+      // a 16-lane group addresses key base+i/4, d 16db+4(i%4), and receives
+      // V[base+e][16db+i] for e = 0..3.
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int cidx = 2 * db + ((i & 3) >> 1);
+        const int boff = 8 * (i & 1);
+        const int r0 = 32 * h + 4 * g + (i >> 2);
+        const int r1 = r0 + 16;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + v_off(r0, cidx) + boff));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + v_off(r1, cidx) + boff));
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[qb], o[db][qb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb], lsum[qb], 0, 0, 0);
+    }
+  };
 
-      // ---- O^T += V^T P^T: o[db][qb] rows = d 16db+4g+r, column = query i ----
-      // The A operand (16 d x 8 keys per lane) comes from two transposing LDS
-      // reads: lane i of a 16-lane group addresses key base+i/4, d 16db+4(i%4),
-      // and receives V[base+e][16db+i] for e = 0..3.
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const int cidx = 2 * db + ((i & 3) >> 1);
-          const int boff = 8 * (i & 1);
-          const int r0 = 32 * s2 + 4 * g + (i >> 2);
-          const int r1 = r0 + 16;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<lds_v4i16*>(Vb + v_off(r0, cidx) + boff));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<lds_v4i16*>(Vb + v_off(r1, cidx) + boff));
-          typedef short v8i16 __attribute__((ext_vector_type(8)));
-          const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[s2][qb],
-                                                                o[db][qb], 0, 0, 0);
-        }
-      }
+  for (int it = 0; it < n_tiles; ++it) {
+    // my direct loads of tile it are done (tile it+1 may still be in flight)
+    if (it + 1 < n_tiles) SWA_WAIT_VMCNT(LOADS_PER_TILE);
+    else SWA_WAIT_VMCNT(0);
+    __syncthreads();   // everyone's loads of tile it landed; everyone is done with tile it-1
+    if (it + 2 < n_tiles) issue_tile(it + 2);   // into the buffer tile it-1 used
+
+    const int buf = it % NBUF;
+    const uint8_t* Kb = smem + (buf * 2) * TILEB;
+    lds_u8* Vb = (lds_u8*)smem + (buf * 2) * TILEB + TILEB;
+    if (has_sink_tile && it == 0) {
+      if ((s0 + q0w + 15 - W) >= 0) tile_body(Kb, Vb, 0, std::integral_constant<int, 2>());
+      continue;
     }
-    // stage the tile after next while this one is being consumed
-    if (it + 1 < n_tiles) {
-      store_tile((it + 1) & 1);
-      if (it + 2 < n_tiles) load_tile(it + 2);
-    }
+    const int u0 = t0 + BN * (kmin + it - sink_off);
+    const bool any = !(u0 > q0w + 15 || u0 + BN - 1 <= q0w - W || s0 + u0 + BN - 1 < 0);
+    const bool full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
+    if (full) tile_body(Kb, Vb, u0, std::integral_constant<int, 0>());
+    else if (any) tile_body(Kb, Vb, u0, std::integral_constant<int, 1>());
   }
 
   // ---- epilogue: O / l, LSE ----
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = xg_sum(l_run[qb]);
+    const float lt = lsum[qb][0];
     const float inv = 1.f / lt;
     if (tq < C) {
       uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + hw + qb) * HD;
