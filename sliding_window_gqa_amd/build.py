@@ -28,6 +28,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# Per-source extra flags.  The prefill kernel keeps its matrix-instruction
+# results (the output accumulators, which the rare softmax rescale multiplies
+# with vector instructions) in VGPRs and lets the operands live in AGPRs.
+EXTRA = {"swa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -39,7 +43,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,25 +10,32 @@
 //
 // Fast kernel (bf16, head_dim 128, GQA group 4), MI355X / gfx950:
 //  * One work-group = 64 query positions x the 4 query heads of one KV head
-//    (256 query rows), 8 waves, 2 per SIMD so that one wave's softmax runs
-//    while the other's matrix instructions do.  Wave w owns positions
-//    t0+16(w&3) .. +15 for 2 of the 4 heads: 32 query rows, about 190 VGPRs.
-//  * Key tiles of 64 keys.  K and V tiles are staged in LDS once per
-//    work-group and used by all 4 heads (the GQA sharing of explainer How It
-//    Works 1), double-buffered so one barrier per tile suffices.  Tiles outside
-//    the band i-W < j <= i of the work-group are never visited, so the work is
-//    O(N*W); a wave skips the matrix work of tiles outside its own band and
-//    masks only the tiles that cut the diagonal or the window edge.
+//    (256 query rows), 4 waves, one per SIMD.  Wave w owns positions
+//    t0+16w .. +15 for all 4 heads (64 query columns), so every K or V
+//    operand read from LDS feeds four matrix instructions (one per head): the
+//    GQA sharing of explainer How It Works 1 applied inside the wave.  The
+//    output accumulators (128 VGPRs) stay in VGPRs; operands live in AGPRs.
+//  * Key tiles of 32 keys in a 3-slot LDS ring, one barrier per tile.  Tiles
+//    outside the band i-W < j <= i of the work-group are never visited, so
+//    the work is O(N*W); only tiles that cut the diagonal or the window edge
+//    are masked.  Tiles move global -> VGPR staging -> LDS one step ahead.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: in the
-//    transposed form every lane owns one query column, so the softmax row
+//    transposed form every lane owns one query column, so the softmax column
 //    statistics stay in one lane plus a 4-lane exchange (permlane swaps), and
 //    the score accumulator is already the B operand of the PV product.
 //  * V stays row-major in LDS; the A operand of the PV product is read with
-//    the transposing LDS load ds_read_b64_tr_b16.  Both tiles use XOR-swizzled
-//    16-byte chunks so the operand reads are free of bank conflicts.
-//  * Online softmax in the log2 domain; the output accumulator is rescaled
-//    only when a running max grows by more than 2^8 (the result is the same:
-//    numerator and denominator carry the same stale max).
+//    the transposing LDS load ds_read_b64_tr_b16.  Padded row pitches keep
+//    the operand reads free of bank conflicts.
+//  * Softmax in the log2 domain with a lazy reference: Q is scaled by
+//    scale*log2(e) before its bf16 rounding, and the QK^T accumulator starts
+//    at minus the column's reference, so the matrix core returns score - ref
+//    and P = exp2 of it: one exponential and half a conversion per score on
+//    the vector ALU.  The reference moves (and O and l are rescaled) only
+//    when a score exceeds it by more than 2^8; numerator and denominator
+//    carry the same reference, so the result is the same.
+//  * One wave per SIMD overlaps its own vector and matrix work: each step
+//    interleaves PV(j-1) with the exponentials of two heads, and QK(j+1)
+//    with those of the other two.
 //  * Work-groups are renumbered so that the 8 XCDs each take a contiguous
 //    range of (sequence, KV head, query tile): the K/V of one KV head then
 //    stays in one XCD's L2.  Query tiles run longest-first.
@@ -47,36 +54,46 @@ namespace swa {
 namespace {
 
 constexpr int BM = 64;       // query positions per work-group
-constexpr int BN = 64;       // keys per tile
+constexpr int BN = 32;       // keys per tile (one pipeline step)
 constexpr int HD = 128;      // head_dim of the fast kernel
-constexpr int ROWB = HD * 2; // bytes of one K or V row
-constexpr int TILEB = BN * ROWB;  // bytes of one K (or V) tile in LDS
+constexpr int NTHR = 256;    // 4 waves, one per SIMD
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
+constexpr int NBUF = 3;      // LDS ring of K/V tiles
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// XOR swizzles of the 16-byte chunks of a 256-byte LDS row, chosen so that the
-// QK^T operand reads (16 lanes: 16 rows, one chunk) and the transposing PV
-// operand reads (4 consecutive rows, 2 chunks per 16 lanes) hit distinct banks.
-__device__ inline int k_off(int r, int c) { return r * ROWB + ((c ^ (r & 15)) << 4); }
-__device__ inline int v_off(int r, int c) { return r * ROWB + ((c ^ (((r & 7) << 1) | ((r >> 3) & 1))) << 4); }
+// LDS row pitches (bytes).  K rows are 272 B apart, so the 16 rows one
+// QK^T operand read touches start in 16 different 16-byte bank groups; V rows
+// are 288 B apart, so the 4 rows x 32 bytes of one transposing PV read (per
+// 16 lanes) fall in 8 different bank groups.
+constexpr int KPITCH = 272;
+constexpr int VPITCH = 288;
+constexpr int KTILEB = BN * KPITCH;
+constexpr int VTILEB = BN * VPITCH;
+constexpr int RINGB = KTILEB + VTILEB;   // one K+V tile in the ring
 
-// max / sum over the 4 lanes l, l^16, l^32, l^48 (one query column)
+// Work-group barrier for the tile ring.  __syncthreads() carries a release
+// fence that makes the compiler wait for every outstanding vector-memory
+// operation (including prefetched tiles) before s_barrier; here only the
+// wave's own LDS operations are awaited, and the asm clobbers keep the
+// compiler from moving LDS accesses across the barrier.
+__device__ inline void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), no vmcnt/expcnt wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// max over the 4 lanes l, l^16, l^32, l^48 (one query column)
 __device__ inline float xg_max(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ inline float xg_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // max of the 4 lanes of a float4 (NaN-propagating IEEE maximum: no
 // canonicalising moves, v_maximum3_f32 on gfx950)
 __device__ inline float vmax4(floatx4 v) {
@@ -99,21 +116,15 @@ struct PrefillArgs {
   float* lse;
 };
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, expcnt 6:4,
-// lgkmcnt 11:8): wait until at most n vector-memory operations of this wave
-// are outstanding.
-#define SWA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
-
-constexpr int NBUF = 3;              // LDS ring of K/V tiles (prefetch distance 2)
-constexpr int LOADS_PER_TILE = 4;    // direct-to-LDS loads per wave per tile (2 K, 2 V)
-
-// One work-group: 64 query positions x 4 query heads of one KV head, 8 waves.
-// Wave w owns positions t0 + 16*(w&3) .. +15 and query heads hw, hw+1 with
-// hw = 4*kvh + 2*(w>>2); lane (i, g) owns query column i of both 16-row
-// query blocks.  K/V tiles of 64 keys go global -> LDS directly
-// (global_load_lds_dwordx4, 1 KB per wave instruction) into a 3-deep ring.
-__global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * 2 * TILEB];
+// One work-group: 64 query positions x the 4 query heads of one KV head,
+// 4 waves, one per SIMD.  Wave w owns positions t0 + 16w .. +15 for all four
+// heads (64 query columns); lane (i, g) owns query column i of each head.
+// Every K/V operand read from LDS feeds four matrix instructions (one per
+// head), and the wave overlaps its own softmax arithmetic with its matrix
+// instructions.
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+prefill_bf16_d128_g4_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
   __shared__ double rope_freq[kMaxPairs];
 
   const Shape& sh = a.sh;
@@ -134,278 +145,348 @@ __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a
   const int s0 = a.start[b];
   const int C = a.C;
   const int t0 = qt * BM;
-  const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
+  const int q0w = t0 + 16 * w;            // first query of this wave (chunk-relative)
   const int tq = q0w + i;                 // this lane's query
-  const int hw = kvh * 4 + 2 * (w >> 2);  // first query head of this wave
+  const int I = s0 + tq;                  // its absolute position
+  const int h0 = kvh * 4;                 // first query head of the group
   const int W = sh.W;
   const int S = sh.S;
   const int nsink = sh.n_sink;
 
-  // ---- tile list: [sink tile] + band tiles k = kmin..0 (u0 = t0 + 64k) ----
+  // ---- tile list: [sink tiles] + band tiles k = kmin..1 (u0 = t0 + 32k) ----
+  // Band tiles cover chunk-relative key positions t0 - W + 1 .. t0 + 63;
+  // sink tiles cover absolute positions 0 .. n_sink-1 for queries whose
+  // window no longer contains them.
   const int tq_last = min(t0 + BM, C) - 1;
-  const bool has_sink_tile = nsink > 0 && (s0 + tq_last - W) >= 0;
+  const int n_stile = (nsink > 0 && (s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
   const int k_lo = -((W - 1 + BN - 1) / BN);
   const int k_clip = -((s0 + t0 + BN - 1) / BN);
   const int kmin = max(k_lo, k_clip);
-  const int n_tiles = (1 - kmin) + (has_sink_tile ? 1 : 0);
-  const int sink_off = has_sink_tile ? 1 : 0;
+  const int n_tiles = n_stile + (2 - kmin);
+  auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
 
-  // ---- direct-to-LDS tile loads ----
-  // Wave w fills rows 8w .. 8w+7 of the K and of the V tile, 4 rows per
-  // instruction; lane l lands at row 8w+4j+l/16, stored chunk l%16, and so
-  // fetches the global chunk that the row's XOR swizzle puts there.
+  // ---- tile loads: global -> staging VGPRs -> padded LDS ----
+  // Thread (lr = tid/16, lc = tid%16) moves 16-byte chunk lc of rows lr and
+  // lr+16 of the K and of the V tile.  A tile's loads are issued one pipeline
+  // step before it is stored.
   const long long rowstride_c = (long long)sh.Hkv * HD;                // elements between tokens
   const uint16_t* kchunk = a.kr + ((long long)b * C * sh.Hkv + kvh) * HD;
   const uint16_t* vchunk = a.v + ((long long)b * C * sh.Hkv + kvh) * HD;
   const uint16_t* kcache = a.kc ? a.kc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
   const uint16_t* vcache = a.vc ? a.vc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
-  // lane-constant byte offsets of this lane's two rows (8w+4j+lane/16) in a
-  // run of consecutive source rows, including the chunk swizzle
-  const int rowstride_b = sh.Hkv * ROWB;
-  int voff_k[2], voff_v[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 8 * w + 4 * j + (lane >> 4);
-    const int pos = lane & 15;
-    voff_k[j] = row * rowstride_b + 16 * (pos ^ (row & 15));
-    voff_v[j] = row * rowstride_b + 16 * (pos ^ (((row & 7) << 1) | ((row >> 3) & 1)));
-  }
-  auto issue_tile = [&](int it) {
-    const int buf = it % NBUF;
-    const bool is_sink = has_sink_tile && it == 0;
-    const int u0 = is_sink ? 0 : t0 + BN * (kmin + it - sink_off);
-    // fast path: the 64 rows are 64 consecutive rows of one tensor
-    const uint16_t* kbase = nullptr;
-    const uint16_t* vbase = nullptr;
-    if (!is_sink) {
-      if (u0 >= 0) {
-        if (u0 + BN <= C) {
-          kbase = kchunk + (long long)u0 * rowstride_c;
-          vbase = vchunk + (long long)u0 * rowstride_c;
-        }
-      } else {
-        const int P0 = s0 + u0;
-        if (P0 >= nsink) {
-          const int slot0 = nsink + (P0 - nsink) % W;
-          if (slot0 + BN <= S) {
-            kbase = kcache + (long long)slot0 * rowstride_c;
-            vbase = vcache + (long long)slot0 * rowstride_c;
-          }
-        }
-      }
+  const int lr = tid >> 4, lc = tid & 15;
+  const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;
+  const unsigned voff0 = (unsigned)lr * rowbytes + 16u * lc;
+  const unsigned voff1 = voff0 + 16u * rowbytes;
+  u32x4 stage[4];   // K row lr, K row lr+16, V row lr, V row lr+16
+  // The loader captures by value and selects pointer values only: with
+  // captures by reference, or a struct returned from several places, the
+  // compiler selects between addresses of the pointer variables and keeps
+  // them in scratch memory.
+  auto load_tile = [=](int t, u32x4 (&st)[4]) __attribute__((always_inline)) {
+    const bool is_sink = t < n_stile;
+    const int u0 = is_sink ? 0 : band_u0(t);
+    const bool in_chunk = u0 >= 0;
+    const int P0 = s0 + u0;
+    // fast path: the 32 rows are 32 consecutive rows of the chunk or cache
+    // (the slot arithmetic is done for cache tiles only)
+    int slot0 = 0;
+    bool fast = !is_sink && in_chunk && u0 + BN <= C;
+    if (!is_sink && !in_chunk && P0 >= nsink) {
+      slot0 = nsink + (P0 - nsink) % W;
+      fast = slot0 + BN <= S;
     }
+    if (fast) {
+      const long long row0 = in_chunk ? u0 : slot0;
+      const uint8_t* kb8 = reinterpret_cast<const uint8_t*>((in_chunk ? kchunk : kcache) + row0 * rowstride_c);
+      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>((in_chunk ? vchunk : vcache) + row0 * rowstride_c);
+      st[0] = *reinterpret_cast<const u32x4*>(kb8 + voff0);
+      st[1] = *reinterpret_cast<const u32x4*>(kb8 + voff1);
+      st[2] = *reinterpret_cast<const u32x4*>(vb8 + voff0);
+      st[3] = *reinterpret_cast<const u32x4*>(vb8 + voff1);
+    } else {
+      // edge tiles: each row is located on its own, clamped to a row that
+      // exists (rows that are not keys of any query are masked later)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint8_t* kl = smem + (buf * 2) * TILEB + (8 * w + 4 * j) * ROWB;
-      uint8_t* vl = kl + TILEB;
-      const uint8_t* kp;
-      const uint8_t* vp;
-      if (kbase) {
-        kp = reinterpret_cast<const uint8_t*>(kbase) + voff_k[j];
-        vp = reinterpret_cast<const uint8_t*>(vbase) + voff_v[j];
-      } else {
-        // edge tiles: each row located separately, clamped to a row that
-        // exists (rows that are not keys of any query are masked later)
-        const int row = 8 * w + 4 * j + (lane >> 4);
-        const uint16_t* kb;
-        const uint16_t* vb;
-        int roff;
-        if (is_sink) {
-          const int P = min(row, nsink - 1);
-          if (P < s0 && kcache) {
-            kb = kcache; vb = vcache; roff = P;
-          } else {
-            kb = kchunk; vb = vchunk; roff = min(max(P - s0, 0), C - 1);
-          }
-        } else if (u0 >= 0) {
-          kb = kchunk; vb = vchunk; roff = min(u0 + row, C - 1);
-        } else {
-          const int P = max(s0 + u0 + row, 0);
-          kb = kcache; vb = vcache;
-          roff = P < nsink ? P : nsink + (P - nsink) % W;
-        }
-        const long long rb = (long long)(roff - row) * rowstride_c;   // voff already holds row*stride
-        kp = reinterpret_cast<const uint8_t*>(kb + rb) + voff_k[j];
-        vp = reinterpret_cast<const uint8_t*>(vb + rb) + voff_v[j];
+      for (int h = 0; h < 2; ++h) {
+        const int r = lr + 16 * h;
+        // absolute position of the row; rows of band tiles with u0 < 0 are
+        // cache rows, those with u0 >= 0 chunk rows
+        const int P = is_sink ? min(BN * t + r, nsink - 1) : max(P0 + r, 0);
+        const bool from_cache = P < s0 && kcache != nullptr;
+        const int roff = from_cache ? (P < nsink ? P : nsink + (P - nsink) % W)
+                                    : min(max(P - s0, 0), C - 1);
+        const long long eoff = (long long)roff * rowstride_c + 8 * lc;
+        st[h] = *reinterpret_cast<const u32x4*>((from_cache ? kcache : kchunk) + eoff);
+        st[2 + h] = *reinterpret_cast<const u32x4*>((from_cache ? vcache : vchunk) + eoff);
       }
-      __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)kl, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)vl, 16, 0, 0);
     }
   };
-  // kick off the first two tiles before the Q prologue
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  // Byte offset of tile t's ring slot.  The empty asm hides the value's
+  // origin from loop strength reduction, which would otherwise keep one
+  // induction variable per LDS address instead of folding the constant parts
+  // into the instructions' offset fields.
+  auto slot_off = [&](int t) __attribute__((always_inline)) {
+    unsigned off = (unsigned)(t % NBUF) * RINGB;
+    asm volatile("" : "+s"(off));
+    return off;
+  };
+  auto store_tile = [&](int t, const u32x4 (&st)[4]) __attribute__((always_inline)) {
+    uint8_t* Kb = smem + slot_off(t);
+    *reinterpret_cast<u32x4*>(Kb + lr * KPITCH + 16 * lc) = st[0];
+    *reinterpret_cast<u32x4*>(Kb + (lr + 16) * KPITCH + 16 * lc) = st[1];
+    *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * VPITCH + 16 * lc) = st[2];
+    *reinterpret_cast<u32x4*>(Kb + KTILEB + (lr + 16) * VPITCH + 16 * lc) = st[3];
+  };
+  // tiles 0 and 1 into the ring, tile 2 in flight
+  if (n_tiles > 0) {
+    load_tile(0, stage);
+    store_tile(0, stage);
+  }
+  if (n_tiles > 1) {
+    load_tile(1, stage);
+    store_tile(1, stage);
+  }
+  if (n_tiles > 2) load_tile(2, stage);
 
-  // ---- Q prologue: rotated, rounded to bf16, in the B-operand layout ----
+  // ---- Q prologue: rotated, scaled, rounded to bf16, in the B-operand layout ----
+  // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
+  // The softmax scale and log2(e) are applied before the rounding, so that
+  // QK^T yields scores in the log2 domain directly.
+  const float c2 = sh.scale_log2;
   if (tid < kMaxPairs) rope_freq[tid] = a.rt.freq[tid];
   __syncthreads();
-  bf16x8 qf[2][4];
-  {
-    const int I = s0 + tq;
+  bf16x8 qf[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      float cs[4], sn[4];
+  for (int kk = 0; kk < 4; ++kk) {
+    float cs[4], sn[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (sh.rope) {
+        rope_cs(I, rope_freq[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
+      } else {
+        cs[jj] = 1.f;
+        sn[jj] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      u32x4 wv = {0u, 0u, 0u, 0u};
+      if (tq < C)
+        wv = *reinterpret_cast<const u32x4*>(
+            a.q + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD + 8 * (4 * kk + g));
+      u32x4 r;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        if (sh.rope) {
-          rope_cs(I, rope_freq[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
-        } else {
-          cs[jj] = 1.f;
-          sn[jj] = 0.f;
-        }
+        float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
+        rotate(x0, x1, cs[jj], sn[jj]);
+        r[jj] = pack_bf16(x0 * c2, x1 * c2);
       }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        u32x4 wv = {0u, 0u, 0u, 0u};
-        if (tq < C)
-          wv = *reinterpret_cast<const u32x4*>(
-              a.q + (((long long)b * C + tq) * sh.Hq + hw + qb) * HD + 8 * (4 * kk + g));
-        u32x4 r;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
-          rotate(x0, x1, cs[jj], sn[jj]);
-          r[jj] = pack_bf16(x0, x1);
-        }
-        qf[qb][kk] = __builtin_bit_cast(bf16x8, r);
-      }
+      qf[qb][kk] = __builtin_bit_cast(bf16x8, r);
     }
   }
 
-  float m_run[2];
-  floatx4 o[8][2];
+  // ---- softmax state of each query column (one per head qb) ----
+  // ref[qb]: reference of the exponentials, the running max of the scores
+  //          up to the lazy threshold; -inf until the column has seen a key.
+  // The QK^T accumulator starts at -off (off = ref, or 0 while ref = -inf),
+  // so the matrix core returns s = score - off and P = exp2(s).  A tile is
+  // taken as is unless some s exceeds thr (kTau, or -inf while ref = -inf);
+  // then the rare path moves ref to the new max, rescales O and l by
+  // exp2(ref_old - ref_new) and shifts s.
+  float ref[4], thr[4];
+  floatx4 negoff[4];
+  floatx4 o[8][4];
   // row sums of P accumulate on the matrix core: an all-ones A operand makes
   // every row of lsum[qb] the sum over keys of P for this lane's query
-  floatx4 lsum[2];
+  floatx4 lsum[4];
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    m_run[qb] = -INFINITY;
+  for (int qb = 0; qb < 4; ++qb) {
+    ref[qb] = -INFINITY;
+    thr[qb] = -INFINITY;
+    negoff[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
     lsum[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  const float c2 = sh.scale_log2;
-  const int I = s0 + tq;
 
-  // One tile, as two 32-key halves: S^T = K Q^T, mask (MK 1: band edge or
-  // diagonal, 2: sink tile), online softmax, O^T += V^T P^T.
-  auto tile_body = [&](const uint8_t* Kb, lds_u8* Vb, int u0, auto mask_kind) {
-    constexpr int MK = decltype(mask_kind)::value;
+  // ---- operands and stages of one 32-key tile ----
+  bf16x8 kop[2][4];   // K operand of the next QK^T: [kb][kk]
+  bf16x8 vop[8];      // V^T operand of the next PV: [db]
+  // K rows 16kb + i, d = 8(4kk+g) .. +7
+  auto read_k = [&](int t) __attribute__((always_inline)) {
+    const uint8_t* Kb = smem + slot_off(t) + i * KPITCH + 16 * g;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // s[kb][qb]: rows = keys 32h + 16kb + 4g + r, column = query i
-      floatx4 s[2][2];
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kop[kb][kk] = *reinterpret_cast<const bf16x8*>(Kb + 16 * kb * KPITCH + 64 * kk);
+  };
+  // Transposing reads: lane i of a 16-lane group addresses key base+i/4,
+  // d 16db+4(i%4), and receives V[base+e][16db+i] for e = 0..3 (base = 4g,
+  // then 16+4g), which is the A operand of O^T += V^T P^T.
+  auto read_v = [&](int t) __attribute__((always_inline)) {
+    lds_u8* Vb = (lds_u8*)smem + slot_off(t) + KTILEB + (4 * g + (i >> 2)) * VPITCH + 8 * (i & 3);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + 32 * db));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + 16 * VPITCH + 32 * db));
+      const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      vop[db] = __builtin_bit_cast(bf16x8, va);
+    }
+  };
+  // s[kb][qb] = K Q^T - off for heads q0, q0+1: rows = keys 16kb + 4g + r,
+  // column = query i.  Four independent accumulation chains.
+  auto qk_mma = [&](floatx4 (&s)[2][4], int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = q0; qb < q0 + 2; ++qb)
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][0], qf[qb][0], negoff[qb], 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = q0; qb < q0 + 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][kk], qf[qb][kk], s[kb][qb], 0, 0, 0);
+  };
+  // O^T += V^T P^T and l += 1 P^T for head qb
+  auto pv_mma = [&](const bf16x8 (&p)[4], int qb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+    for (int db = 0; db < 8; ++db)
+      o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], p[qb], o[db][qb], 0, 0, 0);
+    lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[qb], lsum[qb], 0, 0, 0);
+  };
+  // mask of tile j for this wave: 0 none, 1 band edge / diagonal, 2 sink tile
+  auto mask_kind = [&](int j) __attribute__((always_inline)) {
+    if (j < n_stile) return 2;
+    const int u0 = band_u0(j);
+    const bool full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
+    return full ? 0 : 1;
+  };
+  auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kb + k_off(32 * h + 16 * kb + i, 4 * kk + g));
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][kk], s[kb][qb], 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        const int kr_ = 16 * kb + 4 * g + r;
+        bool ok;
+        if (mk == 2) {
+          const int P = BN * j + kr_;
+          ok = P < nsink && P <= I - W;
+        } else {
+          const int u = band_u0(j) + kr_;
+          ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
         }
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
       }
-      if constexpr (MK != 0) {
+  };
+  // P = exp2(s) of head qb, rounded to bf16 in the B-operand layout
+  auto sexp = [&](const floatx4 (&s)[2][4], bf16x8 (&p)[4], int qb) __attribute__((always_inline)) {
+    u32x4 pk;
+    pk[0] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][0]), __builtin_amdgcn_exp2f(s[0][qb][1]));
+    pk[1] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][2]), __builtin_amdgcn_exp2f(s[0][qb][3]));
+    pk[2] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][0]), __builtin_amdgcn_exp2f(s[1][qb][1]));
+    pk[3] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][2]), __builtin_amdgcn_exp2f(s[1][qb][3]));
+    p[qb] = __builtin_bit_cast(bf16x8, pk);
+  };
+  // whether some s of head qb in this lane exceeds its column's threshold
+  auto over = [&](const floatx4 (&s)[2][4], int qb) __attribute__((always_inline)) {
+    const float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
+    return mx > thr[qb];
+  };
+  // the rare path: new references, rescaled O and l, shifted s
+  auto rebase = [&](floatx4 (&s)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 4; ++qb) {
+      const float off = -negoff[qb][0];
+      const float cm = xg_max(__builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]))) + off;
+      const float nref = __builtin_elementwise_maximum(ref[qb], cm);
+      if (nref > ref[qb] + kTau || (ref[qb] == -INFINITY && nref > -INFINITY)) {
+        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - nref);
+        lsum[qb] *= alpha;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kr_ = 32 * h + 16 * kb + 4 * g + r;
-            bool ok;
-            if constexpr (MK == 2) {
-              ok = kr_ < nsink && kr_ <= I - W;
-            } else {
-              const int u = u0 + kr_;
-              ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
-            }
-            if (!ok) {
-              s[kb][0][r] = -INFINITY;
-              s[kb][1][r] = -INFINITY;
-            }
-          }
+        for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
+        ref[qb] = nref;
       }
-      bf16x8 pb[2];
+      const float noff = ref[qb] == -INFINITY ? 0.f : ref[qb];
+      const float shift = noff - off;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
-        mx = xg_max(mx) * c2;
-        const bool need = mx > m_run[qb] + kTau;
-        if (__builtin_expect(__any(need), 0)) {
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.f;
-          if (need) m_run[qb] = mx;
-          lsum[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
-        }
-        const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-        float pv[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pv[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -msub));
-        u32x4 pk;
-        pk[0] = pack_bf16(pv[0][0], pv[0][1]);
-        pk[1] = pack_bf16(pv[0][2], pv[0][3]);
-        pk[2] = pack_bf16(pv[1][0], pv[1][1]);
-        pk[3] = pack_bf16(pv[1][2], pv[1][3]);
-        pb[qb] = __builtin_bit_cast(bf16x8, pk);
-      }
-      // A operand of the PV product from two transposing LDS reads: lane i of
-      // a 16-lane group addresses key base+i/4, d 16db+4(i%4), and receives
-      // V[base+e][16db+i] for e = 0..3.
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int cidx = 2 * db + ((i & 3) >> 1);
-        const int boff = 8 * (i & 1);
-        const int r0 = 32 * h + 4 * g + (i >> 2);
-        const int r1 = r0 + 16;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + v_off(r0, cidx) + boff));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + v_off(r1, cidx) + boff));
-        typedef short v8i16 __attribute__((ext_vector_type(8)));
-        const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[qb], o[db][qb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb], lsum[qb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) s[kb][qb] -= shift;
+      negoff[qb] = floatx4{-noff, -noff, -noff, -noff};
+      thr[qb] = ref[qb] == -INFINITY ? -INFINITY : kTau;
     }
   };
 
-  for (int it = 0; it < n_tiles; ++it) {
-    // my direct loads of tile it are done (tile it+1 may still be in flight)
-    if (it + 1 < n_tiles) SWA_WAIT_VMCNT(LOADS_PER_TILE);
-    else SWA_WAIT_VMCNT(0);
-    __syncthreads();   // everyone's loads of tile it landed; everyone is done with tile it-1
-    if (it + 2 < n_tiles) issue_tile(it + 2);   // into the buffer tile it-1 used
-
-    const int buf = it % NBUF;
-    const uint8_t* Kb = smem + (buf * 2) * TILEB;
-    lds_u8* Vb = (lds_u8*)smem + (buf * 2) * TILEB + TILEB;
-    if (has_sink_tile && it == 0) {
-      if ((s0 + q0w + 15 - W) >= 0) tile_body(Kb, Vb, 0, std::integral_constant<int, 2>());
-      continue;
+  // ---- software pipeline over tiles ----
+  // Step j, first half: PV(j-1) head by head on the matrix cores, with the
+  // threshold checks of S(j) and the exponentials of heads 0 and 1 (each
+  // head's P registers are rewritten only after PV(j-1) has consumed them).
+  // Second half: QK(j+1) of heads 0 and 1 with the exponentials of heads 2
+  // and 3, then QK(j+1) of heads 2 and 3.  The rare rescale sits between the
+  // halves.  K(j+1) is read from LDS at the start of the step, V(j) at its
+  // end.  Tile j is read during steps j-1 and j; in step j the slot of tile
+  // j-1 (free since the barrier that ended step j-1) receives tile j+2,
+  // which the barrier ending step j publishes, and the loads of tile j+3 are
+  // issued.  The last step also multiplies a stale ring slot into S (and
+  // stores stale staging registers into a free slot); those values are never
+  // used.
+  floatx4 s[2][4];
+  bf16x8 p[4];
+  auto step = [&](int j, bool first) __attribute__((always_inline)) {
+    const int mk = mask_kind(j);
+    if (mk) apply_mask(j, mk, s);
+    read_k(j + 1);
+    bool rare = false;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      if (!first) pv_mma(p, qb);
+      rare |= over(s, qb);
+      if (qb < 2) {
+        sexp(s, p, qb);
+        // keep these exponentials between the matrix instructions: the
+        // compiler would otherwise move them past the rare-path branch
+        asm volatile("" : "+v"(p[qb]));
+      }
     }
-    const int u0 = t0 + BN * (kmin + it - sink_off);
-    const bool any = !(u0 > q0w + 15 || u0 + BN - 1 <= q0w - W || s0 + u0 + BN - 1 < 0);
-    const bool full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
-    if (full) tile_body(Kb, Vb, u0, std::integral_constant<int, 0>());
-    else if (any) tile_body(Kb, Vb, u0, std::integral_constant<int, 1>());
+    if (__builtin_expect(__any(rare), 0)) {
+      rebase(s);
+      sexp(s, p, 0);
+      sexp(s, p, 1);
+    }
+    qk_mma(s, 0);
+    sexp(s, p, 2);
+    sexp(s, p, 3);
+    // the accumulator seeds of QK(j+1) of heads 2 and 3 pass through the
+    // same empty asm as their P, so these exponentials stay ahead of it
+    asm volatile("" : "+v"(p[2]), "+v"(p[3]), "+v"(negoff[2]), "+v"(negoff[3]));
+    qk_mma(s, 2);
+    read_v(j);
+    store_tile(j + 2, stage);
+    if (j + 3 < n_tiles) load_tile(j + 3, stage);
+    ring_barrier();
+  };
+  __syncthreads();
+  if (n_tiles > 0) {
+    read_k(0);
+    qk_mma(s, 0);
+    qk_mma(s, 2);
+    step(0, true);
+    for (int j = 1; j < n_tiles; ++j) step(j, false);
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) pv_mma(p, qb);
   }
 
   // ---- epilogue: O / l, LSE ----
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < 4; ++qb) {
     const float lt = lsum[qb][0];
     const float inv = 1.f / lt;
     if (tq < C) {
-      uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + hw + qb) * HD;
+      uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         u32x2 val = {pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv),
@@ -413,7 +494,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_d128_g4_kernel(PrefillArgs a
         *reinterpret_cast<u32x2*>(dst + 16 * db + 4 * g) = val;
       }
       if (a.lse && g == 0)
-        a.lse[((long long)b * sh.Hq + hw + qb) * C + tq] = (m_run[qb] + log2f(lt)) * 0.69314718055994531f;
+        a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lt)) * 0.69314718055994531f;
     }
   }
 }
@@ -522,7 +603,7 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   const long long nwg = (long long)a.n_qtiles * sh.Hkv * sh.B;
-  prefill_bf16_d128_g4_kernel<<<dim3((unsigned)nwg), dim3(512), 0, st>>>(a);
+  prefill_bf16_d128_g4_kernel<<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   return hipGetLastError();
 }
 
