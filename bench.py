@@ -17,9 +17,11 @@ Only one GPU is used; --gpus above 1 is refused.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -30,6 +32,26 @@ if ROOT not in sys.path:
 METRIC = "SWA prefill TFLOP/s + decode HBM GB/s, W=4096 GQA 32/8 hd128 bf16"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak (published)
+
+
+def profiled_traffic(name, sources):
+    """HBM bytes per launch from the committed rocprofv3 summary profiles/<name>.txt
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a plain
+    256 MiB copy), or None when the summary is missing or was taken on other
+    kernel sources than the ones built now."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", name + ".txt")).read()
+    except OSError:
+        return None
+    h = re.search(r"source_sha256_16: (\w+)", text)
+    t = re.search(r"traffic_bytes: (\d+)", text)
+    if not h or not t:
+        return None
+    sha = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "sliding_window_gqa_amd", "csrc", f), "rb") as fh:
+            sha.update(fh.read())
+    return int(t.group(1)) if sha.hexdigest()[:16] == h.group(1) else None
 
 
 def band_pairs(N, W, start=0, n_sink=0):
@@ -146,7 +168,10 @@ def main():
                        "algorithmic_flops_per_step": flops2, "key_pairs": pairs2},
             "roofline": {"bound": "mfma", "kernel": "prefill_bf16_d128_g4_kernel",
                          "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                         "traffic": profiled_traffic("prefill_bf16_d128_g4_kernel.prefill_n8192_w4096",
+                                                     ["swa_prefill.hip", "swa_device.hpp"]),
+                         "algorithmic_bytes": N * Hq * D * 2 * 2 + 2 * N * Hkv * D * 2 + Hq * N * 4,
                          "avg_kernel_ms": round(attn_ms, 4),
                          "timing": "HIP events around each attention launch in the timed region"},
             "wall_s_timed_region": round(wall, 4),
@@ -207,7 +232,10 @@ def main():
             "algorithmic_bytes_per_step": round((dec_bytes + write_bytes) / T),
             "roofline": {"bound": "hbm", "kernel": "decode_bf16_d128_g4_kernel + decode_combine_kernel",
                          "achieved": round(dec_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(dec_achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                         "frac": round(dec_achieved / PEAK_HBM_GBPS, 4),
+                         "traffic": profiled_traffic("decode_bf16_d128_g4_kernel.decode_b64_w4096",
+                                                     ["swa_decode.hip", "swa_device.hpp"]),
+                         "algorithmic_bytes": round(dec_bytes / T),
                          "avg_call_ms": round(dec_ms / T, 4),
                          "bytes": "valid K/V slots read once + Q + O"},
         }
