@@ -154,10 +154,12 @@ int swa_decode(const swa_params* params, const void* q, const void* k_cache, con
   const bool f32 = params->dtype == SWA_F32;
   float* part = static_cast<float*>(workspace);
   hipError_t e;
-  if (fast_path(params))
-    e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, stream);
-  else
+  if (fast_path(params)) {
+    e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, out, lse, stream);
+    if (n == 1) return launched(e);   // the kernel wrote out and lse
+  } else {
     e = swa::launch_decode_generic(sh, rt, f32, q, k_cache, v_cache, pos, part, n, stream);
+  }
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
   return launched(swa::launch_decode_combine(sh, f32, part, n, out, lse, stream));
 }

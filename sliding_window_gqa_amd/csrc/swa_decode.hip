@@ -55,11 +55,14 @@ struct DecodeArgs {
   float* part;
   int n_splits;
   int split_len;
+  uint16_t* out;   // written directly (normalised) when n_splits == 1
+  float* lse;
 };
 
-__global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
   __shared__ float sm_m[4][4], sm_l[4][4];
   __shared__ float sm_o[4][4][HD];
+  __shared__ double rope_freq[kMaxPairs];
 
   const Shape& sh = a.sh;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -74,55 +77,64 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
   const int vend = min(min(S, sp0 + a.split_len), n_live);
   const int h0 = kvh * 4;
 
-  // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
-  bf16x8 qf[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    u32x4 wv = {0u, 0u, 0u, 0u};
-    if (i < 4) wv = *reinterpret_cast<const u32x4*>(a.q + ((long long)b * sh.Hq + h0 + i) * HD + 8 * (4 * kk + g));
-    u32x4 r;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
-      if (sh.rope) {
-        float cs, sn;
-        rope_cs(p, a.rt.freq[4 * (4 * kk + g) + jj], cs, sn);
-        rotate(x0, x1, cs, sn);
-      }
-      r[jj] = pack_bf16(x0, x1);
-    }
-    qf[kk] = __builtin_bit_cast(bf16x8, r);
-  }
-
   const long long row_stride = (long long)sh.Hkv * HD;       // elements between slots
   const uint16_t* kbase = a.kc + ((long long)b * S * sh.Hkv + kvh) * HD;
   const uint16_t* vbase = a.vc + ((long long)b * S * sh.Hkv + kvh) * HD;
   const float c2 = sh.scale_log2;
+
+  // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
+  // The RoPE frequencies are staged in LDS (one coalesced read instead of a
+  // dependent kernel-argument load per element).
+  if (tid < kMaxPairs) rope_freq[tid] = a.rt.freq[tid];
+  __syncthreads();
+  bf16x8 qf[4];
+  auto load_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 wv = {0u, 0u, 0u, 0u};
+      if (i < 4) wv = *reinterpret_cast<const u32x4*>(a.q + ((long long)b * sh.Hq + h0 + i) * HD + 8 * (4 * kk + g));
+      u32x4 r;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
+        if (sh.rope) {
+          float cs, sn;
+          rope_cs(p, rope_freq[4 * (4 * kk + g) + jj], cs, sn);
+          rotate(x0, x1, cs, sn);
+        }
+        r[jj] = pack_bf16(x0, x1);
+      }
+      qf[kk] = __builtin_bit_cast(bf16x8, r);
+    }
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   floatx4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = sp0 + kChunk * w; c0 < vend; c0 += 4 * kChunk) {
-    // K: A operand rows = slots c0+16kb+i, d = 8*(4kk+g) .. +7
-    u32x4 kr[2][4];
+  // K: A operand rows = slots c0+16kb+i, d = 8*(4kk+g) .. +7
+  // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
+  // Slots at or past vend are read as slot vend-1 (a live slot, so the data
+  // are finite) and masked out of the softmax; every load is unconditional,
+  // from a uniform base plus a 32-bit byte offset.
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kbase);
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vbase);
+  const unsigned rowb = (unsigned)row_stride * 2u;
+  auto load_chunk = [&](int c0, u32x4 (&kr)[2][4], u32x4 (&vr)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int slot = c0 + 16 * kb + i;
+      const unsigned off = (unsigned)min(c0 + 16 * kb + i, vend - 1) * rowb + 16u * g;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kr[kb][kk] = slot < vend ? *reinterpret_cast<const u32x4*>(kbase + slot * row_stride + 8 * (4 * kk + g))
-                                 : u32x4{0u, 0u, 0u, 0u};
+      for (int kk = 0; kk < 4; ++kk) kr[kb][kk] = *reinterpret_cast<const u32x4*>(kb8 + off + 64u * kk);
     }
-    // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
-    u32x4 vr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int slot = c0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-      vr[e] = slot < vend ? *reinterpret_cast<const u32x4*>(vbase + slot * row_stride + 8 * i)
-                          : u32x4{0u, 0u, 0u, 0u};
+      const int slot = min(c0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)), vend - 1);
+      vr[e] = *reinterpret_cast<const u32x4*>(vb8 + (unsigned)slot * rowb + 16u * i);
     }
+  };
+  auto do_chunk = [&](int c0, const u32x4 (&kr)[2][4], const u32x4 (&vr)[8]) __attribute__((always_inline)) {
     floatx4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -180,6 +192,31 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
       }
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[db], 0, 0, 0);
     }
+  };
+  // Each wave takes chunks c0, c0 + 4*kChunk, ... of the range; the loads of
+  // the next chunk are in flight while the current one is computed (two
+  // register buffers, alternating).  The prefetch is unconditional (past the
+  // range it reads slot vend-1 again), so the compiler's count of outstanding
+  // loads stays exact and it waits for the current chunk only.
+  {
+    const int cstep = 4 * kChunk;
+    u32x4 krA[2][4], vrA[8], krB[2][4], vrB[8];
+    int c0 = sp0 + kChunk * w;
+    // the first chunk's loads go out before the query is prepared
+    if (c0 < vend) load_chunk(c0, krA, vrA);
+    load_q();
+    if (c0 < vend) {
+      while (true) {
+        load_chunk(c0 + cstep, krB, vrB);
+        do_chunk(c0, krA, vrA);
+        c0 += cstep;
+        if (c0 >= vend) break;
+        load_chunk(c0 + cstep, krA, vrA);
+        do_chunk(c0, krB, vrB);
+        c0 += cstep;
+        if (c0 >= vend) break;
+      }
+    }
   }
 
   // ---- merge the 4 waves through LDS ----
@@ -209,11 +246,18 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
       Lsum += sm_l[ww][hh] * f;
       O += sm_o[ww][hh][d] * f;
     }
-    float* dst = a.part + (((long long)b * sh.Hq + h0 + hh) * a.n_splits + split) * (HD + 2);
-    dst[d] = O;
-    if (d == 0) {
-      dst[HD] = M;
-      dst[HD + 1] = Lsum;
+    if (a.n_splits == 1) {
+      // one range covers the sequence: this is the final result
+      const long long off = ((long long)b * sh.Hq + h0 + hh) * HD + d;
+      a.out[off] = to_bf16_bits(O / Lsum);
+      if (a.lse && d == 0) a.lse[(long long)b * sh.Hq + h0 + hh] = (M + log2f(Lsum)) * 0.69314718055994531f;
+    } else {
+      float* dst = a.part + (((long long)b * sh.Hq + h0 + hh) * a.n_splits + split) * (HD + 2);
+      dst[d] = O;
+      if (d == 0) {
+        dst[HD] = M;
+        dst[HD + 1] = Lsum;
+      }
     }
   }
 }
@@ -331,11 +375,13 @@ __global__ void decode_combine_kernel(Shape sh, const float* part, int n_splits,
 
 }  // namespace
 
-// Splits: enough work-groups to cover the 256 CUs several times over, each
-// range a multiple of the 128 slots one work-group step covers.
+// Splits: about one round of work-groups (two per CU on 256 CUs; longer
+// ranges per work-group beat more, shorter ones: the per-work-group prologue,
+// merge and the combine pass cost more than the load imbalance), each range a
+// multiple of the 128 slots one work-group step covers.
 int decode_splits(const Shape& sh) {
   const int units = sh.B * sh.Hkv;
-  int n = (2048 + units - 1) / units;
+  int n = (512 + units - 1) / units;
   const int max_n = (sh.S + 4 * kChunk - 1) / (4 * kChunk);
   if (n > max_n) n = max_n;
   if (n < 1) n = 1;
@@ -350,7 +396,8 @@ static int split_len_of(const Shape& sh, int n_splits) {
 
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
-                                      float* partial, int n_splits, hipStream_t st) {
+                                      float* partial, int n_splits, void* out, float* lse,
+                                      hipStream_t st) {
   DecodeArgs a;
   a.sh = sh;
   a.rt = rt;
@@ -361,6 +408,8 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
   a.part = partial;
   a.n_splits = n_splits;
   a.split_len = split_len_of(sh, n_splits);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
   decode_bf16_d128_g4_kernel<<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }

@@ -117,7 +117,7 @@ def test_workspace_sizes():
         assert nbytes % per_split == 0
         n_splits = nbytes // per_split
         assert 1 <= n_splits <= -(-(W + S) // 128)
-        assert B * 8 * n_splits >= min(2048, B * 8 * -(-(W + S) // 128))
+        assert B * 8 * n_splits >= min(512, B * 8 * -(-(W + S) // 128))
 
 
 def test_status_strings():
