@@ -52,7 +52,11 @@ RopeTab rope_table(const swa_params* p) {
 }
 
 bool fast_path(const swa_params* p) {
-  return p->dtype == SWA_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads;
+  // the fast kernels address one sequence's cache with 32-bit byte offsets
+  const long long seq_cache_bytes =
+      (long long)(p->n_sink + p->window) * p->n_kv_heads * p->head_dim * 2;
+  return p->dtype == SWA_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads &&
+         seq_cache_bytes < (1LL << 31);
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }

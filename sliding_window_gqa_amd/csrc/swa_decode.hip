@@ -45,6 +45,14 @@ __device__ inline float xg_sum(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// p, as a value the compiler knows to be the same in every lane
+__device__ inline void* uniform_ptr(const void* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+}
+
 struct DecodeArgs {
   Shape sh;
   RopeTab rt;
@@ -69,7 +77,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, i = lane & 15, g = lane >> 4;
-  const int p = a.pos[b];
+  const int p = __builtin_amdgcn_readfirstlane(a.pos[b]);   // uniform: one sequence per work-group
   const int S = sh.S;
   // slots [0, min(S, p+1)) hold live positions; the others are never read
   const int n_live = min(S, p + 1);
@@ -115,24 +123,33 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
 
   // K: A operand rows = slots c0+16kb+i, d = 8*(4kk+g) .. +7
   // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
-  // Slots at or past vend are read as slot vend-1 (a live slot, so the data
-  // are finite) and masked out of the softmax; every load is unconditional,
-  // from a uniform base plus a 32-bit byte offset.
-  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kbase);
-  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vbase);
+  // Buffer loads: the descriptors cover exactly this head's rows of the live
+  // slots [0, vend), so rows past vend read as zeros (and are masked out of
+  // the softmax) with no per-lane branch or clamp; every address is a 32-bit
+  // lane offset plus the chunk's row offset.
   const unsigned rowb = (unsigned)row_stride * 2u;
+  // (the descriptor inputs are made explicitly wave-uniform; otherwise the
+  // compiler keeps the descriptors in VGPRs and loops over lanes per load)
+  const int nrec = __builtin_amdgcn_readfirstlane((vend - 1) * (int)rowb + HD * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbase), (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbase), (short)0, nrec, 0x00020000);
+  unsigned koff[2], voff[8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) koff[kb] = (unsigned)(16 * kb + i) * rowb + 16u * g;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) voff[e] = (unsigned)(e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) * rowb + 16u * i;
+  // Each K/V byte is read once per call: the loads are non-temporal (nt).
+  constexpr int kNT = 2;
   auto load_chunk = [&](int c0, u32x4 (&kr)[2][4], u32x4 (&vr)[8]) __attribute__((always_inline)) {
+    const unsigned cb = (unsigned)c0 * rowb;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const unsigned off = (unsigned)min(c0 + 16 * kb + i, vend - 1) * rowb + 16u * g;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kr[kb][kk] = *reinterpret_cast<const u32x4*>(kb8 + off + 64u * kk);
-    }
+      for (int kk = 0; kk < 4; ++kk)
+        kr[kb][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(cb + koff[kb] + 64u * kk), 0, kNT));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int slot = min(c0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)), vend - 1);
-      vr[e] = *reinterpret_cast<const u32x4*>(vb8 + (unsigned)slot * rowb + 16u * i);
-    }
+    for (int e = 0; e < 8; ++e)
+      vr[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(cb + voff[e]), 0, kNT));
   };
   auto do_chunk = [&](int c0, const u32x4 (&kr)[2][4], const u32x4 (&vr)[8]) __attribute__((always_inline)) {
     floatx4 s[2];
@@ -158,7 +175,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = xg_max(mx) * c2;
     const bool need = mx > m_run + kTau;
-    const float alpha = need ? exp2f(m_run - mx) : 1.f;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
     if (need) m_run = mx;
     if (__any(need)) {
       l_run *= alpha;
@@ -171,7 +188,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[kb][r] = exp2f(fmaf(s[kb][r], c2, -msub));
+        pv[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -msub));
         l_run += pv[kb][r];
       }
     u32x4 pk;
@@ -187,8 +204,8 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
       u32x4 va;
 #pragma unroll
       for (int m2 = 0; m2 < 4; ++m2) {
-        const uint32_t x0 = vr[2 * m2][wd], x1 = vr[2 * m2 + 1][wd];
-        va[m2] = (db & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+        // low halves (even db) or high halves (odd db) of two packed pairs
+        va[m2] = __builtin_amdgcn_perm(vr[2 * m2 + 1][wd], vr[2 * m2][wd], (db & 1) ? 0x07060302u : 0x05040100u);
       }
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[db], 0, 0, 0);
     }
