@@ -10,11 +10,12 @@
 //
 // Fast kernel (bf16, head_dim 128, GQA group 4), MI355X / gfx950:
 //  * One work-group = 64 query positions x the 4 query heads of one KV head
-//    (256 query rows), 4 waves, one per SIMD.  Wave w owns positions
-//    t0+16w .. +15 for all 4 heads (64 query columns), so every K or V
-//    operand read from LDS feeds four matrix instructions (one per head): the
-//    GQA sharing of explainer How It Works 1 applied inside the wave.  The
-//    output accumulators (128 VGPRs) stay in VGPRs; operands live in AGPRs.
+//    (256 query rows), 8 waves, two per SIMD.  Wave w owns positions
+//    t0+16(w&3) .. +15 for 2 of the 4 heads (32 query columns), so every K or
+//    V operand read from LDS feeds two matrix instructions (one per head):
+//    the GQA sharing of explainer How It Works 1 applied inside the wave.
+//    The two waves of a SIMD hide each other's barrier, LDS and exponential
+//    latencies.
 //  * Key tiles of 32 keys in a 3-slot LDS ring, one barrier per tile.  Tiles
 //    outside the band i-W < j <= i of the work-group are never visited, so
 //    the work is O(N*W); only tiles that cut the diagonal or the window edge
@@ -33,9 +34,8 @@
 //    the vector ALU.  The reference moves (and O and l are rescaled) only
 //    when a score exceeds it by more than 2^8; numerator and denominator
 //    carry the same reference, so the result is the same.
-//  * One wave per SIMD overlaps its own vector and matrix work: each step
-//    interleaves PV(j-1) with the exponentials of two heads, and QK(j+1)
-//    with those of the other two.
+//  * Each step interleaves PV(j-1) with the exponentials of one head, and
+//    QK(j+1) with those of the other.
 //  * Work-groups are renumbered so that the 8 XCDs each take a contiguous
 //    range of (sequence, KV head, query tile): the K/V of one KV head then
 //    stays in one XCD's L2.  Query tiles run longest-first.
@@ -56,7 +56,8 @@ namespace {
 constexpr int BM = 64;       // query positions per work-group
 constexpr int BN = 32;       // keys per tile (one pipeline step)
 constexpr int HD = 128;      // head_dim of the fast kernel
-constexpr int NTHR = 256;    // 4 waves, one per SIMD
+constexpr int NTHR = 512;    // 8 waves, two per SIMD
+constexpr int QB = 2;        // query heads per wave
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
 constexpr int NBUF = 3;      // LDS ring of K/V tiles
 
@@ -117,12 +118,11 @@ struct PrefillArgs {
 };
 
 // One work-group: 64 query positions x the 4 query heads of one KV head,
-// 4 waves, one per SIMD.  Wave w owns positions t0 + 16w .. +15 for all four
-// heads (64 query columns); lane (i, g) owns query column i of each head.
-// Every K/V operand read from LDS feeds four matrix instructions (one per
-// head), and the wave overlaps its own softmax arithmetic with its matrix
-// instructions.
-__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// 8 waves, two per SIMD.  Wave w owns positions t0 + 16(w&3) .. +15 for heads
+// h0, h0+1 (h0 = 4 kvh + 2(w>>2)); lane (i, g) owns query column i of each
+// of its heads.  Every K/V operand read from LDS feeds two matrix
+// instructions (one per head).
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
   __shared__ double rope_freq[kMaxPairs];
@@ -145,10 +145,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   const int s0 = a.start[b];
   const int C = a.C;
   const int t0 = qt * BM;
-  const int q0w = t0 + 16 * w;            // first query of this wave (chunk-relative)
+  const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
   const int tq = q0w + i;                 // this lane's query
   const int I = s0 + tq;                  // its absolute position
-  const int h0 = kvh * 4;                 // first query head of the group
+  const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
   const int W = sh.W;
   const int S = sh.S;
   const int nsink = sh.n_sink;
@@ -166,9 +166,9 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
 
   // ---- tile loads: global -> staging VGPRs -> padded LDS ----
-  // Thread (lr = tid/16, lc = tid%16) moves 16-byte chunk lc of rows lr and
-  // lr+16 of the K and of the V tile.  A tile's loads are issued one pipeline
-  // step before it is stored.
+  // Thread (lr = tid/16, lc = tid%16) moves 16-byte chunk lc of row lr of
+  // the K and of the V tile.  A tile's loads are issued one pipeline step
+  // before it is stored.
   const long long rowstride_c = (long long)sh.Hkv * HD;                // elements between tokens
   const uint16_t* kchunk = a.kr + ((long long)b * C * sh.Hkv + kvh) * HD;
   const uint16_t* vchunk = a.v + ((long long)b * C * sh.Hkv + kvh) * HD;
@@ -177,13 +177,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   const int lr = tid >> 4, lc = tid & 15;
   const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;
   const unsigned voff0 = (unsigned)lr * rowbytes + 16u * lc;
-  const unsigned voff1 = voff0 + 16u * rowbytes;
-  u32x4 stage[4];   // K row lr, K row lr+16, V row lr, V row lr+16
+  u32x4 stage[2];   // K row lr, V row lr
   // The loader captures by value and selects pointer values only: with
   // captures by reference, or a struct returned from several places, the
   // compiler selects between addresses of the pointer variables and keeps
   // them in scratch memory.
-  auto load_tile = [=](int t, u32x4 (&st)[4]) __attribute__((always_inline)) {
+  auto load_tile = [=](int t, u32x4 (&st)[2]) __attribute__((always_inline)) {
     const bool is_sink = t < n_stile;
     const int u0 = is_sink ? 0 : band_u0(t);
     const bool in_chunk = u0 >= 0;
@@ -201,15 +200,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       const uint8_t* kb8 = reinterpret_cast<const uint8_t*>((in_chunk ? kchunk : kcache) + row0 * rowstride_c);
       const uint8_t* vb8 = reinterpret_cast<const uint8_t*>((in_chunk ? vchunk : vcache) + row0 * rowstride_c);
       st[0] = *reinterpret_cast<const u32x4*>(kb8 + voff0);
-      st[1] = *reinterpret_cast<const u32x4*>(kb8 + voff1);
-      st[2] = *reinterpret_cast<const u32x4*>(vb8 + voff0);
-      st[3] = *reinterpret_cast<const u32x4*>(vb8 + voff1);
+      st[1] = *reinterpret_cast<const u32x4*>(vb8 + voff0);
     } else {
       // edge tiles: each row is located on its own, clamped to a row that
       // exists (rows that are not keys of any query are masked later)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = lr + 16 * h;
+      {
+        const int r = lr;
         // absolute position of the row; rows of band tiles with u0 < 0 are
         // cache rows, those with u0 >= 0 chunk rows
         const int P = is_sink ? min(BN * t + r, nsink - 1) : max(P0 + r, 0);
@@ -217,8 +213,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         const int roff = from_cache ? (P < nsink ? P : nsink + (P - nsink) % W)
                                     : min(max(P - s0, 0), C - 1);
         const long long eoff = (long long)roff * rowstride_c + 8 * lc;
-        st[h] = *reinterpret_cast<const u32x4*>((from_cache ? kcache : kchunk) + eoff);
-        st[2 + h] = *reinterpret_cast<const u32x4*>((from_cache ? vcache : vchunk) + eoff);
+        st[0] = *reinterpret_cast<const u32x4*>((from_cache ? kcache : kchunk) + eoff);
+        st[1] = *reinterpret_cast<const u32x4*>((from_cache ? vcache : vchunk) + eoff);
       }
     }
   };
@@ -231,12 +227,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     asm volatile("" : "+s"(off));
     return off;
   };
-  auto store_tile = [&](int t, const u32x4 (&st)[4]) __attribute__((always_inline)) {
+  auto store_tile = [&](int t, const u32x4 (&st)[2]) __attribute__((always_inline)) {
     uint8_t* Kb = smem + slot_off(t);
     *reinterpret_cast<u32x4*>(Kb + lr * KPITCH + 16 * lc) = st[0];
-    *reinterpret_cast<u32x4*>(Kb + (lr + 16) * KPITCH + 16 * lc) = st[1];
-    *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * VPITCH + 16 * lc) = st[2];
-    *reinterpret_cast<u32x4*>(Kb + KTILEB + (lr + 16) * VPITCH + 16 * lc) = st[3];
+    *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * VPITCH + 16 * lc) = st[1];
   };
   // tiles 0 and 1 into the ring, tile 2 in flight
   if (n_tiles > 0) {
@@ -256,7 +250,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   const float c2 = sh.scale_log2;
   if (tid < kMaxPairs) rope_freq[tid] = a.rt.freq[tid];
   __syncthreads();
-  bf16x8 qf[4][4];
+  bf16x8 qf[QB][4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     float cs[4], sn[4];
@@ -270,7 +264,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       }
     }
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       u32x4 wv = {0u, 0u, 0u, 0u};
       if (tq < C)
         wv = *reinterpret_cast<const u32x4*>(
@@ -294,15 +288,15 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // taken as is unless some s exceeds thr (kTau, or -inf while ref = -inf);
   // then the rare path moves ref to the new max, rescales O and l by
   // exp2(ref_old - ref_new) and shifts s.
-  float ref[4], thr[4];
-  floatx4 negoff[4];
-  floatx4 o[8][4];
+  float ref[QB], thr[QB];
+  floatx4 negoff[QB];
+  floatx4 o[8][QB];
   // row sums of P accumulate on the matrix core: an all-ones A operand makes
   // every row of lsum[qb] the sum over keys of P for this lane's query
-  floatx4 lsum[4];
+  floatx4 lsum[QB];
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     ref[qb] = -INFINITY;
     thr[qb] = -INFINITY;
     negoff[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -338,22 +332,22 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   };
   // s[kb][qb] = K Q^T - off for heads q0, q0+1: rows = keys 16kb + 4g + r,
   // column = query i.  Four independent accumulation chains.
-  auto qk_mma = [&](floatx4 (&s)[2][4], int q0) __attribute__((always_inline)) {
+  auto qk_mma = [&](floatx4 (&s)[2][QB], int q0, int nq) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = q0; qb < q0 + 2; ++qb)
+      for (int qb = q0; qb < q0 + nq; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][0], qf[qb][0], negoff[qb], 0, 0, 0);
 #pragma unroll
     for (int kk = 1; kk < 4; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = q0; qb < q0 + 2; ++qb)
+        for (int qb = q0; qb < q0 + nq; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][kk], qf[qb][kk], s[kb][qb], 0, 0, 0);
   };
   // O^T += V^T P^T and l += 1 P^T for head qb
-  auto pv_mma = [&](const bf16x8 (&p)[4], int qb) __attribute__((always_inline)) {
+  auto pv_mma = [&](const bf16x8 (&p)[QB], int qb) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], p[qb], o[db][qb], 0, 0, 0);
@@ -366,7 +360,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     const bool full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
     return full ? 0 : 1;
   };
-  auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][4]) __attribute__((always_inline)) {
+  auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -381,11 +375,11 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
           ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
         }
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
       }
   };
   // P = exp2(s) of head qb, rounded to bf16 in the B-operand layout
-  auto sexp = [&](const floatx4 (&s)[2][4], bf16x8 (&p)[4], int qb) __attribute__((always_inline)) {
+  auto sexp = [&](const floatx4 (&s)[2][QB], bf16x8 (&p)[QB], int qb) __attribute__((always_inline)) {
     u32x4 pk;
     pk[0] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][0]), __builtin_amdgcn_exp2f(s[0][qb][1]));
     pk[1] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][2]), __builtin_amdgcn_exp2f(s[0][qb][3]));
@@ -394,14 +388,14 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     p[qb] = __builtin_bit_cast(bf16x8, pk);
   };
   // whether some s of head qb in this lane exceeds its column's threshold
-  auto over = [&](const floatx4 (&s)[2][4], int qb) __attribute__((always_inline)) {
+  auto over = [&](const floatx4 (&s)[2][QB], int qb) __attribute__((always_inline)) {
     const float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
     return mx > thr[qb];
   };
   // the rare path: new references, rescaled O and l, shifted s
-  auto rebase = [&](floatx4 (&s)[2][4]) __attribute__((always_inline)) {
+  auto rebase = [&](floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const float off = -negoff[qb][0];
       const float cm = xg_max(__builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]))) + off;
       const float nref = __builtin_elementwise_maximum(ref[qb], cm);
@@ -423,10 +417,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 
   // ---- software pipeline over tiles ----
   // Step j, first half: PV(j-1) head by head on the matrix cores, with the
-  // threshold checks of S(j) and the exponentials of heads 0 and 1 (each
-  // head's P registers are rewritten only after PV(j-1) has consumed them).
-  // Second half: QK(j+1) of heads 0 and 1 with the exponentials of heads 2
-  // and 3, then QK(j+1) of heads 2 and 3.  The rare rescale sits between the
+  // threshold checks of S(j) and the exponentials of the wave's first head
+  // (each head's P registers are rewritten only after PV(j-1) has consumed
+  // them).  Second half: QK(j+1) of the first head with the exponentials of
+  // the second, then QK(j+1) of the second.  The rare rescale sits between the
   // halves.  K(j+1) is read from LDS at the start of the step, V(j) at its
   // end.  Tile j is read during steps j-1 and j; in step j the slot of tile
   // j-1 (free since the barrier that ended step j-1) receives tile j+2,
@@ -434,18 +428,18 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // issued.  The last step also multiplies a stale ring slot into S (and
   // stores stale staging registers into a free slot); those values are never
   // used.
-  floatx4 s[2][4];
-  bf16x8 p[4];
+  floatx4 s[2][QB];
+  bf16x8 p[QB];
   auto step = [&](int j, bool first) __attribute__((always_inline)) {
     const int mk = mask_kind(j);
     if (mk) apply_mask(j, mk, s);
     read_k(j + 1);
     bool rare = false;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       if (!first) pv_mma(p, qb);
       rare |= over(s, qb);
-      if (qb < 2) {
+      if (qb < QB / 2) {
         sexp(s, p, qb);
         // keep these exponentials between the matrix instructions: the
         // compiler would otherwise move them past the rare-path branch
@@ -454,16 +448,18 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     }
     if (__builtin_expect(__any(rare), 0)) {
       rebase(s);
-      sexp(s, p, 0);
-      sexp(s, p, 1);
+#pragma unroll
+      for (int qb = 0; qb < QB / 2; ++qb) sexp(s, p, qb);
     }
-    qk_mma(s, 0);
-    sexp(s, p, 2);
-    sexp(s, p, 3);
-    // the accumulator seeds of QK(j+1) of heads 2 and 3 pass through the
-    // same empty asm as their P, so these exponentials stay ahead of it
-    asm volatile("" : "+v"(p[2]), "+v"(p[3]), "+v"(negoff[2]), "+v"(negoff[3]));
-    qk_mma(s, 2);
+    qk_mma(s, 0, QB / 2);
+#pragma unroll
+    for (int qb = QB / 2; qb < QB; ++qb) {
+      sexp(s, p, qb);
+      // the accumulator seed of QK(j+1) of this head passes through the
+      // same empty asm as its P, so these exponentials stay ahead of it
+      asm volatile("" : "+v"(p[qb]), "+v"(negoff[qb]));
+    }
+    qk_mma(s, QB / 2, QB - QB / 2);
     read_v(j);
     store_tile(j + 2, stage);
     if (j + 3 < n_tiles) load_tile(j + 3, stage);
@@ -472,17 +468,16 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __syncthreads();
   if (n_tiles > 0) {
     read_k(0);
-    qk_mma(s, 0);
-    qk_mma(s, 2);
+    qk_mma(s, 0, QB);
     step(0, true);
     for (int j = 1; j < n_tiles; ++j) step(j, false);
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) pv_mma(p, qb);
+    for (int qb = 0; qb < QB; ++qb) pv_mma(p, qb);
   }
 
   // ---- epilogue: O / l, LSE ----
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = lsum[qb][0];
     const float inv = 1.f / lt;
     if (tq < C) {
