@@ -16,17 +16,18 @@
 //    the GQA sharing of explainer How It Works 1 applied inside the wave.
 //    The two waves of a SIMD hide each other's barrier, LDS and exponential
 //    latencies.
-//  * Key tiles of 32 keys in a 3-slot LDS ring, one barrier per tile.  Tiles
+//  * Key tiles of 32 keys in a 4-slot LDS ring, one barrier per tile.  Tiles
 //    outside the band i-W < j <= i of the work-group are never visited, so
 //    the work is O(N*W); only tiles that cut the diagonal or the window edge
-//    are masked.  Tiles move global -> VGPR staging -> LDS one step ahead.
+//    are masked.  Tiles move global -> LDS directly (buffer loads with the
+//    lds modifier, out-of-range rows read as zeros) three steps ahead.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: in the
 //    transposed form every lane owns one query column, so the softmax column
 //    statistics stay in one lane plus a 4-lane exchange (permlane swaps), and
 //    the score accumulator is already the B operand of the PV product.
 //  * V stays row-major in LDS; the A operand of the PV product is read with
-//    the transposing LDS load ds_read_b64_tr_b16.  Padded row pitches keep
-//    the operand reads free of bank conflicts.
+//    the transposing LDS load ds_read_b64_tr_b16.  XOR-swizzled 16-byte
+//    chunks keep the operand reads free of bank conflicts.
 //  * Softmax in the log2 domain with a lazy reference: Q is scaled by
 //    scale*log2(e) before its bf16 rounding, and the QK^T accumulator starts
 //    at minus the column's reference, so the matrix core returns score - ref
@@ -59,22 +60,24 @@ constexpr int HD = 128;      // head_dim of the fast kernel
 constexpr int NTHR = 512;    // 8 waves, two per SIMD
 constexpr int QB = 2;        // query heads per wave
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
-constexpr int NBUF = 3;      // LDS ring of K/V tiles
+constexpr int NBUF = 4;      // LDS ring of K/V tiles
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// LDS row pitches (bytes).  K rows are 272 B apart, so the 16 rows one
-// QK^T operand read touches start in 16 different 16-byte bank groups; V rows
-// are 288 B apart, so the 4 rows x 32 bytes of one transposing PV read (per
-// 16 lanes) fall in 8 different bank groups.
-constexpr int KPITCH = 272;
-constexpr int VPITCH = 288;
-constexpr int KTILEB = BN * KPITCH;
-constexpr int VTILEB = BN * VPITCH;
+// LDS tiles: 32 rows of 256 bytes, the 16-byte chunk c of row r stored at
+// position c ^ kswz(r) (K) or c ^ vswz(r) (V).  The 16 rows one QK^T operand
+// read touches then sit in 16 different bank groups, and so do the 8 rows x
+// 32 bytes of a transposing PV read.  Rows are unpadded so that the direct
+// global-to-LDS loads (1 KB per wave instruction) fill 4 whole rows.
+constexpr int ROWB = HD * 2;
+constexpr int KTILEB = BN * ROWB;
+constexpr int VTILEB = BN * ROWB;
 constexpr int RINGB = KTILEB + VTILEB;   // one K+V tile in the ring
+__device__ inline int kswz(int r) { return r & 15; }
+__device__ inline int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // Work-group barrier for the tile ring.  __syncthreads() carries a release
 // fence that makes the compiler wait for every outstanding vector-memory
@@ -82,10 +85,29 @@ constexpr int RINGB = KTILEB + VTILEB;   // one K+V tile in the ring
 // wave's own LDS operations are awaited, and the asm clobbers keep the
 // compiler from moving LDS accesses across the barrier.
 __device__ inline void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), no vmcnt/expcnt wait
-  asm volatile("" ::: "memory");
+  // lgkmcnt(0), and vmcnt(2): of the direct-to-LDS tile loads only the two
+  // issued in this step (the newest tile) may still be in flight
+  asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// One direct global-to-LDS load: every lane's 16 bytes at byte offset `off`
+// of the buffer `rsrc` (zeros when out of range) land at LDS address
+// lds + 16 * lane.  M0 carries the LDS address; it is saved and restored
+// around the load, and one wait state separates its write from the load.
+// The compiler does not count these loads: ring_barrier() waits for them.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, int off, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(off), "s"(rsrc)
+      : "memory");
 }
 
 // max over the 4 lanes l, l^16, l^32, l^48 (one query column)
@@ -100,6 +122,14 @@ __device__ inline float xg_max(float x) {
 __device__ inline float vmax4(floatx4 v) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]),
                                        __builtin_elementwise_maximum(v[2], v[3]));
+}
+
+// p, as a value the compiler knows to be the same in every lane
+__device__ inline void* uniform_ptr(const void* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
 }
 
 struct PrefillArgs {
@@ -229,10 +259,42 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   };
   auto store_tile = [&](int t, const u32x4 (&st)[2]) __attribute__((always_inline)) {
     uint8_t* Kb = smem + slot_off(t);
-    *reinterpret_cast<u32x4*>(Kb + lr * KPITCH + 16 * lc) = st[0];
-    *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * VPITCH + 16 * lc) = st[1];
+    *reinterpret_cast<u32x4*>(Kb + lr * ROWB + 16 * (lc ^ kswz(lr))) = st[0];
+    *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * ROWB + 16 * (lc ^ vswz(lr))) = st[1];
   };
-  // tiles 0 and 1 into the ring, tile 2 in flight
+  // Band tiles (every tile from 2 on; only tiles 0 and 1 can be sink tiles)
+  // go global -> LDS directly.  Wave w fills rows 4w .. 4w+3 of the K and of
+  // the V tile: lane L loads the chunk that belongs at position L%16 of row
+  // 4w + L/16 under the swizzle.  The descriptor (chunk or cache, uniform per
+  // tile) covers exactly this head's rows of that tensor, so rows past its
+  // end read as zeros; cache rows take the slot map, and rows before
+  // position 0 read slot 0 (they are masked).
+  const int nrec_c = __builtin_amdgcn_readfirstlane((C - 1) * (int)rowbytes + HD * 2);
+  const int nrec_s = __builtin_amdgcn_readfirstlane(kcache ? (S - 1) * (int)rowbytes + HD * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kchunk), (short)0, nrec_c, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vchunk), (short)0, nrec_c, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kcache ? kcache : kchunk), (short)0, nrec_s, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vcache ? vcache : vchunk), (short)0, nrec_s, 0x00020000);
+  const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
+  const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
+  const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
+  const unsigned lds_base = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
+  auto dma_tile = [&](int t) __attribute__((always_inline)) {
+    const int u0 = band_u0(t);
+    const unsigned lk = lds_base + (unsigned)(t % NBUF) * RINGB;
+    if (u0 >= 0) {
+      const int row = (u0 + rdma) * (int)rowbytes;
+      dma16(rkc, row + dk, lk);
+      dma16(rvc, row + dv, lk + KTILEB);
+    } else {
+      const int P = max(s0 + u0 + rdma, 0);
+      const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;
+      dma16(rks, row + dk, lk);
+      dma16(rvs, row + dv, lk + KTILEB);
+    }
+  };
+  // tiles 0 and 1 through registers into the ring, tile 2 in flight
   if (n_tiles > 0) {
     load_tile(0, stage);
     store_tile(0, stage);
@@ -241,7 +303,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     load_tile(1, stage);
     store_tile(1, stage);
   }
-  if (n_tiles > 2) load_tile(2, stage);
+  dma_tile(2);
 
   // ---- Q prologue: rotated, scaled, rounded to bf16, in the B-operand layout ----
   // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
@@ -309,23 +371,32 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   bf16x8 kop[2][4];   // K operand of the next QK^T: [kb][kk]
   bf16x8 vop[8];      // V^T operand of the next PV: [db]
   // K rows 16kb + i, d = 8(4kk+g) .. +7
+  // lane offsets of the operand reads in a tile (rows 16 apart share a swizzle)
+  int kofs[4], vofs[8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kofs[kk] = i * ROWB + 16 * ((4 * kk + g) ^ kswz(i));
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int r0 = 4 * g + (i >> 2);
+    vofs[db] = r0 * ROWB + 16 * ((2 * db + ((i & 3) >> 1)) ^ vswz(r0)) + 8 * (i & 1);
+  }
   auto read_k = [&](int t) __attribute__((always_inline)) {
-    const uint8_t* Kb = smem + slot_off(t) + i * KPITCH + 16 * g;
+    const uint8_t* Kb = smem + slot_off(t);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        kop[kb][kk] = *reinterpret_cast<const bf16x8*>(Kb + 16 * kb * KPITCH + 64 * kk);
+        kop[kb][kk] = *reinterpret_cast<const bf16x8*>(Kb + kofs[kk] + 16 * kb * ROWB);
   };
   // Transposing reads: lane i of a 16-lane group addresses key base+i/4,
   // d 16db+4(i%4), and receives V[base+e][16db+i] for e = 0..3 (base = 4g,
   // then 16+4g), which is the A operand of O^T += V^T P^T.
   auto read_v = [&](int t) __attribute__((always_inline)) {
-    lds_u8* Vb = (lds_u8*)smem + slot_off(t) + KTILEB + (4 * g + (i >> 2)) * VPITCH + 8 * (i & 3);
+    lds_u8* Vb = (lds_u8*)smem + slot_off(t) + KTILEB;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + 32 * db));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + 16 * VPITCH + 32 * db));
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db]));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db] + 16 * ROWB));
       const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       vop[db] = __builtin_bit_cast(bf16x8, va);
     }
@@ -422,12 +493,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // them).  Second half: QK(j+1) of the first head with the exponentials of
   // the second, then QK(j+1) of the second.  The rare rescale sits between the
   // halves.  K(j+1) is read from LDS at the start of the step, V(j) at its
-  // end.  Tile j is read during steps j-1 and j; in step j the slot of tile
-  // j-1 (free since the barrier that ended step j-1) receives tile j+2,
-  // which the barrier ending step j publishes, and the loads of tile j+3 are
-  // issued.  The last step also multiplies a stale ring slot into S (and
-  // stores stale staging registers into a free slot); those values are never
-  // used.
+  // end, so tile j is read during steps j-1 and j.  In step j the direct
+  // loads of tile j+3 go to the slot of tile j-1 (free since the barrier that
+  // ended step j-1); the barrier ending step j+1 waits for them, before their
+  // first read in step j+2.  Loads past the band read whatever the buffers
+  // hold there (or zeros) and are never used, and neither is the stale slot
+  // the last step multiplies into S.
   floatx4 s[2][QB];
   bf16x8 p[QB];
   auto step = [&](int j, bool first) __attribute__((always_inline)) {
@@ -461,8 +532,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     }
     qk_mma(s, QB / 2, QB - QB / 2);
     read_v(j);
-    store_tile(j + 2, stage);
-    if (j + 3 < n_tiles) load_tile(j + 3, stage);
+    dma_tile(j + 3);
     ring_barrier();
   };
   __syncthreads();
@@ -474,6 +544,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) pv_mma(p, qb);
   }
+  // the last tile loads must land before the work-group's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O / l, LSE ----
 #pragma unroll
