@@ -14,13 +14,16 @@
 //    t0+16(w&3) .. +15 for 2 of the 4 heads (32 query columns), so every K or
 //    V operand read from LDS feeds two matrix instructions (one per head):
 //    the GQA sharing of explainer How It Works 1 applied inside the wave.
-//    The two waves of a SIMD hide each other's barrier, LDS and exponential
-//    latencies.
-//  * Key tiles of 32 keys in a 4-slot LDS ring, one barrier per tile.  Tiles
-//    outside the band i-W < j <= i of the work-group are never visited, so
-//    the work is O(N*W); only tiles that cut the diagonal or the window edge
-//    are masked.  Tiles move global -> LDS directly (buffer loads with the
-//    lds modifier, out-of-range rows read as zeros) three steps ahead.
+//  * Each tile takes two phases, a barrier after each: a matrix phase (the
+//    QK^T and PV products, plus the LDS operand reads) and a vector phase
+//    (masks, threshold checks, exponentials, tile loads).  The two waves of
+//    a SIMD run one phase apart, so one feeds the matrix core while the
+//    other works on the vector ALU.
+//  * Key tiles of 32 keys in an 8-slot LDS ring.  Tiles outside the band
+//    i-W < j <= i of the work-group are never visited, so the work is
+//    O(N*W); only tiles that cut the diagonal or the window edge are
+//    masked.  Tiles move global -> LDS directly (buffer loads with the lds
+//    modifier, out-of-range rows read as zeros) four tiles ahead.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: in the
 //    transposed form every lane owns one query column, so the softmax column
 //    statistics stay in one lane plus a 4-lane exchange (permlane swaps), and
@@ -35,8 +38,6 @@
 //    the vector ALU.  The reference moves (and O and l are rescaled) only
 //    when a score exceeds it by more than 2^8; numerator and denominator
 //    carry the same reference, so the result is the same.
-//  * Each step interleaves PV(j-1) with the exponentials of one head, and
-//    QK(j+1) with those of the other.
 //  * Work-groups are renumbered so that the 8 XCDs each take a contiguous
 //    range of (sequence, KV head, query tile): the K/V of one KV head then
 //    stays in one XCD's L2.  Query tiles run longest-first.
@@ -60,7 +61,7 @@ constexpr int HD = 128;      // head_dim of the fast kernel
 constexpr int NTHR = 512;    // 8 waves, two per SIMD
 constexpr int QB = 2;        // query heads per wave
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
-constexpr int NBUF = 4;      // LDS ring of K/V tiles
+constexpr int NBUF = 8;      // LDS ring of K/V tiles
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -85,9 +86,12 @@ __device__ inline int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 // wave's own LDS operations are awaited, and the asm clobbers keep the
 // compiler from moving LDS accesses across the barrier.
 __device__ inline void ring_barrier() {
-  // lgkmcnt(0), and vmcnt(2): of the direct-to-LDS tile loads only the two
-  // issued in this step (the newest tile) may still be in flight
-  asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
+  // vmcnt(2): of the direct-to-LDS tile loads only the two of the newest
+  // tile may still be in flight.  lgkmcnt(0) goes through the builtin so
+  // that the compiler knows the LDS reads are complete and adds no waits of
+  // its own after the barrier.
+  asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -294,7 +298,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       dma16(rvs, row + dv, lk + KTILEB);
     }
   };
-  // tiles 0 and 1 through registers into the ring, tile 2 in flight
+  // tiles 0 and 1 through registers into the ring, tiles 2 and 3 in flight
   if (n_tiles > 0) {
     load_tile(0, stage);
     store_tile(0, stage);
@@ -304,6 +308,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     store_tile(1, stage);
   }
   dma_tile(2);
+  dma_tile(3);
 
   // ---- Q prologue: rotated, scaled, rounded to bf16, in the B-operand layout ----
   // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
@@ -486,63 +491,85 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- software pipeline over tiles ----
-  // Step j, first half: PV(j-1) head by head on the matrix cores, with the
-  // threshold checks of S(j) and the exponentials of the wave's first head
-  // (each head's P registers are rewritten only after PV(j-1) has consumed
-  // them).  Second half: QK(j+1) of the first head with the exponentials of
-  // the second, then QK(j+1) of the second.  The rare rescale sits between the
-  // halves.  K(j+1) is read from LDS at the start of the step, V(j) at its
-  // end, so tile j is read during steps j-1 and j.  In step j the direct
-  // loads of tile j+3 go to the slot of tile j-1 (free since the barrier that
-  // ended step j-1); the barrier ending step j+1 waits for them, before their
-  // first read in step j+2.  Loads past the band read whatever the buffers
-  // hold there (or zeros) and are never used, and neither is the stale slot
-  // the last step multiplies into S.
+  // ---- software pipeline over tiles: two phases per tile ----
+  // Matrix phase j: QK(j) (S of tile j, seeded with -off), then PV(j-1)
+  // head by head, with K(j+1) and V(j) read from LDS into the operand
+  // registers as the products release them.
+  // Vector phase j: the mask and threshold checks of S(j), the rare rescale,
+  // P(j) = exp2(S(j)), and the direct loads of tile j+4.  A barrier ends
+  // every phase.  Waves 4..7 run one phase behind waves 0..3, so the two
+  // waves of each SIMD (w and w+4) are always in different phases: one feeds
+  // the matrix core and the LDS while the other uses the vector ALU.
+  // Ring timing (phases counted from the first matrix phase of waves 0..3:
+  // matrix phase j is phase 2j for those, 2j+1 for waves 4..7).  Every
+  // barrier waits for all but the newest tile load of the wave, so tile t,
+  // loaded in phases 2t-7 and 2t-6, is complete at the barrier ending phase
+  // 2t-4 and visible before its first read (K(t) in phase 2t-2).  Its last
+  // read (V(t), phase 2t+1) completes before the barrier ending the vector
+  // phase that follows (lgkmcnt(0)), and the loads of tile t+8 into its slot
+  // start in phase 2t+9.  Loads past the band read whatever the buffers hold
+  // there (or zeros) and are never used.
   floatx4 s[2][QB];
   bf16x8 p[QB];
-  auto step = [&](int j, bool first) __attribute__((always_inline)) {
+  auto mphase = [&](int j, bool qk, bool pv) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (qk) qk_mma(s, 0, QB);
+    __builtin_amdgcn_sched_barrier(0);
+    if (pv) {
+      pv_mma(p, 0);
+      if (qk) read_k(j + 1);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pv_mma(p, 1);
+      if (qk) read_v(j);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    } else {
+      read_k(j + 1);
+      read_v(j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto vphase = [&](int j) __attribute__((always_inline)) {
     const int mk = mask_kind(j);
     if (mk) apply_mask(j, mk, s);
-    read_k(j + 1);
     bool rare = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (!first) pv_mma(p, qb);
-      rare |= over(s, qb);
-      if (qb < QB / 2) {
-        sexp(s, p, qb);
-        // keep these exponentials between the matrix instructions: the
-        // compiler would otherwise move them past the rare-path branch
-        asm volatile("" : "+v"(p[qb]));
-      }
-    }
-    if (__builtin_expect(__any(rare), 0)) {
-      rebase(s);
+    for (int qb = 0; qb < QB; ++qb) rare |= over(s, qb);
+    if (__builtin_expect(__any(rare), 0)) rebase(s);
 #pragma unroll
-      for (int qb = 0; qb < QB / 2; ++qb) sexp(s, p, qb);
-    }
-    qk_mma(s, 0, QB / 2);
+    for (int qb = 0; qb < QB; ++qb) sexp(s, p, qb);
+    // the empty asm keeps the exponentials in this phase
 #pragma unroll
-    for (int qb = QB / 2; qb < QB; ++qb) {
-      sexp(s, p, qb);
-      // the accumulator seed of QK(j+1) of this head passes through the
-      // same empty asm as its P, so these exponentials stay ahead of it
-      asm volatile("" : "+v"(p[qb]), "+v"(negoff[qb]));
-    }
-    qk_mma(s, QB / 2, QB - QB / 2);
-    read_v(j);
-    dma_tile(j + 3);
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(p[qb]));
+    __builtin_amdgcn_sched_barrier(0);
+    dma_tile(j + 4);
     ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
+  const bool lead = (w >> 2) == 0;
   __syncthreads();
   if (n_tiles > 0) {
     read_k(0);
-    qk_mma(s, 0, QB);
-    step(0, true);
-    for (int j = 1; j < n_tiles; ++j) step(j, false);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) pv_mma(p, qb);
+    if (!lead) __builtin_amdgcn_s_barrier();
+    mphase(0, true, false);
+    vphase(0);
+    for (int j = 1; j < n_tiles; ++j) {
+      mphase(j, true, true);
+      vphase(j);
+    }
+    mphase(n_tiles, false, true);
+    if (lead) __builtin_amdgcn_s_barrier();
   }
   // the last tile loads must land before the work-group's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
