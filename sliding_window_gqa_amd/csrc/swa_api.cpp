@@ -44,10 +44,10 @@ int check_params(const swa_params* p, Shape* sh) {
 
 RopeTab rope_table(const swa_params* p) {
   RopeTab rt;
-  for (int k = 0; k < swa::kMaxPairs; ++k) rt.freq[k] = 0.0;
+  for (int k = 0; k < swa::kMaxPairs; ++k) rt.rev[k] = 0.0;
   if (p->rope_theta > 0.f)
     for (int k = 0; k < p->head_dim / 2; ++k)
-      rt.freq[k] = pow((double)p->rope_theta, -2.0 * k / p->head_dim);
+      rt.rev[k] = pow((double)p->rope_theta, -2.0 * k / p->head_dim) / (2.0 * 3.14159265358979323846);
   return rt;
 }
 

@@ -70,7 +70,7 @@ struct DecodeArgs {
 __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
   __shared__ float sm_m[4][4], sm_l[4][4];
   __shared__ float sm_o[4][4][HD];
-  __shared__ double rope_freq[kMaxPairs];
+  __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
   // The RoPE frequencies are staged in LDS (one coalesced read instead of a
   // dependent kernel-argument load per element).
-  if (tid < kMaxPairs) rope_freq[tid] = a.rt.freq[tid];
+  if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
   __syncthreads();
   bf16x8 qf[4];
   auto load_q = [&]() __attribute__((always_inline)) {
@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
         float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
         if (sh.rope) {
           float cs, sn;
-          rope_cs(p, rope_freq[4 * (4 * kk + g) + jj], cs, sn);
+          rope_cs(p, rope_rev[4 * (4 * kk + g) + jj], cs, sn);
           rotate(x0, x1, cs, sn);
         }
         r[jj] = pack_bf16(x0, x1);
@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(Shape sh, RopeTab rt
 #pragma unroll
     for (int kk = 0; kk < D / 2; ++kk) {
       float cs, sn;
-      rope_cs(p, rt.freq[kk], cs, sn);
+      rope_cs(p, rt.rev[kk], cs, sn);
       rotate(qv[2 * kk], qv[2 * kk + 1], cs, sn);
     }
   }

@@ -62,6 +62,7 @@ constexpr int NTHR = 512;    // 8 waves, two per SIMD
 constexpr int QB = 2;        // query heads per wave
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
 constexpr int NBUF = 8;      // LDS ring of K/V tiles
+static_assert(BN == 32, "the tile arithmetic below divides by 32 with >> 5");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -159,7 +160,7 @@ struct PrefillArgs {
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
-  __shared__ double rope_freq[kMaxPairs];
+  __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
   // ---- work mapping: XCD-contiguous, longest tiles first ----
@@ -266,7 +267,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     *reinterpret_cast<u32x4*>(Kb + lr * ROWB + 16 * (lc ^ kswz(lr))) = st[0];
     *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * ROWB + 16 * (lc ^ vswz(lr))) = st[1];
   };
-  // Band tiles (every tile from 2 on; only tiles 0 and 1 can be sink tiles)
+  // Band tiles (all tiles but sink tiles, which can only be tiles 0 and 1)
   // go global -> LDS directly.  Wave w fills rows 4w .. 4w+3 of the K and of
   // the V tile: lane L loads the chunk that belongs at position L%16 of row
   // 4w + L/16 under the swizzle.  The descriptor (chunk or cache, uniform per
@@ -298,14 +299,20 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       dma16(rvs, row + dv, lk + KTILEB);
     }
   };
-  // tiles 0 and 1 through registers into the ring, tiles 2 and 3 in flight
-  if (n_tiles > 0) {
-    load_tile(0, stage);
-    store_tile(0, stage);
-  }
-  if (n_tiles > 1) {
-    load_tile(1, stage);
-    store_tile(1, stage);
+  // tiles 0 .. 3 in flight while Q is prepared; tiles 0 and 1 go through
+  // registers when the work-group has sink tiles
+  if (n_stile == 0) {
+    dma_tile(0);
+    dma_tile(1);
+  } else {
+    if (n_tiles > 0) {
+      load_tile(0, stage);
+      store_tile(0, stage);
+    }
+    if (n_tiles > 1) {
+      load_tile(1, stage);
+      store_tile(1, stage);
+    }
   }
   dma_tile(2);
   dma_tile(3);
@@ -315,8 +322,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // The softmax scale and log2(e) are applied before the rounding, so that
   // QK^T yields scores in the log2 domain directly.
   const float c2 = sh.scale_log2;
-  if (tid < kMaxPairs) rope_freq[tid] = a.rt.freq[tid];
-  __syncthreads();
+  if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
+  // LDS-only barrier: __syncthreads() would also wait for the tile loads
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   bf16x8 qf[QB][4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -324,7 +335,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       if (sh.rope) {
-        rope_cs(I, rope_freq[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
+        rope_cs(I, rope_rev[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
       } else {
         cs[jj] = 1.f;
         sn[jj] = 0.f;
@@ -429,12 +440,18 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], p[qb], o[db][qb], 0, 0, 0);
     lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[qb], lsum[qb], 0, 0, 0);
   };
-  // mask of tile j for this wave: 0 none, 1 band edge / diagonal, 2 sink tile
+  // mask of tile j for this wave: 0 none, 1 band edge / diagonal, 2 sink tile.
+  // Band tile j (keys u0 .. u0+31, u0 = t0 + 32(m + j)) needs no mask when
+  // all its keys precede the wave's first query (u0 + 31 <= q0w), lie inside
+  // the window of its last query (u0 > q0w + 15 - W) and exist (s0 + u0 >=
+  // 0); each condition bounds j on one side, so the unmasked tiles are the
+  // range jlo <= j <= jhi (>> 5 is the floor division by 32).
+  const int mfull = kmin - n_stile, dq = q0w - t0;
+  const int jhi = ((dq - (BN - 1)) >> 5) - mfull;
+  const int jlo = max(max(n_stile, ((dq + 15 - W) >> 5) + 1 - mfull), -((s0 + t0) >> 5) - mfull);
   auto mask_kind = [&](int j) __attribute__((always_inline)) {
     if (j < n_stile) return 2;
-    const int u0 = band_u0(j);
-    const bool full = (u0 + BN - 1 <= q0w) && (u0 > q0w + 15 - W) && (s0 + u0 >= 0);
-    return full ? 0 : 1;
+    return (j >= jlo && j <= jhi) ? 0 : 1;
   };
   auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
 #pragma unroll
@@ -629,7 +646,7 @@ __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab r
 #pragma unroll
     for (int kk = 0; kk < D / 2; ++kk) {
       float cs, sn;
-      rope_cs(I, rt.freq[kk], cs, sn);
+      rope_cs(I, rt.rev[kk], cs, sn);
       rotate(qv[2 * kk], qv[2 * kk + 1], cs, sn);
     }
   }

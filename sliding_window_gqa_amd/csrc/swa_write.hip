@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float cs, sn;
-      rope_cs(p, rt.freq[4 * c + j], cs, sn);
+      rope_cs(p, rt.rev[4 * c + j], cs, sn);
       rotate(x[2 * j], x[2 * j + 1], cs, sn);
     }
   }
