@@ -47,6 +47,8 @@
 // not cover (e.g. the float32 path).
 #include <math.h>
 
+#include <atomic>
+#include <climits>
 #include <type_traits>
 
 #include "swa_device.hpp"
@@ -148,6 +150,7 @@ struct PrefillArgs {
   const int32_t* start;
   int C;
   int n_qtiles;
+  int n_items;          // n_qtiles * Hkv * B
   uint16_t* out;
   float* lse;
 };
@@ -163,451 +166,470 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
-  // ---- work mapping: XCD-contiguous, longest tiles first ----
-  const int nwg = gridDim.x;
-  const int wg = blockIdx.x;
-  const int xcd = wg & 7, idx = wg >> 3, q8 = nwg >> 3, r8 = nwg & 7;
-  const int L = xcd * q8 + min(xcd, r8) + idx;
-  const int per_b = sh.Hkv * a.n_qtiles;
-  const int b = L / per_b;
-  const int rem = L - b * per_b;
-  const int kvh = rem / a.n_qtiles;
-  const int qt = a.n_qtiles - 1 - (rem - kvh * a.n_qtiles);
-
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, i = lane & 15, g = lane >> 4;
-  const int s0 = a.start[b];
-  const int C = a.C;
-  const int t0 = qt * BM;
-  const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
-  const int tq = q0w + i;                 // this lane's query
-  const int I = s0 + tq;                  // its absolute position
-  const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
-  const int W = sh.W;
-  const int S = sh.S;
-  const int nsink = sh.n_sink;
-
-  // ---- tile list: [sink tiles] + band tiles k = kmin..1 (u0 = t0 + 32k) ----
-  // Band tiles cover chunk-relative key positions t0 - W + 1 .. t0 + 63;
-  // sink tiles cover absolute positions 0 .. n_sink-1 for queries whose
-  // window no longer contains them.
-  const int tq_last = min(t0 + BM, C) - 1;
-  const int n_stile = (nsink > 0 && (s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
-  const int k_lo = -((W - 1 + BN - 1) / BN);
-  const int k_clip = -((s0 + t0 + BN - 1) / BN);
-  const int kmin = max(k_lo, k_clip);
-  const int n_tiles = n_stile + (2 - kmin);
-  auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
-
-  // ---- tile loads: global -> staging VGPRs -> padded LDS ----
-  // Thread (lr = tid/16, lc = tid%16) moves 16-byte chunk lc of row lr of
-  // the K and of the V tile.  A tile's loads are issued one pipeline step
-  // before it is stored.
-  const long long rowstride_c = (long long)sh.Hkv * HD;                // elements between tokens
-  const uint16_t* kchunk = a.kr + ((long long)b * C * sh.Hkv + kvh) * HD;
-  const uint16_t* vchunk = a.v + ((long long)b * C * sh.Hkv + kvh) * HD;
-  const uint16_t* kcache = a.kc ? a.kc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
-  const uint16_t* vcache = a.vc ? a.vc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
-  const int lr = tid >> 4, lc = tid & 15;
-  const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;
-  const unsigned voff0 = (unsigned)lr * rowbytes + 16u * lc;
-  u32x4 stage[2];   // K row lr, V row lr
-  // The loader captures by value and selects pointer values only: with
-  // captures by reference, or a struct returned from several places, the
-  // compiler selects between addresses of the pointer variables and keeps
-  // them in scratch memory.
-  auto load_tile = [=](int t, u32x4 (&st)[2]) __attribute__((always_inline)) {
-    const bool is_sink = t < n_stile;
-    const int u0 = is_sink ? 0 : band_u0(t);
-    const bool in_chunk = u0 >= 0;
-    const int P0 = s0 + u0;
-    // fast path: the 32 rows are 32 consecutive rows of the chunk or cache
-    // (the slot arithmetic is done for cache tiles only)
-    int slot0 = 0;
-    bool fast = !is_sink && in_chunk && u0 + BN <= C;
-    if (!is_sink && !in_chunk && P0 >= nsink) {
-      slot0 = nsink + (P0 - nsink) % W;
-      fast = slot0 + BN <= S;
-    }
-    if (fast) {
-      const long long row0 = in_chunk ? u0 : slot0;
-      const uint8_t* kb8 = reinterpret_cast<const uint8_t*>((in_chunk ? kchunk : kcache) + row0 * rowstride_c);
-      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>((in_chunk ? vchunk : vcache) + row0 * rowstride_c);
-      st[0] = *reinterpret_cast<const u32x4*>(kb8 + voff0);
-      st[1] = *reinterpret_cast<const u32x4*>(vb8 + voff0);
-    } else {
-      // edge tiles: each row is located on its own, clamped to a row that
-      // exists (rows that are not keys of any query are masked later)
-      {
-        const int r = lr;
-        // absolute position of the row; rows of band tiles with u0 < 0 are
-        // cache rows, those with u0 >= 0 chunk rows
-        const int P = is_sink ? min(BN * t + r, nsink - 1) : max(P0 + r, 0);
-        const bool from_cache = P < s0 && kcache != nullptr;
-        const int roff = from_cache ? (P < nsink ? P : nsink + (P - nsink) % W)
-                                    : min(max(P - s0, 0), C - 1);
-        const long long eoff = (long long)roff * rowstride_c + 8 * lc;
-        st[0] = *reinterpret_cast<const u32x4*>((from_cache ? kcache : kchunk) + eoff);
-        st[1] = *reinterpret_cast<const u32x4*>((from_cache ? vcache : vchunk) + eoff);
-      }
-    }
-  };
-  // Byte offset of tile t's ring slot.  The empty asm hides the value's
-  // origin from loop strength reduction, which would otherwise keep one
-  // induction variable per LDS address instead of folding the constant parts
-  // into the instructions' offset fields.
-  auto slot_off = [&](int t) __attribute__((always_inline)) {
-    unsigned off = (unsigned)(t % NBUF) * RINGB;
-    asm volatile("" : "+s"(off));
-    return off;
-  };
-  auto store_tile = [&](int t, const u32x4 (&st)[2]) __attribute__((always_inline)) {
-    uint8_t* Kb = smem + slot_off(t);
-    *reinterpret_cast<u32x4*>(Kb + lr * ROWB + 16 * (lc ^ kswz(lr))) = st[0];
-    *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * ROWB + 16 * (lc ^ vswz(lr))) = st[1];
-  };
-  // Band tiles (all tiles but sink tiles, which can only be tiles 0 and 1)
-  // go global -> LDS directly.  Wave w fills rows 4w .. 4w+3 of the K and of
-  // the V tile: lane L loads the chunk that belongs at position L%16 of row
-  // 4w + L/16 under the swizzle.  The descriptor (chunk or cache, uniform per
-  // tile) covers exactly this head's rows of that tensor, so rows past its
-  // end read as zeros; cache rows take the slot map, and rows before
-  // position 0 read slot 0 (they are masked).
-  const int nrec_c = __builtin_amdgcn_readfirstlane((C - 1) * (int)rowbytes + HD * 2);
-  const int nrec_s = __builtin_amdgcn_readfirstlane(kcache ? (S - 1) * (int)rowbytes + HD * 2 : 0);
-  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kchunk), (short)0, nrec_c, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vchunk), (short)0, nrec_c, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kcache ? kcache : kchunk), (short)0, nrec_s, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vcache ? vcache : vchunk), (short)0, nrec_s, 0x00020000);
-  const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
-  const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
-  const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
-  const unsigned lds_base = __builtin_amdgcn_readfirstlane(
-      (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
-  auto dma_tile = [&](int t) __attribute__((always_inline)) {
-    const int u0 = band_u0(t);
-    const unsigned lk = lds_base + (unsigned)(t % NBUF) * RINGB;
-    if (u0 >= 0) {
-      const int row = (u0 + rdma) * (int)rowbytes;
-      dma16(rkc, row + dk, lk);
-      dma16(rvc, row + dv, lk + KTILEB);
-    } else {
-      const int P = max(s0 + u0 + rdma, 0);
-      const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;
-      dma16(rks, row + dk, lk);
-      dma16(rvs, row + dv, lk + KTILEB);
-    }
-  };
-  // tiles 0 .. 3 in flight while Q is prepared; tiles 0 and 1 go through
-  // registers when the work-group has sink tiles
-  if (n_stile == 0) {
-    dma_tile(0);
-    dma_tile(1);
-  } else {
-    if (n_tiles > 0) {
-      load_tile(0, stage);
-      store_tile(0, stage);
-    }
-    if (n_tiles > 1) {
-      load_tile(1, stage);
-      store_tile(1, stage);
-    }
-  }
-  dma_tile(2);
-  dma_tile(3);
-
-  // ---- Q prologue: rotated, scaled, rounded to bf16, in the B-operand layout ----
-  // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
-  // The softmax scale and log2(e) are applied before the rounding, so that
-  // QK^T yields scores in the log2 domain directly.
-  const float c2 = sh.scale_log2;
   if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
-  // LDS-only barrier: __syncthreads() would also wait for the tile loads
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  bf16x8 qf[QB][4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    float cs[4], sn[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      if (sh.rope) {
-        rope_cs(I, rope_rev[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
+  __syncthreads();
+
+  // ---- work mapping ----
+  // Items (sequence, KV head, query tile) are numbered sequence-major, KV
+  // head next, query tiles longest first, and split into 8 contiguous
+  // ranges, one per XCD (work-group w runs on XCD w mod 8), so that the K/V
+  // of a KV head stays in one XCD's L2.  With one item per work-group the
+  // hardware hands them out in that order; with fewer work-groups (one per
+  // CU, a multiple of 8) each takes the items of its XCD's range in a
+  // serpentine order over the rounds, which evens out the longest-first
+  // lengths.
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7;
+  for (int round = 0;; ++round) {
+    int L;
+    if (G >= a.n_items) {
+      if (round > 0) break;
+      const int q8 = G >> 3, r8 = G & 7;
+      L = xcd * q8 + min(xcd, r8) + (wg >> 3);
+    } else {
+      const int q8 = a.n_items >> 3, r8 = a.n_items & 7;
+      const int lo = xcd * q8 + min(xcd, r8), cnt = q8 + (xcd < r8 ? 1 : 0);
+      const int nl = G >> 3, li = wg >> 3;
+      const int pos = round * nl + ((round & 1) ? nl - 1 - li : li);
+      if (pos >= cnt) break;
+      L = lo + pos;
+    }
+    const int per_b = sh.Hkv * a.n_qtiles;
+    const int b = L / per_b;
+    const int rem = L - b * per_b;
+    const int kvh = rem / a.n_qtiles;
+    const int qt = a.n_qtiles - 1 - (rem - kvh * a.n_qtiles);
+
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int s0 = a.start[b];
+    const int C = a.C;
+    const int t0 = qt * BM;
+    const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
+    const int tq = q0w + i;                 // this lane's query
+    const int I = s0 + tq;                  // its absolute position
+    const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
+    const int W = sh.W;
+    const int S = sh.S;
+    const int nsink = sh.n_sink;
+
+    // ---- tile list: [sink tiles] + band tiles k = kmin..1 (u0 = t0 + 32k) ----
+    // Band tiles cover chunk-relative key positions t0 - W + 1 .. t0 + 63;
+    // sink tiles cover absolute positions 0 .. n_sink-1 for queries whose
+    // window no longer contains them.
+    const int tq_last = min(t0 + BM, C) - 1;
+    const int n_stile = (nsink > 0 && (s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
+    const int k_lo = -((W - 1 + BN - 1) / BN);
+    const int k_clip = -((s0 + t0 + BN - 1) / BN);
+    const int kmin = max(k_lo, k_clip);
+    const int n_tiles = n_stile + (2 - kmin);
+    auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
+
+    // ---- tile loads: global -> staging VGPRs -> padded LDS ----
+    // Thread (lr = tid/16, lc = tid%16) moves 16-byte chunk lc of row lr of
+    // the K and of the V tile.  A tile's loads are issued one pipeline step
+    // before it is stored.
+    const long long rowstride_c = (long long)sh.Hkv * HD;                // elements between tokens
+    const uint16_t* kchunk = a.kr + ((long long)b * C * sh.Hkv + kvh) * HD;
+    const uint16_t* vchunk = a.v + ((long long)b * C * sh.Hkv + kvh) * HD;
+    const uint16_t* kcache = a.kc ? a.kc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
+    const uint16_t* vcache = a.vc ? a.vc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
+    const int lr = tid >> 4, lc = tid & 15;
+    const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;
+    const unsigned voff0 = (unsigned)lr * rowbytes + 16u * lc;
+    u32x4 stage[2];   // K row lr, V row lr
+    // The loader captures by value and selects pointer values only: with
+    // captures by reference, or a struct returned from several places, the
+    // compiler selects between addresses of the pointer variables and keeps
+    // them in scratch memory.
+    auto load_tile = [=](int t, u32x4 (&st)[2]) __attribute__((always_inline)) {
+      const bool is_sink = t < n_stile;
+      const int u0 = is_sink ? 0 : band_u0(t);
+      const bool in_chunk = u0 >= 0;
+      const int P0 = s0 + u0;
+      // fast path: the 32 rows are 32 consecutive rows of the chunk or cache
+      // (the slot arithmetic is done for cache tiles only)
+      int slot0 = 0;
+      bool fast = !is_sink && in_chunk && u0 + BN <= C;
+      if (!is_sink && !in_chunk && P0 >= nsink) {
+        slot0 = nsink + (P0 - nsink) % W;
+        fast = slot0 + BN <= S;
+      }
+      if (fast) {
+        const long long row0 = in_chunk ? u0 : slot0;
+        const uint8_t* kb8 = reinterpret_cast<const uint8_t*>((in_chunk ? kchunk : kcache) + row0 * rowstride_c);
+        const uint8_t* vb8 = reinterpret_cast<const uint8_t*>((in_chunk ? vchunk : vcache) + row0 * rowstride_c);
+        st[0] = *reinterpret_cast<const u32x4*>(kb8 + voff0);
+        st[1] = *reinterpret_cast<const u32x4*>(vb8 + voff0);
       } else {
-        cs[jj] = 1.f;
-        sn[jj] = 0.f;
+        // edge tiles: each row is located on its own, clamped to a row that
+        // exists (rows that are not keys of any query are masked later)
+        {
+          const int r = lr;
+          // absolute position of the row; rows of band tiles with u0 < 0 are
+          // cache rows, those with u0 >= 0 chunk rows
+          const int P = is_sink ? min(BN * t + r, nsink - 1) : max(P0 + r, 0);
+          const bool from_cache = P < s0 && kcache != nullptr;
+          const int roff = from_cache ? (P < nsink ? P : nsink + (P - nsink) % W)
+                                      : min(max(P - s0, 0), C - 1);
+          const long long eoff = (long long)roff * rowstride_c + 8 * lc;
+          st[0] = *reinterpret_cast<const u32x4*>((from_cache ? kcache : kchunk) + eoff);
+          st[1] = *reinterpret_cast<const u32x4*>((from_cache ? vcache : vchunk) + eoff);
+        }
+      }
+    };
+    // Byte offset of tile t's ring slot.  The empty asm hides the value's
+    // origin from loop strength reduction, which would otherwise keep one
+    // induction variable per LDS address instead of folding the constant parts
+    // into the instructions' offset fields.
+    auto slot_off = [&](int t) __attribute__((always_inline)) {
+      unsigned off = (unsigned)(t % NBUF) * RINGB;
+      asm volatile("" : "+s"(off));
+      return off;
+    };
+    auto store_tile = [&](int t, const u32x4 (&st)[2]) __attribute__((always_inline)) {
+      uint8_t* Kb = smem + slot_off(t);
+      *reinterpret_cast<u32x4*>(Kb + lr * ROWB + 16 * (lc ^ kswz(lr))) = st[0];
+      *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * ROWB + 16 * (lc ^ vswz(lr))) = st[1];
+    };
+    // Band tiles (all tiles but sink tiles, which can only be tiles 0 and 1)
+    // go global -> LDS directly.  Wave w fills rows 4w .. 4w+3 of the K and of
+    // the V tile: lane L loads the chunk that belongs at position L%16 of row
+    // 4w + L/16 under the swizzle.  The descriptor (chunk or cache, uniform per
+    // tile) covers exactly this head's rows of that tensor, so rows past its
+    // end read as zeros; cache rows take the slot map, and rows before
+    // position 0 read slot 0 (they are masked).
+    const int nrec_c = __builtin_amdgcn_readfirstlane((C - 1) * (int)rowbytes + HD * 2);
+    const int nrec_s = __builtin_amdgcn_readfirstlane(kcache ? (S - 1) * (int)rowbytes + HD * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kchunk), (short)0, nrec_c, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vchunk), (short)0, nrec_c, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kcache ? kcache : kchunk), (short)0, nrec_s, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vcache ? vcache : vchunk), (short)0, nrec_s, 0x00020000);
+    const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
+    const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
+    const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
+    const unsigned lds_base = __builtin_amdgcn_readfirstlane(
+        (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
+    auto dma_tile = [&](int t) __attribute__((always_inline)) {
+      const int u0 = band_u0(t);
+      const unsigned lk = lds_base + (unsigned)(t % NBUF) * RINGB;
+      if (u0 >= 0) {
+        const int row = (u0 + rdma) * (int)rowbytes;
+        dma16(rkc, row + dk, lk);
+        dma16(rvc, row + dv, lk + KTILEB);
+      } else {
+        const int P = max(s0 + u0 + rdma, 0);
+        const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;
+        dma16(rks, row + dk, lk);
+        dma16(rvs, row + dv, lk + KTILEB);
+      }
+    };
+    // tiles 0 .. 3 in flight while Q is prepared; tiles 0 and 1 go through
+    // registers when the work-group has sink tiles
+    if (n_stile == 0) {
+      dma_tile(0);
+      dma_tile(1);
+    } else {
+      if (n_tiles > 0) {
+        load_tile(0, stage);
+        store_tile(0, stage);
+      }
+      if (n_tiles > 1) {
+        load_tile(1, stage);
+        store_tile(1, stage);
       }
     }
+    dma_tile(2);
+    dma_tile(3);
+
+    // ---- Q prologue: rotated, scaled, rounded to bf16, in the B-operand layout ----
+    // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
+    // The softmax scale and log2(e) are applied before the rounding, so that
+    // QK^T yields scores in the log2 domain directly.
+    const float c2 = sh.scale_log2;
+    bf16x8 qf[QB][4];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (tq < C)
-        wv = *reinterpret_cast<const u32x4*>(
-            a.q + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD + 8 * (4 * kk + g));
-      u32x4 r;
+    for (int kk = 0; kk < 4; ++kk) {
+      float cs[4], sn[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
-        rotate(x0, x1, cs[jj], sn[jj]);
-        r[jj] = pack_bf16(x0 * c2, x1 * c2);
+        if (sh.rope) {
+          rope_cs(I, rope_rev[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
+        } else {
+          cs[jj] = 1.f;
+          sn[jj] = 0.f;
+        }
       }
-      qf[qb][kk] = __builtin_bit_cast(bf16x8, r);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        u32x4 wv = {0u, 0u, 0u, 0u};
+        if (tq < C)
+          wv = *reinterpret_cast<const u32x4*>(
+              a.q + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD + 8 * (4 * kk + g));
+        u32x4 r;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float x0 = bf16_lo(wv[jj]), x1 = bf16_hi(wv[jj]);
+          rotate(x0, x1, cs[jj], sn[jj]);
+          r[jj] = pack_bf16(x0 * c2, x1 * c2);
+        }
+        qf[qb][kk] = __builtin_bit_cast(bf16x8, r);
+      }
     }
-  }
 
-  // ---- softmax state of each query column (one per head qb) ----
-  // ref[qb]: reference of the exponentials, the running max of the scores
-  //          up to the lazy threshold; -inf until the column has seen a key.
-  // The QK^T accumulator starts at -off (off = ref, or 0 while ref = -inf),
-  // so the matrix core returns s = score - off and P = exp2(s).  A tile is
-  // taken as is unless some s exceeds thr (kTau, or -inf while ref = -inf);
-  // then the rare path moves ref to the new max, rescales O and l by
-  // exp2(ref_old - ref_new) and shifts s.
-  float ref[QB], thr[QB];
-  floatx4 negoff[QB];
-  floatx4 o[8][QB];
-  // row sums of P accumulate on the matrix core: an all-ones A operand makes
-  // every row of lsum[qb] the sum over keys of P for this lane's query
-  floatx4 lsum[QB];
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    // ---- softmax state of each query column (one per head qb) ----
+    // ref[qb]: reference of the exponentials, the running max of the scores
+    //          up to the lazy threshold; -inf until the column has seen a key.
+    // The QK^T accumulator starts at -off (off = ref, or 0 while ref = -inf),
+    // so the matrix core returns s = score - off and P = exp2(s).  A tile is
+    // taken as is unless some s exceeds thr (kTau, or -inf while ref = -inf);
+    // then the rare path moves ref to the new max, rescales O and l by
+    // exp2(ref_old - ref_new) and shifts s.
+    float ref[QB], thr[QB];
+    floatx4 negoff[QB];
+    floatx4 o[8][QB];
+    // row sums of P accumulate on the matrix core: an all-ones A operand makes
+    // every row of lsum[qb] the sum over keys of P for this lane's query
+    floatx4 lsum[QB];
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    ref[qb] = -INFINITY;
-    thr[qb] = -INFINITY;
-    negoff[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    lsum[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb) {
+      ref[qb] = -INFINITY;
+      thr[qb] = -INFINITY;
+      negoff[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      lsum[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+      for (int db = 0; db < 8; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 
-  // ---- operands and stages of one 32-key tile ----
-  bf16x8 kop[2][4];   // K operand of the next QK^T: [kb][kk]
-  bf16x8 vop[8];      // V^T operand of the next PV: [db]
-  // K rows 16kb + i, d = 8(4kk+g) .. +7
-  // lane offsets of the operand reads in a tile (rows 16 apart share a swizzle)
-  int kofs[4], vofs[8];
+    // ---- operands and stages of one 32-key tile ----
+    bf16x8 kop[2][4];   // K operand of the next QK^T: [kb][kk]
+    bf16x8 vop[8];      // V^T operand of the next PV: [db]
+    // K rows 16kb + i, d = 8(4kk+g) .. +7
+    // lane offsets of the operand reads in a tile (rows 16 apart share a swizzle)
+    int kofs[4], vofs[8];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kofs[kk] = i * ROWB + 16 * ((4 * kk + g) ^ kswz(i));
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const int r0 = 4 * g + (i >> 2);
-    vofs[db] = r0 * ROWB + 16 * ((2 * db + ((i & 3) >> 1)) ^ vswz(r0)) + 8 * (i & 1);
-  }
-  auto read_k = [&](int t) __attribute__((always_inline)) {
-    const uint8_t* Kb = smem + slot_off(t);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kop[kb][kk] = *reinterpret_cast<const bf16x8*>(Kb + kofs[kk] + 16 * kb * ROWB);
-  };
-  // Transposing reads: lane i of a 16-lane group addresses key base+i/4,
-  // d 16db+4(i%4), and receives V[base+e][16db+i] for e = 0..3 (base = 4g,
-  // then 16+4g), which is the A operand of O^T += V^T P^T.
-  auto read_v = [&](int t) __attribute__((always_inline)) {
-    lds_u8* Vb = (lds_u8*)smem + slot_off(t) + KTILEB;
+    for (int kk = 0; kk < 4; ++kk) kofs[kk] = i * ROWB + 16 * ((4 * kk + g) ^ kswz(i));
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db]));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db] + 16 * ROWB));
-      const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      vop[db] = __builtin_bit_cast(bf16x8, va);
+      const int r0 = 4 * g + (i >> 2);
+      vofs[db] = r0 * ROWB + 16 * ((2 * db + ((i & 3) >> 1)) ^ vswz(r0)) + 8 * (i & 1);
     }
-  };
-  // s[kb][qb] = K Q^T - off for heads q0, q0+1: rows = keys 16kb + 4g + r,
-  // column = query i.  Four independent accumulation chains.
-  auto qk_mma = [&](floatx4 (&s)[2][QB], int q0, int nq) __attribute__((always_inline)) {
+    auto read_k = [&](int t) __attribute__((always_inline)) {
+      const uint8_t* Kb = smem + slot_off(t);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = q0; qb < q0 + nq; ++qb)
-        s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][0], qf[qb][0], negoff[qb], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk)
+          kop[kb][kk] = *reinterpret_cast<const bf16x8*>(Kb + kofs[kk] + 16 * kb * ROWB);
+    };
+    // Transposing reads: lane i of a 16-lane group addresses key base+i/4,
+    // d 16db+4(i%4), and receives V[base+e][16db+i] for e = 0..3 (base = 4g,
+    // then 16+4g), which is the A operand of O^T += V^T P^T.
+    auto read_v = [&](int t) __attribute__((always_inline)) {
+      lds_u8* Vb = (lds_u8*)smem + slot_off(t) + KTILEB;
 #pragma unroll
-    for (int kk = 1; kk < 4; ++kk)
+      for (int db = 0; db < 8; ++db) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db] + 16 * ROWB));
+        const v8i16 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        vop[db] = __builtin_bit_cast(bf16x8, va);
+      }
+    };
+    // s[kb][qb] = K Q^T - off for heads q0, q0+1: rows = keys 16kb + 4g + r,
+    // column = query i.  Four independent accumulation chains.
+    auto qk_mma = [&](floatx4 (&s)[2][QB], int q0, int nq) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = q0; qb < q0 + nq; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][kk], qf[qb][kk], s[kb][qb], 0, 0, 0);
-  };
-  // O^T += V^T P^T and l += 1 P^T for head qb
-  auto pv_mma = [&](const bf16x8 (&p)[QB], int qb) __attribute__((always_inline)) {
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][0], qf[qb][0], negoff[qb], 0, 0, 0);
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], p[qb], o[db][qb], 0, 0, 0);
-    lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[qb], lsum[qb], 0, 0, 0);
-  };
-  // mask of tile j for this wave: 0 none, 1 band edge / diagonal, 2 sink tile.
-  // Band tile j (keys u0 .. u0+31, u0 = t0 + 32(m + j)) needs no mask when
-  // all its keys precede the wave's first query (u0 + 31 <= q0w), lie inside
-  // the window of its last query (u0 > q0w + 15 - W) and exist (s0 + u0 >=
-  // 0); each condition bounds j on one side, so the unmasked tiles are the
-  // range jlo <= j <= jhi (>> 5 is the floor division by 32).
-  const int mfull = kmin - n_stile, dq = q0w - t0;
-  const int jhi = ((dq - (BN - 1)) >> 5) - mfull;
-  const int jlo = max(max(n_stile, ((dq + 15 - W) >> 5) + 1 - mfull), -((s0 + t0) >> 5) - mfull);
-  auto mask_kind = [&](int j) __attribute__((always_inline)) {
-    if (j < n_stile) return 2;
-    return (j >= jlo && j <= jhi) ? 0 : 1;
-  };
-  auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
+      for (int kk = 1; kk < 4; ++kk)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr_ = 16 * kb + 4 * g + r;
-        bool ok;
-        if (mk == 2) {
-          const int P = BN * j + kr_;
-          ok = P < nsink && P <= I - W;
-        } else {
-          const int u = band_u0(j) + kr_;
-          ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
+          for (int qb = q0; qb < q0 + nq; ++qb)
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][kk], qf[qb][kk], s[kb][qb], 0, 0, 0);
+    };
+    // O^T += V^T P^T and l += 1 P^T for head qb
+    auto pv_mma = [&](const bf16x8 (&p)[QB], int qb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], p[qb], o[db][qb], 0, 0, 0);
+      lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[qb], lsum[qb], 0, 0, 0);
+    };
+    // mask of tile j for this wave: 0 none, 1 band edge / diagonal, 2 sink tile.
+    // Band tile j (keys u0 .. u0+31, u0 = t0 + 32(m + j)) needs no mask when
+    // all its keys precede the wave's first query (u0 + 31 <= q0w), lie inside
+    // the window of its last query (u0 > q0w + 15 - W) and exist (s0 + u0 >=
+    // 0); each condition bounds j on one side, so the unmasked tiles are the
+    // range jlo <= j <= jhi (>> 5 is the floor division by 32).
+    const int mfull = kmin - n_stile, dq = q0w - t0;
+    const int jhi = ((dq - (BN - 1)) >> 5) - mfull;
+    const int jlo = max(max(n_stile, ((dq + 15 - W) >> 5) + 1 - mfull), -((s0 + t0) >> 5) - mfull);
+    auto mask_kind = [&](int j) __attribute__((always_inline)) {
+      if (j < n_stile) return 2;
+      return (j >= jlo && j <= jhi) ? 0 : 1;
+    };
+    auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kr_ = 16 * kb + 4 * g + r;
+          bool ok;
+          if (mk == 2) {
+            const int P = BN * j + kr_;
+            ok = P < nsink && P <= I - W;
+          } else {
+            const int u = band_u0(j) + kr_;
+            ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
+          }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
         }
+    };
+    // P = exp2(s) of head qb, rounded to bf16 in the B-operand layout
+    auto sexp = [&](const floatx4 (&s)[2][QB], bf16x8 (&p)[QB], int qb) __attribute__((always_inline)) {
+      u32x4 pk;
+      pk[0] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][0]), __builtin_amdgcn_exp2f(s[0][qb][1]));
+      pk[1] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][2]), __builtin_amdgcn_exp2f(s[0][qb][3]));
+      pk[2] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][0]), __builtin_amdgcn_exp2f(s[1][qb][1]));
+      pk[3] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][2]), __builtin_amdgcn_exp2f(s[1][qb][3]));
+      p[qb] = __builtin_bit_cast(bf16x8, pk);
+    };
+    // whether some s of head qb in this lane exceeds its column's threshold
+    auto over = [&](const floatx4 (&s)[2][QB], int qb) __attribute__((always_inline)) {
+      const float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
+      return mx > thr[qb];
+    };
+    // the rare path: new references, rescaled O and l, shifted s
+    auto rebase = [&](floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
+      for (int qb = 0; qb < QB; ++qb) {
+        const float off = -negoff[qb][0];
+        const float cm = xg_max(__builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]))) + off;
+        const float nref = __builtin_elementwise_maximum(ref[qb], cm);
+        if (nref > ref[qb] + kTau || (ref[qb] == -INFINITY && nref > -INFINITY)) {
+          const float alpha = __builtin_amdgcn_exp2f(ref[qb] - nref);
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
+          ref[qb] = nref;
+        }
+        const float noff = ref[qb] == -INFINITY ? 0.f : ref[qb];
+        const float shift = noff - off;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb][qb] -= shift;
+        negoff[qb] = floatx4{-noff, -noff, -noff, -noff};
+        thr[qb] = ref[qb] == -INFINITY ? -INFINITY : kTau;
       }
-  };
-  // P = exp2(s) of head qb, rounded to bf16 in the B-operand layout
-  auto sexp = [&](const floatx4 (&s)[2][QB], bf16x8 (&p)[QB], int qb) __attribute__((always_inline)) {
-    u32x4 pk;
-    pk[0] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][0]), __builtin_amdgcn_exp2f(s[0][qb][1]));
-    pk[1] = pack_bf16(__builtin_amdgcn_exp2f(s[0][qb][2]), __builtin_amdgcn_exp2f(s[0][qb][3]));
-    pk[2] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][0]), __builtin_amdgcn_exp2f(s[1][qb][1]));
-    pk[3] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][2]), __builtin_amdgcn_exp2f(s[1][qb][3]));
-    p[qb] = __builtin_bit_cast(bf16x8, pk);
-  };
-  // whether some s of head qb in this lane exceeds its column's threshold
-  auto over = [&](const floatx4 (&s)[2][QB], int qb) __attribute__((always_inline)) {
-    const float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
-    return mx > thr[qb];
-  };
-  // the rare path: new references, rescaled O and l, shifted s
-  auto rebase = [&](floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float off = -negoff[qb][0];
-      const float cm = xg_max(__builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]))) + off;
-      const float nref = __builtin_elementwise_maximum(ref[qb], cm);
-      if (nref > ref[qb] + kTau || (ref[qb] == -INFINITY && nref > -INFINITY)) {
-        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - nref);
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
-        ref[qb] = nref;
-      }
-      const float noff = ref[qb] == -INFINITY ? 0.f : ref[qb];
-      const float shift = noff - off;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb][qb] -= shift;
-      negoff[qb] = floatx4{-noff, -noff, -noff, -noff};
-      thr[qb] = ref[qb] == -INFINITY ? -INFINITY : kTau;
-    }
-  };
+    };
 
-  // ---- software pipeline over tiles: two phases per tile ----
-  // Matrix phase j: QK(j) (S of tile j, seeded with -off), then PV(j-1)
-  // head by head, with K(j+1) and V(j) read from LDS into the operand
-  // registers as the products release them.
-  // Vector phase j: the mask and threshold checks of S(j), the rare rescale,
-  // P(j) = exp2(S(j)), and the direct loads of tile j+4.  A barrier ends
-  // every phase.  Waves 4..7 run one phase behind waves 0..3, so the two
-  // waves of each SIMD (w and w+4) are always in different phases: one feeds
-  // the matrix core and the LDS while the other uses the vector ALU.
-  // Ring timing (phases counted from the first matrix phase of waves 0..3:
-  // matrix phase j is phase 2j for those, 2j+1 for waves 4..7).  Every
-  // barrier waits for all but the newest tile load of the wave, so tile t,
-  // loaded in phases 2t-7 and 2t-6, is complete at the barrier ending phase
-  // 2t-4 and visible before its first read (K(t) in phase 2t-2).  Its last
-  // read (V(t), phase 2t+1) completes before the barrier ending the vector
-  // phase that follows (lgkmcnt(0)), and the loads of tile t+8 into its slot
-  // start in phase 2t+9.  Loads past the band read whatever the buffers hold
-  // there (or zeros) and are never used.
-  floatx4 s[2][QB];
-  bf16x8 p[QB];
-  auto mphase = [&](int j, bool qk, bool pv) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (qk) qk_mma(s, 0, QB);
-    __builtin_amdgcn_sched_barrier(0);
-    if (pv) {
-      pv_mma(p, 0);
-      if (qk) read_k(j + 1);
+    // ---- software pipeline over tiles: two phases per tile ----
+    // Matrix phase j: QK(j) (S of tile j, seeded with -off), then PV(j-1)
+    // head by head, with K(j+1) and V(j) read from LDS into the operand
+    // registers as the products release them.
+    // Vector phase j: the mask and threshold checks of S(j), the rare rescale,
+    // P(j) = exp2(S(j)), and the direct loads of tile j+4.  A barrier ends
+    // every phase.  Waves 4..7 run one phase behind waves 0..3, so the two
+    // waves of each SIMD (w and w+4) are always in different phases: one feeds
+    // the matrix core and the LDS while the other uses the vector ALU.
+    // Ring timing (phases counted from the first matrix phase of waves 0..3:
+    // matrix phase j is phase 2j for those, 2j+1 for waves 4..7).  Every
+    // barrier waits for all but the newest tile load of the wave, so tile t,
+    // loaded in phases 2t-7 and 2t-6, is complete at the barrier ending phase
+    // 2t-4 and visible before its first read (K(t) in phase 2t-2).  Its last
+    // read (V(t), phase 2t+1) completes before the barrier ending the vector
+    // phase that follows (lgkmcnt(0)), and the loads of tile t+8 into its slot
+    // start in phase 2t+9.  Loads past the band read whatever the buffers hold
+    // there (or zeros) and are never used.
+    floatx4 s[2][QB];
+    bf16x8 p[QB];
+    auto mphase = [&](int j, bool qk, bool pv) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (qk) qk_mma(s, 0, QB);
+      __builtin_amdgcn_sched_barrier(0);
+      if (pv) {
+        pv_mma(p, 0);
+        if (qk) read_k(j + 1);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pv_mma(p, 1);
+        if (qk) read_v(j);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      } else {
+        read_k(j + 1);
+        read_v(j);
       }
       __builtin_amdgcn_sched_barrier(0);
-      pv_mma(p, 1);
-      if (qk) read_v(j);
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto vphase = [&](int j) __attribute__((always_inline)) {
+      const int mk = mask_kind(j);
+      if (mk) apply_mask(j, mk, s);
+      bool rare = false;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int qb = 0; qb < QB; ++qb) rare |= over(s, qb);
+      if (__builtin_expect(__any(rare), 0)) rebase(s);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sexp(s, p, qb);
+      // the empty asm keeps the exponentials in this phase
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(p[qb]));
+      __builtin_amdgcn_sched_barrier(0);
+      dma_tile(j + 4);
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const bool lead = (w >> 2) == 0;
+    __syncthreads();
+    if (n_tiles > 0) {
+      read_k(0);
+      if (!lead) __builtin_amdgcn_s_barrier();
+      mphase(0, true, false);
+      vphase(0);
+      for (int j = 1; j < n_tiles; ++j) {
+        mphase(j, true, true);
+        vphase(j);
       }
-    } else {
-      read_k(j + 1);
-      read_v(j);
+      mphase(n_tiles, false, true);
+      if (lead) __builtin_amdgcn_s_barrier();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto vphase = [&](int j) __attribute__((always_inline)) {
-    const int mk = mask_kind(j);
-    if (mk) apply_mask(j, mk, s);
-    bool rare = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) rare |= over(s, qb);
-    if (__builtin_expect(__any(rare), 0)) rebase(s);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sexp(s, p, qb);
-    // the empty asm keeps the exponentials in this phase
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(p[qb]));
-    __builtin_amdgcn_sched_barrier(0);
-    dma_tile(j + 4);
-    ring_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  const bool lead = (w >> 2) == 0;
-  __syncthreads();
-  if (n_tiles > 0) {
-    read_k(0);
-    if (!lead) __builtin_amdgcn_s_barrier();
-    mphase(0, true, false);
-    vphase(0);
-    for (int j = 1; j < n_tiles; ++j) {
-      mphase(j, true, true);
-      vphase(j);
-    }
-    mphase(n_tiles, false, true);
-    if (lead) __builtin_amdgcn_s_barrier();
-  }
-  // the last tile loads must land before the work-group's LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the last tile loads must land before the work-group's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: O / l, LSE ----
+    // ---- epilogue: O / l, LSE ----
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lsum[qb][0];
-    const float inv = 1.f / lt;
-    if (tq < C) {
-      uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = lsum[qb][0];
+      const float inv = 1.f / lt;
+      if (tq < C) {
+        uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        u32x2 val = {pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv),
-                     pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
-        *reinterpret_cast<u32x2*>(dst + 16 * db + 4 * g) = val;
+        for (int db = 0; db < 8; ++db) {
+          u32x2 val = {pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv),
+                       pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
+          *reinterpret_cast<u32x2*>(dst + 16 * db + 4 * g) = val;
+        }
+        if (a.lse && g == 0)
+          a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lt)) * 0.69314718055994531f;
       }
-      if (a.lse && g == 0)
-        a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lt)) * 0.69314718055994531f;
     }
-  }
+  }  // items
 }
 
 // ---------------------------------------------------------------------------
@@ -696,6 +718,17 @@ __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab r
 
 }  // namespace
 
+// Number of compute units of the current device (0 if unknown), cached per device.
+static int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
@@ -713,7 +746,12 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.n_qtiles = (C + BM - 1) / BM;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  const long long nwg = (long long)a.n_qtiles * sh.Hkv * sh.B;
+  const long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B;
+  if (n_items > INT32_MAX) return hipErrorInvalidValue;
+  a.n_items = (int)n_items;
+  // one work-group per CU (a multiple of 8), each looping over its items
+  const long long ncu = (long long)(device_cu_count() & ~7);
+  const long long nwg = (ncu >= 8 && n_items > ncu) ? ncu : n_items;
   prefill_bf16_d128_g4_kernel<<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   return hipGetLastError();
 }
