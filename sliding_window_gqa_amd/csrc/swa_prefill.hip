@@ -310,15 +310,17 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
     const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
     const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
+    const int vrk = rdma * (int)rowbytes + dk;          // lane offsets within a chunk tile
+    const int vrv = rdma * (int)rowbytes + dv;
     const unsigned lds_base = __builtin_amdgcn_readfirstlane(
         (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
     auto dma_tile = [&](int t) __attribute__((always_inline)) {
       const int u0 = band_u0(t);
       const unsigned lk = lds_base + (unsigned)(t % NBUF) * RINGB;
       if (u0 >= 0) {
-        const int row = (u0 + rdma) * (int)rowbytes;
-        dma16(rkc, row + dk, lk);
-        dma16(rvc, row + dv, lk + KTILEB);
+        const int srow = u0 * (int)rowbytes;   // uniform part of the offsets
+        dma16(rkc, srow + vrk, lk);
+        dma16(rvc, srow + vrv, lk + KTILEB);
       } else {
         const int P = max(s0 + u0 + rdma, 0);
         const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;

@@ -7,9 +7,16 @@
 // rotated keys and values verbatim.
 //
 // One thread moves 8 consecutive elements (one 16-byte bf16 chunk, or two
-// 16-byte float chunks) of one (token, kv-head) row.  Only positions that
-// survive the call are written: a rolling position p is overwritten inside the
-// same call iff p + W <= last position, so each slot has exactly one writer.
+// 16-byte float chunks) of one (token, kv-head) row.  A block covers whole
+// tokens of one sequence (blockIdx.y): thread x handles chunk x mod cpt of
+// token x / cpt of the block's run of 256 / cpt tokens (cpt = chunks per
+// token), or loops over the chunks of one token when cpt > 256, so the index
+// arithmetic stays in 32 bits with one division per thread.  Only positions
+// that survive the call are written: a rolling position p is overwritten
+// inside the same call iff p + W <= last position, so each slot has exactly
+// one writer.
+#include <climits>
+
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
 
@@ -21,71 +28,65 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
                                                          const void* __restrict__ v,
                                                          const int32_t* __restrict__ start, int n_tok,
                                                          void* __restrict__ kdst, void* __restrict__ vdst,
-                                                         int mode, long long total_chunks) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= total_chunks) return;
-  const int cpr = sh.D / 8;  // chunks per row
-  const int c = (int)(gid % cpr);
-  const long long row = gid / cpr;
-  const int h = (int)(row % sh.Hkv);
-  const long long bt = row / sh.Hkv;
-  const int t = (int)(bt % n_tok);
-  const int b = (int)(bt / n_tok);
-
+                                                         int mode, int tok_per_block) {
+  const int cpr = sh.D / 8;           // chunks per (token, head) row: 8 or 16
+  const int cpt = sh.Hkv * cpr;       // chunks per token
+  const int b = blockIdx.y;
   const int s0 = start[b];
+  const int last = s0 + n_tok - 1;
+  const int tb = (int)threadIdx.x / cpt;  // token of this thread within the block's run
+  const int t = blockIdx.x * tok_per_block + tb;
+  if (tb >= tok_per_block || t >= n_tok) return;
   const int p = s0 + t;
-  long long dst_row;
-  if (mode == kToCache) {
-    const int last = s0 + n_tok - 1;
-    if (p >= sh.n_sink && p + sh.W <= last) return;  // overwritten later in this call
-    const int slot = slot_of(p, sh.W, sh.n_sink);
-    dst_row = ((long long)b * sh.S + slot) * sh.Hkv + h;
-  } else {
-    dst_row = row;
-  }
-  const long long src_off = row * sh.D + 8 * c;
-  const long long dst_off = dst_row * sh.D + 8 * c;
+  if (mode == kToCache && p >= sh.n_sink && p + sh.W <= last) return;  // overwritten later in this call
+  const long long row0 = (long long)b * n_tok + t;                      // source token row
+  const long long drow0 = mode == kToCache ? (long long)b * sh.S + slot_of(p, sh.W, sh.n_sink) : row0;
+  for (int ct = (int)threadIdx.x - tb * cpt; ct < cpt; ct += (int)blockDim.x) {
+    const int h = ct / cpr, c = ct - h * cpr;
+    const long long src_off = (row0 * sh.Hkv + h) * sh.D + 8 * c;
+    const long long dst_off = (drow0 * sh.Hkv + h) * sh.D + 8 * c;
 
-  float x[8];
-  if (F32) {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(k) + src_off);
-    const float4 a = src[0], bb = src[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = bb.x; x[5] = bb.y; x[6] = bb.z; x[7] = bb.w;
-  } else {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(k) + src_off);
+    float x[8];
+    if (F32) {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(k) + src_off);
+      const float4 a = src[0], bb = src[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = bb.x; x[5] = bb.y; x[6] = bb.z; x[7] = bb.w;
+    } else {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(k) + src_off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = bf16_lo(w[j]);
-      x[2 * j + 1] = bf16_hi(w[j]);
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_lo(w[j]);
+        x[2 * j + 1] = bf16_hi(w[j]);
+      }
     }
-  }
-  if (sh.rope) {
+    if (sh.rope) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float cs, sn;
-      rope_cs(p, rt.rev[4 * c + j], cs, sn);
-      rotate(x[2 * j], x[2 * j + 1], cs, sn);
+      for (int j = 0; j < 4; ++j) {
+        float cs, sn;
+        rope_cs(p, rt.rev[4 * c + j], cs, sn);
+        rotate(x[2 * j], x[2 * j + 1], cs, sn);
+      }
     }
-  }
-  if (F32) {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(kdst) + dst_off);
-    dst[0] = make_float4(x[0], x[1], x[2], x[3]);
-    dst[1] = make_float4(x[4], x[5], x[6], x[7]);
-    if (mode == kToCache) {
-      const float4* vs = reinterpret_cast<const float4*>(static_cast<const float*>(v) + src_off);
-      float4* vd = reinterpret_cast<float4*>(static_cast<float*>(vdst) + dst_off);
-      vd[0] = vs[0];
-      vd[1] = vs[1];
-    }
-  } else {
-    u32x4 w;
+    if (F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(kdst) + dst_off);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+      if (mode == kToCache) {
+        const float4* vs = reinterpret_cast<const float4*>(static_cast<const float*>(v) + src_off);
+        float4* vd = reinterpret_cast<float4*>(static_cast<float*>(vdst) + dst_off);
+        vd[0] = vs[0];
+        vd[1] = vs[1];
+      }
+    } else {
+      u32x4 w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = pack_bf16(x[2 * j], x[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + dst_off) = w;
-    if (mode == kToCache) {
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(vdst) + dst_off) =
-          *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + src_off);
+      for (int j = 0; j < 4; ++j) w[j] = pack_bf16(x[2 * j], x[2 * j + 1]);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + dst_off) = w;
+      if (mode == kToCache) {
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(vdst) + dst_off) =
+            *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + src_off);
+      }
     }
   }
 }
@@ -95,15 +96,18 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
 hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
                               const void* v, const int32_t* start, int n_tok, void* kdst,
                               void* vdst, WriteMode mode, hipStream_t st) {
-  const long long total = (long long)sh.B * n_tok * sh.Hkv * (sh.D / 8);
   const int threads = 256;
-  const long long blocks = (total + threads - 1) / threads;
+  const int cpt = sh.Hkv * (sh.D / 8);
+  const int tok_per_block = cpt <= threads ? threads / cpt : 1;
+  const long long bx = ((long long)n_tok + tok_per_block - 1) / tok_per_block;
+  if (bx > INT32_MAX || sh.B > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)bx, (unsigned)sh.B);
   if (f32)
-    cache_write_kernel<true><<<dim3((unsigned)blocks), dim3(threads), 0, st>>>(
-        sh, rt, k, v, start, n_tok, kdst, vdst, (int)mode, total);
+    cache_write_kernel<true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
+                                                             (int)mode, tok_per_block);
   else
-    cache_write_kernel<false><<<dim3((unsigned)blocks), dim3(threads), 0, st>>>(
-        sh, rt, k, v, start, n_tok, kdst, vdst, (int)mode, total);
+    cache_write_kernel<false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
+                                                              (int)mode, tok_per_block);
   return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ PREFILL_CASES = [
     (1, 4, 1, 128, 64, 0, torch.bfloat16, [200, 64, 65]),
     (1, 4, 1, 128, 1, 0, torch.bfloat16, [70, 5]),
     (2, 4, 1, 128, 300, 2, torch.bfloat16, [500, 77]),
+    # more (sequence, KV head, query tile) items than CUs: work-groups loop
+    # over several items (288 and 272 items in the first and second chunk)
+    (2, 32, 8, 128, 300, 0, torch.bfloat16, [1100, 1030]),
+    (2, 32, 8, 128, 300, 4, torch.bfloat16, [1100, 1030]),
     # generic path
     (2, 4, 2, 64, 100, 0, torch.bfloat16, [130, 1, 70]),
     (1, 6, 2, 128, 50, 3, torch.float32, [90, 7, 40]),
