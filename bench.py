@@ -371,6 +371,28 @@ def context_timings(swa, synth, torch, dev):
     ms_flushed = run5(True)
     ms_warm = run5(False)
     bytes5 = B * S * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2
+    # sink workload's prefill chunk: one 4096-token chunk per sequence after
+    # the decode steps, against the rolling cache with its 4 sink slots
+    C5 = wl5.chunk
+    st5 = pos[T - 1] + 1
+    q5c = torch.randn((B, C5, Hq, D), generator=g, device=dev).to(bf)
+    k5c = torch.randn((B, C5, Hkv, D), generator=g, device=dev).to(bf)
+    v5c = torch.randn((B, C5, Hkv, D), generator=g, device=dev).to(bf)
+    o5c = torch.empty((B, C5, Hq, D), dtype=bf, device=dev)
+    l5c = torch.empty((B, Hq, C5), dtype=torch.float32, device=dev)
+    ws5c = torch.empty(swa.swa_prefill_workspace_bytes(p5, C5), dtype=torch.uint8, device=dev)
+
+    def chunk5():
+        swa.swa_prefill_chunk(p5, q5c, k5c, v5c, kc5, vc5, st5, o5c, l5c, ws5c)
+
+    chunk_ms = timeit(chunk5)
+    chunk_pairs = sum(band_pairs(C5, wl5.window, int(x), wl5.n_sink) for x in st5.cpu().tolist())
+    ctx["sink_chunk_prefill"] = {
+        "workload": wl5.name, "batch": B, "chunk": C5, "ms": round(chunk_ms, 4),
+        "flops": attn_flops(chunk_pairs),
+        "tflops": round(attn_flops(chunk_pairs) / (chunk_ms * 1e-3) / 1e12, 1),
+        "step": "prefill_chunk (key rotation + attention over cache and chunk)",
+    }
     ctx["sink_decode"] = {
         "workload": wl5.name, "bytes_per_step": bytes5,
         "ms_per_decode_mall_flushed": round(ms_flushed, 4),
