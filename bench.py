@@ -165,7 +165,8 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         ms_step = t0.elapsed_time(t1) / args.steps
-        attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        attn_times = sorted(a.elapsed_time(b) for a, b in evs)
+        attn_ms = sum(attn_times) / args.steps
         achieved = flops2 / (attn_ms * 1e-3) / 1e12
         result.update({
             "value": round(flops2 / (ms_step * 1e-3) / 1e12, 2),
@@ -185,6 +186,8 @@ def main():
                                                      ["swa_prefill.hip", "swa_device.hpp"]),
                          "algorithmic_bytes": N * Hq * D * 2 * 2 + 2 * N * Hkv * D * 2 + Hq * N * 4,
                          "avg_kernel_ms": round(attn_ms, 4),
+                         "median_kernel_ms": round(attn_times[len(attn_times) // 2], 4),
+                         "min_kernel_ms": round(attn_times[0], 4),
                          "timing": "HIP events around each attention launch in the timed region"},
             "wall_s_timed_region": round(wall, 4),
         })
@@ -235,7 +238,8 @@ def main():
         t1.record()
         torch.cuda.synchronize()
         total_ms = t0.elapsed_time(t1)
-        dec_ms = sum(a.elapsed_time(b) for a, b in evs)
+        dec_times = sorted(a.elapsed_time(b) for a, b in evs)
+        dec_ms = sum(dec_times)
         dec_achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
         result["decode"] = {
             "workload": wl4.name, "batch": B4, "steps": T, "window": wl4.window,
@@ -250,6 +254,7 @@ def main():
                                                      ["swa_decode.hip", "swa_device.hpp"]),
                          "algorithmic_bytes": round(dec_bytes / T),
                          "avg_call_ms": round(dec_ms / T, 4),
+                         "median_call_ms": round(dec_times[len(dec_times) // 2], 4),
                          "bytes": "valid K/V slots read once + Q + O"},
         }
         del kc4, vc4, qs, ks, vs
@@ -266,7 +271,8 @@ def main():
     if not args.no_cpu_baseline and args.only in ("prefill", "all"):
         result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), W, wl.rope_theta, args.cpu_seconds)
 
-    result["host"] = {"cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
+    result["host"] = {"cpu": cpu_model(), "os_cpu_count": os.cpu_count(),
+                      "affinity_cpus": len(os.sched_getaffinity(0))}
     print(json.dumps(result), flush=True)
 
 
@@ -404,6 +410,17 @@ def context_timings(swa, synth, torch, dev):
     return ctx
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(q, k, v, W, theta, target_s):
     """The fp64 oracle, untuned, on a bounded sample of query rows of the
     prefill workload; reported as algorithmic TFLOP/s on the host cores."""
@@ -438,7 +455,8 @@ def cpu_baseline(q, k, v, W, theta, target_s):
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads or os.cpu_count(),
             "kind": "oracle",
             "sample": f"{done} of {N} query rows (random) of the n8192 w4096 prefill, fp64 NumPy, {el:.1f} s",
-            "seconds": round(el, 2), "affinity_cpus": len(os.sched_getaffinity(0))}
+            "seconds": round(el, 2), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads": blas_threads, "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":
