@@ -59,6 +59,13 @@ bool fast_path(const swa_params* p) {
          seq_cache_bytes < (1LL << 31);
 }
 
+// The fast prefill kernel also addresses one sequence's chunk (Q, K, V, and
+// a few tiles past its end) with 32-bit byte offsets.
+bool fast_prefill(const swa_params* p, int32_t chunk_len) {
+  const long long seq_q_bytes = (long long)(chunk_len + 256) * p->n_q_heads * p->head_dim * 2;
+  return fast_path(p) && seq_q_bytes < (1LL << 31);
+}
+
 int launched(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
 
 }  // namespace
@@ -109,7 +116,7 @@ int swa_prefill_attention(const swa_params* params, const void* q, const void* k
   if (chunk_len < 1 || chunk_len > (1 << 24)) return SWA_ERR_SHAPE;
   const RopeTab rt = rope_table(params);
   hipError_t e;
-  if (fast_path(params))
+  if (fast_prefill(params, chunk_len))
     e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, k_rot, v, k_cache, v_cache, start_pos,
                                          chunk_len, out, lse, stream);
   else

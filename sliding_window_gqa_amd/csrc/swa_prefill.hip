@@ -19,11 +19,13 @@
 //    (masks, threshold checks, exponentials, tile loads).  The two waves of
 //    a SIMD run one phase apart, so one feeds the matrix core while the
 //    other works on the vector ALU.
-//  * Key tiles of 32 keys in an 8-slot LDS ring.  Tiles outside the band
+//  * Key tiles of 32 keys in a 5-slot LDS ring.  Tiles outside the band
 //    i-W < j <= i of the work-group are never visited, so the work is
 //    O(N*W); only tiles that cut the diagonal or the window edge are
 //    masked.  Tiles move global -> LDS directly (buffer loads with the lds
-//    modifier, out-of-range rows read as zeros) four tiles ahead.
+//    modifier, out-of-range rows read as zeros) four tiles ahead, as one
+//    stream over all the items a work-group runs; the next item's query rows
+//    wait in an LDS stage, so an item starts without waiting for memory.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: in the
 //    transposed form every lane owns one query column, so the softmax column
 //    statistics stay in one lane plus a 4-lane exchange (permlane swaps), and
@@ -40,7 +42,8 @@
 //    carry the same reference, so the result is the same.
 //  * Work-groups are renumbered so that the 8 XCDs each take a contiguous
 //    range of (sequence, KV head, query tile): the K/V of one KV head then
-//    stays in one XCD's L2.  Query tiles run longest-first.
+//    stays in one XCD's L2.  Query tiles run longest-first; with more items
+//    than CUs, one work-group per CU loops over its items.
 //
 // Generic kernel: float32 or bf16, head_dim 64 or 128, any group size; one
 // thread per query row, scalar loops.  Used for shapes the fast kernel does
@@ -63,7 +66,7 @@ constexpr int HD = 128;      // head_dim of the fast kernel
 constexpr int NTHR = 512;    // 8 waves, two per SIMD
 constexpr int QB = 2;        // query heads per wave
 constexpr float kTau = 8.0f; // lazy-rescale threshold (log2 units)
-constexpr int NBUF = 8;      // LDS ring of K/V tiles
+constexpr int NBUF = 5;      // LDS ring of K/V tiles (the least the ring timing allows)
 static_assert(BN == 32, "the tile arithmetic below divides by 32 with >> 5");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -80,30 +83,16 @@ constexpr int ROWB = HD * 2;
 constexpr int KTILEB = BN * ROWB;
 constexpr int VTILEB = BN * ROWB;
 constexpr int RINGB = KTILEB + VTILEB;   // one K+V tile in the ring
+constexpr int QROWB = 4 * ROWB;          // the 4 query heads of one position
 __device__ inline int kswz(int r) { return r & 15; }
 __device__ inline int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-// Work-group barrier for the tile ring.  __syncthreads() carries a release
-// fence that makes the compiler wait for every outstanding vector-memory
-// operation (including prefetched tiles) before s_barrier; here only the
-// wave's own LDS operations are awaited, and the asm clobbers keep the
-// compiler from moving LDS accesses across the barrier.
-__device__ inline void ring_barrier() {
-  // vmcnt(2): of the direct-to-LDS tile loads only the two of the newest
-  // tile may still be in flight.  lgkmcnt(0) goes through the builtin so
-  // that the compiler knows the LDS reads are complete and adds no waits of
-  // its own after the barrier.
-  asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // One direct global-to-LDS load: every lane's 16 bytes at byte offset `off`
 // of the buffer `rsrc` (zeros when out of range) land at LDS address
 // lds + 16 * lane.  M0 carries the LDS address; it is saved and restored
 // around the load, and one wait state separates its write from the load.
-// The compiler does not count these loads: ring_barrier() waits for them.
+// The compiler does not count these loads: the barriers of the tile loop
+// wait for them (s_waitcnt vmcnt) explicitly.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, int off, unsigned lds) {
   unsigned saved;
   asm volatile(
@@ -114,6 +103,25 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, int off, unsigned lds)
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds), "v"(off), "s"(rsrc)
+      : "memory");
+}
+
+// The K and the V row of one tile: as dma16, twice, with one save and
+// restore of M0.
+__device__ inline void dma16x2(__amdgpu_buffer_rsrc_t rk, int ok, unsigned lk,
+                               __amdgpu_buffer_rsrc_t rv, int ov, unsigned lv) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %5, %6, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lk), "v"(ok), "s"(rk), "s"(lv), "v"(ov), "s"(rv)
       : "memory");
 }
 
@@ -160,15 +168,31 @@ struct PrefillArgs {
 // h0, h0+1 (h0 = 4 kvh + 2(w>>2)); lane (i, g) owns query column i of each
 // of its heads.  Every K/V operand read from LDS feeds two matrix
 // instructions (one per head).
+//
+// A work-group runs several items (sequence, KV head, query tile) one after
+// the other.  The tile loads run ahead of the computation as one stream over
+// all of the work-group's items: the last steps of an item already load the
+// first tiles of the next one into the ring, and the next item's query rows
+// go to an LDS stage while the current item runs, so that an item starts
+// without waiting for memory.
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
+  __shared__ __attribute__((aligned(16))) uint8_t qstage[BM * QROWB];
   __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
   const int tid = threadIdx.x;
   if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
-  __syncthreads();
+
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, i = lane & 15, g = lane >> 4;
+  const int C = a.C;
+  const int W = sh.W;
+  const int S = sh.S;
+  const int nsink = sh.n_sink;
+  const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;   // bytes between tokens of K/V
+  const unsigned qrowbytes = (unsigned)sh.Hq * 2u * HD;   // bytes between tokens of Q
 
   // ---- work mapping ----
   // Items (sequence, KV head, query tile) are numbered sequence-major, KV
@@ -178,198 +202,225 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // hardware hands them out in that order; with fewer work-groups (one per
   // CU, a multiple of 8) each takes the items of its XCD's range in a
   // serpentine order over the rounds, which evens out the longest-first
-  // lengths.
+  // lengths.  item_at(r) is the item of round r, or -1 past the last.
   const int G = gridDim.x;
   const int wg = blockIdx.x;
   const int xcd = wg & 7;
-  for (int round = 0;; ++round) {
-    int L;
+  auto item_at = [&](int round) __attribute__((always_inline)) {
+    int L = -1;
     if (G >= a.n_items) {
-      if (round > 0) break;
       const int q8 = G >> 3, r8 = G & 7;
-      L = xcd * q8 + min(xcd, r8) + (wg >> 3);
+      if (round == 0) L = xcd * q8 + min(xcd, r8) + (wg >> 3);
     } else {
       const int q8 = a.n_items >> 3, r8 = a.n_items & 7;
       const int lo = xcd * q8 + min(xcd, r8), cnt = q8 + (xcd < r8 ? 1 : 0);
       const int nl = G >> 3, li = wg >> 3;
       const int pos = round * nl + ((round & 1) ? nl - 1 - li : li);
-      if (pos >= cnt) break;
-      L = lo + pos;
+      if (pos < cnt) L = lo + pos;
     }
+    return L;
+  };
+  // An item's tiles: [sink tiles] + band tiles k = kmin..1 (keys u0 .. u0+31,
+  // u0 = t0 + 32k).  Band tiles cover chunk-relative key positions
+  // t0 - W + 1 .. t0 + 63; sink tiles cover absolute positions 0 ..
+  // n_sink-1 for queries whose window no longer contains them.
+  struct Item {
+    int b, kvh, t0, s0, n_stile, kmin, n_tiles;
+  };
+  // The start positions are read through the constant address space, so
+  // that they come in with scalar loads, which the wait for the tile loads
+  // (vector memory) does not cover.
+  typedef __attribute__((address_space(4))) const int32_t c_i32;
+  c_i32* start_c = (c_i32*)a.start;
+  auto item_params = [&](int L) __attribute__((always_inline)) {
+    Item it;
     const int per_b = sh.Hkv * a.n_qtiles;
-    const int b = L / per_b;
-    const int rem = L - b * per_b;
-    const int kvh = rem / a.n_qtiles;
-    const int qt = a.n_qtiles - 1 - (rem - kvh * a.n_qtiles);
+    it.b = L / per_b;
+    const int rem = L - it.b * per_b;
+    it.kvh = rem / a.n_qtiles;
+    it.t0 = (a.n_qtiles - 1 - (rem - it.kvh * a.n_qtiles)) * BM;
+    it.s0 = start_c[it.b];
+    const int tq_last = min(it.t0 + BM, C) - 1;
+    it.n_stile = (nsink > 0 && (it.s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
+    const int k_lo = -((W - 1 + BN - 1) / BN);
+    const int k_clip = -((it.s0 + it.t0 + BN - 1) / BN);
+    it.kmin = max(k_lo, k_clip);
+    it.n_tiles = it.n_stile + (2 - it.kmin);
+    return it;
+  };
 
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, i = lane & 15, g = lane >> 4;
-    const int s0 = a.start[b];
-    const int C = a.C;
-    const int t0 = qt * BM;
+  // ---- the load stream: tiles global -> LDS ring, directly ----
+  // Wave w fills rows 4w .. 4w+3 of the K and of the V tile: lane L loads the
+  // chunk that belongs at position L%16 of row 4w + L/16 under the swizzle.
+  // The descriptors (chunk or cache of the item being loaded) cover exactly
+  // one KV head's rows of that tensor, so rows past its end read as zeros;
+  // cache rows take the slot map, and rows before position 0 read slot 0
+  // (they are masked).
+  const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
+  const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
+  const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
+  const int vrk = rdma * (int)rowbytes + dk;          // lane offsets within a chunk tile
+  const int vrv = rdma * (int)rowbytes + dv;
+  const unsigned lds_ring = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
+  const unsigned lds_q = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)qstage));
+  const int nrec_c = (C - 1) * (int)rowbytes + HD * 2;
+  const int nrec_s = a.kc ? (S - 1) * (int)rowbytes + HD * 2 : 0;
+  const int nrec_q = (C - 1) * (int)qrowbytes + QROWB;
+
+  // Cursor of the load stream: the item of round lr_round, its tile lt
+  // (tiles past an item's end, once no item follows, load unused rows), and
+  // the number of tiles loaded so far (the ring position of the next one).
+  // Of the item only what the loads need is kept; the descriptors are made
+  // at each load from the element offsets of its (sequence, KV head) rows.
+  int lr_round = 0, lt = 0;
+  unsigned lslot = 0;           // LDS offset of the ring slot the next load fills
+  int l_nt, l_ns, l_u0, l_s0;   // tiles, sink tiles, u0 of the first band tile, start
+  long long l_ec, l_es;         // element offset of the rows in the chunk, the cache
+  __amdgpu_buffer_rsrc_t rkc, rvc;   // the item's rows of the chunk's K and V
+  auto rsrc = [&](const uint16_t* base, long long e, int nrec) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base + e), (short)0, nrec, 0x00020000);
+  };
+  auto set_cursor = [&](int L) __attribute__((always_inline)) {
+    const Item it = item_params(L);
+    l_nt = it.n_tiles;
+    l_ns = it.n_stile;
+    l_u0 = it.t0 + BN * (it.kmin - it.n_stile);
+    l_s0 = it.s0;
+    l_ec = ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
+    l_es = ((long long)it.b * S * sh.Hkv + it.kvh) * HD;
+    rkc = rsrc(a.kr, l_ec, nrec_c);
+    rvc = rsrc(a.v, l_ec, nrec_c);
+  };
+  set_cursor(item_at(0));
+  // The next load is prepared one step ahead (prepare(), run while the
+  // previous loads are awaited) and issued by issue(): band tiles of the
+  // chunk, the common case, take the straight path with the uniform part of
+  // their offsets (l_srow) ready.
+  int l_slow = -1;       // >= 0 iff the next tile is a band tile of the chunk
+  int l_srow = 0;        // its uniform byte offset
+  auto prepare = [&]() __attribute__((always_inline)) {
+    if (lt >= l_nt) {
+      const int L = item_at(lr_round + 1);
+      if (L >= 0) {
+        ++lr_round;
+        set_cursor(L);
+        lt = 0;
+      }
+    }
+    const int u0 = l_u0 + BN * lt;
+    l_slow = (lt - l_ns) | u0;
+    l_srow = u0 * (int)rowbytes;
+    asm volatile("" : "+s"(l_slow), "+s"(l_srow));   // (computed here, in the wait's shadow)
+  };
+  // load the prepared tile into its ring slot
+  auto issue = [&]() __attribute__((always_inline)) {
+    const unsigned lk = lds_ring + lslot;
+    if (__builtin_expect(l_slow >= 0, 1)) {
+      dma16x2(rkc, l_srow + vrk, lk, rvc, l_srow + vrv, lk + KTILEB);
+    } else if (lt < l_ns) {
+      // sink tile: absolute positions 32 lt + r (clamped to the last sink);
+      // those before the item's chunk come from the cache, the rest from
+      // the chunk
+      const int P = min(BN * lt + rdma, nsink - 1);
+      if (P < l_s0 && a.kc != nullptr) {
+        dma16(rsrc(a.kc, l_es, nrec_s), P * (int)rowbytes + dk, lk);
+        dma16(rsrc(a.vc, l_es, nrec_s), P * (int)rowbytes + dv, lk + KTILEB);
+      } else {
+        const int r = min(max(P - l_s0, 0), C - 1) * (int)rowbytes;
+        dma16(rkc, r + dk, lk);
+        dma16(rvc, r + dv, lk + KTILEB);
+      }
+    } else {
+      // cache rows (a chunk without a cache has none: nrec_s = 0 reads zeros)
+      const int P = max(l_s0 + l_u0 + BN * lt + rdma, 0);
+      const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;
+      const uint16_t* kcb = a.kc ? a.kc : a.kr;
+      const uint16_t* vcb = a.vc ? a.vc : a.v;
+      dma16(rsrc(kcb, a.kc ? l_es : 0, nrec_s), row + dk, lk);
+      dma16(rsrc(vcb, a.kc ? l_es : 0, nrec_s), row + dv, lk + KTILEB);
+    }
+    ++lt;
+    lslot = lslot + RINGB == NBUF * RINGB ? 0u : lslot + RINGB;
+  };
+  // Query rows of an item -> the LDS stage (64 positions x 1 KB: the 4 query
+  // heads of the KV head).  Wave w loads positions 8w .. 8w+7; the 16-byte
+  // chunk c of position q sits at c ^ (q & 15), so the 16 positions one
+  // operand read touches fall in 16 different bank groups.  Rows past the
+  // chunk read as zeros.
+  auto load_q = [&](const Item& it) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.q + ((long long)it.b * C * sh.Hq + 4 * it.kvh) * HD), (short)0, nrec_q, 0x00020000);
+    int ln_ = lane;   // (computed here, not held in registers across the loop)
+    asm volatile("" : "+v"(ln_));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int q = 8 * w + m;
+      dma16(rq, (it.t0 + q) * (int)qrowbytes + 16 * (ln_ ^ (q & 15)), lds_q + (unsigned)q * QROWB);
+    }
+  };
+
+  // the first item's query rows and the first four tiles of the stream
+  {
+    const int L0 = item_at(0);
+    load_q(item_params(L0));
+  }
+  prepare();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    issue();
+    prepare();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // ---- operand reads ----
+  // K rows 16kb + i, d = 8(4kk+g) .. +7; lane offsets of the operand reads in
+  // a tile (rows 16 apart share a swizzle)
+  int kofs[4], vofs[8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kofs[kk] = i * ROWB + 16 * ((4 * kk + g) ^ kswz(i));
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int r0 = 4 * g + (i >> 2);
+    vofs[db] = r0 * ROWB + 16 * ((2 * db + ((i & 3) >> 1)) ^ vswz(r0)) + 8 * (i & 1);
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const float c2 = sh.scale_log2;
+  const bool lead = (w >> 2) == 0;
+
+  unsigned base = 0;   // stream position of the current item's first tile
+  int L = item_at(0);
+  for (int round = 0;; ++round) {
+    const Item it = item_params(L);
+    const int b = it.b, kvh = it.kvh, t0 = it.t0, s0 = it.s0;
+    const int n_stile = it.n_stile, kmin = it.kmin, n_tiles = it.n_tiles;
     const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
     const int tq = q0w + i;                 // this lane's query
     const int I = s0 + tq;                  // its absolute position
     const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
-    const int W = sh.W;
-    const int S = sh.S;
-    const int nsink = sh.n_sink;
-
-    // ---- tile list: [sink tiles] + band tiles k = kmin..1 (u0 = t0 + 32k) ----
-    // Band tiles cover chunk-relative key positions t0 - W + 1 .. t0 + 63;
-    // sink tiles cover absolute positions 0 .. n_sink-1 for queries whose
-    // window no longer contains them.
-    const int tq_last = min(t0 + BM, C) - 1;
-    const int n_stile = (nsink > 0 && (s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
-    const int k_lo = -((W - 1 + BN - 1) / BN);
-    const int k_clip = -((s0 + t0 + BN - 1) / BN);
-    const int kmin = max(k_lo, k_clip);
-    const int n_tiles = n_stile + (2 - kmin);
     auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
 
-    // ---- tile loads: global -> staging VGPRs -> padded LDS ----
-    // Thread (lr = tid/16, lc = tid%16) moves 16-byte chunk lc of row lr of
-    // the K and of the V tile.  A tile's loads are issued one pipeline step
-    // before it is stored.
-    const long long rowstride_c = (long long)sh.Hkv * HD;                // elements between tokens
-    const uint16_t* kchunk = a.kr + ((long long)b * C * sh.Hkv + kvh) * HD;
-    const uint16_t* vchunk = a.v + ((long long)b * C * sh.Hkv + kvh) * HD;
-    const uint16_t* kcache = a.kc ? a.kc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
-    const uint16_t* vcache = a.vc ? a.vc + ((long long)b * S * sh.Hkv + kvh) * HD : nullptr;
-    const int lr = tid >> 4, lc = tid & 15;
-    const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;
-    const unsigned voff0 = (unsigned)lr * rowbytes + 16u * lc;
-    u32x4 stage[2];   // K row lr, V row lr
-    // The loader captures by value and selects pointer values only: with
-    // captures by reference, or a struct returned from several places, the
-    // compiler selects between addresses of the pointer variables and keeps
-    // them in scratch memory.
-    auto load_tile = [=](int t, u32x4 (&st)[2]) __attribute__((always_inline)) {
-      const bool is_sink = t < n_stile;
-      const int u0 = is_sink ? 0 : band_u0(t);
-      const bool in_chunk = u0 >= 0;
-      const int P0 = s0 + u0;
-      // fast path: the 32 rows are 32 consecutive rows of the chunk or cache
-      // (the slot arithmetic is done for cache tiles only)
-      int slot0 = 0;
-      bool fast = !is_sink && in_chunk && u0 + BN <= C;
-      if (!is_sink && !in_chunk && P0 >= nsink) {
-        slot0 = nsink + (P0 - nsink) % W;
-        fast = slot0 + BN <= S;
-      }
-      if (fast) {
-        const long long row0 = in_chunk ? u0 : slot0;
-        const uint8_t* kb8 = reinterpret_cast<const uint8_t*>((in_chunk ? kchunk : kcache) + row0 * rowstride_c);
-        const uint8_t* vb8 = reinterpret_cast<const uint8_t*>((in_chunk ? vchunk : vcache) + row0 * rowstride_c);
-        st[0] = *reinterpret_cast<const u32x4*>(kb8 + voff0);
-        st[1] = *reinterpret_cast<const u32x4*>(vb8 + voff0);
-      } else {
-        // edge tiles: each row is located on its own, clamped to a row that
-        // exists (rows that are not keys of any query are masked later)
-        {
-          const int r = lr;
-          // absolute position of the row; rows of band tiles with u0 < 0 are
-          // cache rows, those with u0 >= 0 chunk rows
-          const int P = is_sink ? min(BN * t + r, nsink - 1) : max(P0 + r, 0);
-          const bool from_cache = P < s0 && kcache != nullptr;
-          const int roff = from_cache ? (P < nsink ? P : nsink + (P - nsink) % W)
-                                      : min(max(P - s0, 0), C - 1);
-          const long long eoff = (long long)roff * rowstride_c + 8 * lc;
-          st[0] = *reinterpret_cast<const u32x4*>((from_cache ? kcache : kchunk) + eoff);
-          st[1] = *reinterpret_cast<const u32x4*>((from_cache ? vcache : vchunk) + eoff);
-        }
-      }
-    };
-    // Byte offset of tile t's ring slot.  The empty asm hides the value's
-    // origin from loop strength reduction, which would otherwise keep one
-    // induction variable per LDS address instead of folding the constant parts
-    // into the instructions' offset fields.
-    auto slot_off = [&](int t) __attribute__((always_inline)) {
-      unsigned off = (unsigned)(t % NBUF) * RINGB;
-      asm volatile("" : "+s"(off));
-      return off;
-    };
-    auto store_tile = [&](int t, const u32x4 (&st)[2]) __attribute__((always_inline)) {
-      uint8_t* Kb = smem + slot_off(t);
-      *reinterpret_cast<u32x4*>(Kb + lr * ROWB + 16 * (lc ^ kswz(lr))) = st[0];
-      *reinterpret_cast<u32x4*>(Kb + KTILEB + lr * ROWB + 16 * (lc ^ vswz(lr))) = st[1];
-    };
-    // Band tiles (all tiles but sink tiles, which can only be tiles 0 and 1)
-    // go global -> LDS directly.  Wave w fills rows 4w .. 4w+3 of the K and of
-    // the V tile: lane L loads the chunk that belongs at position L%16 of row
-    // 4w + L/16 under the swizzle.  The descriptor (chunk or cache, uniform per
-    // tile) covers exactly this head's rows of that tensor, so rows past its
-    // end read as zeros; cache rows take the slot map, and rows before
-    // position 0 read slot 0 (they are masked).
-    const int nrec_c = __builtin_amdgcn_readfirstlane((C - 1) * (int)rowbytes + HD * 2);
-    const int nrec_s = __builtin_amdgcn_readfirstlane(kcache ? (S - 1) * (int)rowbytes + HD * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kchunk), (short)0, nrec_c, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vchunk), (short)0, nrec_c, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kcache ? kcache : kchunk), (short)0, nrec_s, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vcache ? vcache : vchunk), (short)0, nrec_s, 0x00020000);
-    const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
-    const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
-    const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
-    const int vrk = rdma * (int)rowbytes + dk;          // lane offsets within a chunk tile
-    const int vrv = rdma * (int)rowbytes + dv;
-    const unsigned lds_base = __builtin_amdgcn_readfirstlane(
-        (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
-    auto dma_tile = [&](int t) __attribute__((always_inline)) {
-      const int u0 = band_u0(t);
-      const unsigned lk = lds_base + (unsigned)(t % NBUF) * RINGB;
-      if (u0 >= 0) {
-        const int srow = u0 * (int)rowbytes;   // uniform part of the offsets
-        dma16(rkc, srow + vrk, lk);
-        dma16(rvc, srow + vrv, lk + KTILEB);
-      } else {
-        const int P = max(s0 + u0 + rdma, 0);
-        const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;
-        dma16(rks, row + dk, lk);
-        dma16(rvs, row + dv, lk + KTILEB);
-      }
-    };
-    // tiles 0 .. 3 in flight while Q is prepared; tiles 0 and 1 go through
-    // registers when the work-group has sink tiles
-    if (n_stile == 0) {
-      dma_tile(0);
-      dma_tile(1);
-    } else {
-      if (n_tiles > 0) {
-        load_tile(0, stage);
-        store_tile(0, stage);
-      }
-      if (n_tiles > 1) {
-        load_tile(1, stage);
-        store_tile(1, stage);
-      }
-    }
-    dma_tile(2);
-    dma_tile(3);
-
-    // ---- Q prologue: rotated, scaled, rounded to bf16, in the B-operand layout ----
+    // ---- Q from the stage: rotated, scaled, rounded to bf16, in the B-operand layout ----
     // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
     // The softmax scale and log2(e) are applied before the rounding, so that
     // QK^T yields scores in the log2 domain directly.
-    const float c2 = sh.scale_log2;
     bf16x8 qf[QB][4];
+    // (the asm keeps the table addresses from being computed once for all
+    // items and held in registers)
+    int gi = g;
+    asm volatile("" : "+v"(gi));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      // without RoPE every rev is 0: the rotation is the identity
       float cs[4], sn[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if (sh.rope) {
-          rope_cs(I, rope_rev[4 * (4 * kk + g) + jj], cs[jj], sn[jj]);
-        } else {
-          cs[jj] = 1.f;
-          sn[jj] = 0.f;
-        }
-      }
+      for (int jj = 0; jj < 4; ++jj) rope_cs(I, rope_rev[4 * (4 * kk + gi) + jj], cs[jj], sn[jj]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        u32x4 wv = {0u, 0u, 0u, 0u};
-        if (tq < C)
-          wv = *reinterpret_cast<const u32x4*>(
-              a.q + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD + 8 * (4 * kk + g));
+        const int c = 16 * (QB * (w >> 2) + qb) + 4 * kk + g;
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(qstage + (16 * (w & 3) + i) * QROWB + 16 * (c ^ i));
         u32x4 r;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -395,7 +446,6 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // row sums of P accumulate on the matrix core: an all-ones A operand makes
     // every row of lsum[qb] the sum over keys of P for this lane's query
     floatx4 lsum[QB];
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       ref[qb] = -INFINITY;
@@ -409,18 +459,26 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // ---- operands and stages of one 32-key tile ----
     bf16x8 kop[2][4];   // K operand of the next QK^T: [kb][kk]
     bf16x8 vop[8];      // V^T operand of the next PV: [db]
-    // K rows 16kb + i, d = 8(4kk+g) .. +7
-    // lane offsets of the operand reads in a tile (rows 16 apart share a swizzle)
-    int kofs[4], vofs[8];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kofs[kk] = i * ROWB + 16 * ((4 * kk + g) ^ kswz(i));
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int r0 = 4 * g + (i >> 2);
-      vofs[db] = r0 * ROWB + 16 * ((2 * db + ((i & 3) >> 1)) ^ vswz(r0)) + 8 * (i & 1);
-    }
-    auto read_k = [&](int t) __attribute__((always_inline)) {
-      const uint8_t* Kb = smem + slot_off(t);
+    // Byte offset of tile t's ring slot.  The empty asm hides the value's
+    // origin from loop strength reduction, which would otherwise keep one
+    // induction variable per LDS address instead of folding the constant
+    // parts into the instructions' offset fields.
+    // Ring offsets of tile j (cur) and tile j+1 (nxt) in matrix phase j;
+    // matrix phase j > 0 advances them after its QK^T products, while those
+    // still execute.
+    unsigned cur = (base % NBUF) * RINGB;
+    unsigned nxt = cur + RINGB == NBUF * RINGB ? 0u : cur + RINGB;
+    auto advance = [&]() __attribute__((always_inline)) {
+      cur = nxt;
+      nxt = nxt + RINGB == NBUF * RINGB ? 0u : nxt + RINGB;
+      asm volatile("" : "+s"(cur), "+s"(nxt));
+    };
+    auto slot_off = [&](unsigned o) __attribute__((always_inline)) {
+      asm volatile("" : "+s"(o));
+      return o;
+    };
+    auto read_k = [&](unsigned so) __attribute__((always_inline)) {
+      const uint8_t* Kb = smem + slot_off(so);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -430,8 +488,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // Transposing reads: lane i of a 16-lane group addresses key base+i/4,
     // d 16db+4(i%4), and receives V[base+e][16db+i] for e = 0..3 (base = 4g,
     // then 16+4g), which is the A operand of O^T += V^T P^T.
-    auto read_v = [&](int t) __attribute__((always_inline)) {
-      lds_u8* Vb = (lds_u8*)smem + slot_off(t) + KTILEB;
+    auto read_v = [&](unsigned so) __attribute__((always_inline)) {
+      lds_u8* Vb = (lds_u8*)smem + slot_off(so) + KTILEB;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(Vb + vofs[db]));
@@ -536,28 +594,32 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // head by head, with K(j+1) and V(j) read from LDS into the operand
     // registers as the products release them.
     // Vector phase j: the mask and threshold checks of S(j), the rare rescale,
-    // P(j) = exp2(S(j)), and the direct loads of tile j+4.  A barrier ends
-    // every phase.  Waves 4..7 run one phase behind waves 0..3, so the two
-    // waves of each SIMD (w and w+4) are always in different phases: one feeds
-    // the matrix core and the LDS while the other uses the vector ALU.
-    // Ring timing (phases counted from the first matrix phase of waves 0..3:
-    // matrix phase j is phase 2j for those, 2j+1 for waves 4..7).  Every
-    // barrier waits for all but the newest tile load of the wave, so tile t,
-    // loaded in phases 2t-7 and 2t-6, is complete at the barrier ending phase
-    // 2t-4 and visible before its first read (K(t) in phase 2t-2).  Its last
-    // read (V(t), phase 2t+1) completes before the barrier ending the vector
-    // phase that follows (lgkmcnt(0)), and the loads of tile t+8 into its slot
-    // start in phase 2t+9.  Loads past the band read whatever the buffers hold
-    // there (or zeros) and are never used.
+    // P(j) = exp2(S(j)), and the load of the stream's next tile (tile j+4 of
+    // this item, or an early tile of the next).  A barrier ends every phase.
+    // Waves 4..7 run one phase behind waves 0..3, so the two waves of each
+    // SIMD (w and w+4) are always in different phases: one feeds the matrix
+    // core and the LDS while the other uses the vector ALU.
+    // Ring timing, counted in stream tiles T and in phases from the first
+    // matrix phase of waves 0..3 (matrix phase j is phase 2j for those, 2j+1
+    // for waves 4..7; the barriers between items only add phases).  Tile T
+    // is loaded in the vector phase of tile T-4 (phases 2T-7 / 2T-6).  The
+    // barrier ending every vector phase waits for all but the wave's newest
+    // tile load, so T is complete at the barrier ending phase 2T-4 and
+    // visible before its first read (K(T) in phase 2T-2).  Its last read (V(T),
+    // phases 2T / 2T+1) completes before the barrier ending phase 2T+2
+    // (lgkmcnt(0)), and the load of tile T+5 into its slot starts in phase
+    // 2T+3.  The barriers ending matrix phases need no memory wait: no load
+    // is issued in a matrix phase.
     floatx4 s[2][QB];
     bf16x8 p[QB];
     auto mphase = [&](int j, bool qk, bool pv) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       if (qk) qk_mma(s, 0, QB);
       __builtin_amdgcn_sched_barrier(0);
+      if (j > 0) advance();
       if (pv) {
         pv_mma(p, 0);
-        if (qk) read_k(j + 1);
+        if (qk) read_k(nxt);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -565,24 +627,30 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         pv_mma(p, 1);
-        if (qk) read_v(j);
+        if (qk) read_v(cur);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       } else {
-        read_k(j + 1);
-        read_v(j);
+        read_k(nxt);
+        read_v(cur);
       }
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto vphase = [&](int j) __attribute__((always_inline)) {
-      const int mk = mask_kind(j);
-      if (mk) apply_mask(j, mk, s);
+    // the next item, whose query rows go to the stage during this item
+    const int Ln = item_at(round + 1);
+    // masked: 0 no mask, 1 the mask kind is looked up, 2 a band-edge or sink mask
+    auto vphase = [&](int j, bool first, int masked) __attribute__((always_inline)) {
+      if (masked == 1) {
+        const int mk = mask_kind(j);
+        if (mk) apply_mask(j, mk, s);
+      } else if (masked == 2) {
+        apply_mask(j, j < n_stile ? 2 : 1, s);
+      }
       bool rare = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) rare |= over(s, qb);
@@ -593,32 +661,54 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(p[qb]));
       __builtin_amdgcn_sched_barrier(0);
-      dma_tile(j + 4);
-      ring_barrier();
+      issue();
+      prepare();
+      if (first && Ln >= 0) {
+        // The stage was read before the barrier that opened this item.  The
+        // 8 query-row loads are younger than the tile load, so this barrier
+        // still completes everything but the newest tile; the next vector
+        // phase's barrier completes them.
+        load_q(item_params(Ln));
+        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
-    const bool lead = (w >> 2) == 0;
-    __syncthreads();
-    if (n_tiles > 0) {
-      read_k(0);
-      if (!lead) __builtin_amdgcn_s_barrier();
-      mphase(0, true, false);
-      vphase(0);
-      for (int j = 1; j < n_tiles; ++j) {
-        mphase(j, true, true);
-        vphase(j);
-      }
-      mphase(n_tiles, false, true);
-      if (lead) __builtin_amdgcn_s_barrier();
+    // all waves have read the stage (and the previous item's last operands)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_k(cur);
+    if (!lead) __builtin_amdgcn_s_barrier();
+    mphase(0, true, false);
+    vphase(0, true, 1);
+    // tiles 1 .. n-1: masked below jlo, unmasked jlo .. jhi, masked above
+    const int ju = min(max(jlo, 1), n_tiles), jv = min(max(jhi + 1, ju), n_tiles);
+    int j = 1;
+    for (; j < ju; ++j) {
+      mphase(j, true, true);
+      vphase(j, false, 2);
     }
-    // the last tile loads must land before the work-group's LDS is released
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (; j < jv; ++j) {
+      mphase(j, true, true);
+      vphase(j, false, 0);
+    }
+    for (; j < n_tiles; ++j) {
+      mphase(j, true, true);
+      vphase(j, false, 2);
+    }
+    mphase(n_tiles, false, true);
+    if (lead) __builtin_amdgcn_s_barrier();
 
     // ---- epilogue: O / l, LSE ----
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float lt = lsum[qb][0];
-      const float inv = 1.f / lt;
+      const float lt_ = lsum[qb][0];
+      const float inv = 1.f / lt_;
       if (tq < C) {
         uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD;
 #pragma unroll
@@ -628,10 +718,15 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
           *reinterpret_cast<u32x2*>(dst + 16 * db + 4 * g) = val;
         }
         if (a.lse && g == 0)
-          a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lt)) * 0.69314718055994531f;
+          a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lt_)) * 0.69314718055994531f;
       }
     }
+    base += (unsigned)n_tiles;
+    if (Ln < 0) break;
+    L = Ln;
   }  // items
+  // the stream's last loads must land before the work-group's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
