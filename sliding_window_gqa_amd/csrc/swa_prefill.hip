@@ -257,10 +257,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // cache rows take the slot map, and rows before position 0 read slot 0
   // (they are masked).
   const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
-  const int dk = 16 * ((lane & 15) ^ kswz(rdma));     // byte of that row, K
-  const int dv = 16 * ((lane & 15) ^ vswz(rdma));     // byte of that row, V
-  const int vrk = rdma * (int)rowbytes + dk;          // lane offsets within a chunk tile
-  const int vrv = rdma * (int)rowbytes + dv;
+  const int vrk = rdma * (int)rowbytes + 16 * ((lane & 15) ^ kswz(rdma));   // lane offsets
+  const int vrv = rdma * (int)rowbytes + 16 * ((lane & 15) ^ vswz(rdma));   // in a chunk tile
   const unsigned lds_ring = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
   const unsigned lds_q = __builtin_amdgcn_readfirstlane(
@@ -300,6 +298,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // their offsets (l_srow) ready.
   int l_slow = -1;       // >= 0 iff the next tile is a band tile of the chunk
   int l_srow = 0;        // its uniform byte offset
+  int l_cm = -1;         // cache band tiles: see prepare()
   auto prepare = [&]() __attribute__((always_inline)) {
     if (lt >= l_nt) {
       const int L = item_at(lr_round + 1);
@@ -310,36 +309,56 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       }
     }
     const int u0 = l_u0 + BN * lt;
-    l_slow = (lt - l_ns) | u0;
-    l_srow = u0 * (int)rowbytes;
+    l_slow = __builtin_amdgcn_readfirstlane((lt - l_ns) | u0);
+    l_srow = __builtin_amdgcn_readfirstlane(u0 * (int)rowbytes);
     asm volatile("" : "+s"(l_slow), "+s"(l_srow));   // (computed here, in the wait's shadow)
+    if (l_slow < 0 && lt >= l_ns) {
+      // cache band tile: the rolling-buffer slot of the wave's first row,
+      // less n_sink, when all its rows lie past the sinks
+      const int P0 = l_s0 + u0 + 4 * w;
+      l_cm = P0 >= nsink ? (P0 - nsink) % W : -1;
+    }
   };
   // load the prepared tile into its ring slot
   auto issue = [&]() __attribute__((always_inline)) {
     const unsigned lk = lds_ring + lslot;
     if (__builtin_expect(l_slow >= 0, 1)) {
       dma16x2(rkc, l_srow + vrk, lk, rvc, l_srow + vrv, lk + KTILEB);
-    } else if (lt < l_ns) {
-      // sink tile: absolute positions 32 lt + r (clamped to the last sink);
-      // those before the item's chunk come from the cache, the rest from
-      // the chunk
-      const int P = min(BN * lt + rdma, nsink - 1);
-      if (P < l_s0 && a.kc != nullptr) {
-        dma16(rsrc(a.kc, l_es, nrec_s), P * (int)rowbytes + dk, lk);
-        dma16(rsrc(a.vc, l_es, nrec_s), P * (int)rowbytes + dv, lk + KTILEB);
-      } else {
-        const int r = min(max(P - l_s0, 0), C - 1) * (int)rowbytes;
-        dma16(rkc, r + dk, lk);
-        dma16(rvc, r + dv, lk + KTILEB);
-      }
     } else {
-      // cache rows (a chunk without a cache has none: nrec_s = 0 reads zeros)
-      const int P = max(l_s0 + l_u0 + BN * lt + rdma, 0);
-      const int row = (P < nsink ? P : nsink + (P - nsink) % W) * (int)rowbytes;
-      const uint16_t* kcb = a.kc ? a.kc : a.kr;
-      const uint16_t* vcb = a.vc ? a.vc : a.v;
-      dma16(rsrc(kcb, a.kc ? l_es : 0, nrec_s), row + dk, lk);
-      dma16(rsrc(vcb, a.kc ? l_es : 0, nrec_s), row + dv, lk + KTILEB);
+      // (lane offsets recomputed here rather than held in registers)
+      int ln_ = lane;
+      asm volatile("" : "+v"(ln_));
+      const int r = ln_ >> 4, rd = 4 * w + r;
+      const int dk_ = 16 * ((ln_ & 15) ^ kswz(rd)), dv_ = 16 * ((ln_ & 15) ^ vswz(rd));
+      if (lt < l_ns) {
+        // sink tile: absolute positions 32 lt + r (clamped to the last sink);
+        // those before the item's chunk come from the cache, the rest from
+        // the chunk
+        const int P = min(BN * lt + rd, nsink - 1);
+        if (P < l_s0 && a.kc != nullptr) {
+          dma16(rsrc(a.kc, l_es, nrec_s), P * (int)rowbytes + dk_, lk);
+          dma16(rsrc(a.vc, l_es, nrec_s), P * (int)rowbytes + dv_, lk + KTILEB);
+        } else {
+          const int rr = min(max(P - l_s0, 0), C - 1) * (int)rowbytes;
+          dma16(rkc, rr + dk_, lk);
+          dma16(rvc, rr + dv_, lk + KTILEB);
+        }
+      } else {
+        // cache rows (a chunk without a cache has none: nrec_s = 0 reads zeros)
+        int sl;
+        if (l_cm >= 0) {
+          sl = l_cm + r;
+          sl = nsink + (sl >= W ? sl - W : sl);
+        } else {
+          const int P = max(l_s0 + l_u0 + BN * lt + rd, 0);
+          sl = P < nsink ? P : nsink + (P - nsink) % W;
+        }
+        const int row = sl * (int)rowbytes;
+        const uint16_t* kcb = a.kc ? a.kc : a.kr;
+        const uint16_t* vcb = a.vc ? a.vc : a.v;
+        dma16x2(rsrc(kcb, a.kc ? l_es : 0, nrec_s), row + dk_, lk,
+                rsrc(vcb, a.kc ? l_es : 0, nrec_s), row + dv_, lk + KTILEB);
+      }
     }
     ++lt;
     lslot = lslot + RINGB == NBUF * RINGB ? 0u : lslot + RINGB;
@@ -390,23 +409,14 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   const float c2 = sh.scale_log2;
   const bool lead = (w >> 2) == 0;
 
-  unsigned base = 0;   // stream position of the current item's first tile
-  int L = item_at(0);
-  for (int round = 0;; ++round) {
-    const Item it = item_params(L);
-    const int b = it.b, kvh = it.kvh, t0 = it.t0, s0 = it.s0;
-    const int n_stile = it.n_stile, kmin = it.kmin, n_tiles = it.n_tiles;
-    const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
-    const int tq = q0w + i;                 // this lane's query
-    const int I = s0 + tq;                  // its absolute position
-    const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
-    auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
-
-    // ---- Q from the stage: rotated, scaled, rounded to bf16, in the B-operand layout ----
-    // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query tq, head h0+qb.
-    // The softmax scale and log2(e) are applied before the rounding, so that
-    // QK^T yields scores in the log2 domain directly.
-    bf16x8 qf[QB][4];
+  // ---- Q from the stage: rotated, scaled, rounded to bf16, in the B-operand layout ----
+  // lane (i, g), step kk holds d = 8*(4kk+g) .. +7 of query t0 + 16(w&3) + i,
+  // head 4 kvh + 2(w>>2) + qb.  The softmax scale and log2(e) are applied
+  // before the rounding, so that QK^T yields scores in the log2 domain
+  // directly.
+  bf16x8 qf[QB][4];
+  auto load_qf = [&](const Item& it) __attribute__((always_inline)) {
+    const int I = it.s0 + it.t0 + 16 * (w & 3) + i;   // absolute position of the lane's query
     // (the asm keeps the table addresses from being computed once for all
     // items and held in registers)
     int gi = g;
@@ -431,6 +441,22 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         qf[qb][kk] = __builtin_bit_cast(bf16x8, r);
       }
     }
+  };
+
+  unsigned base = 0;   // stream position of the current item's first tile
+  int L = item_at(0);
+  Item it = item_params(L);
+  load_qf(it);
+  for (int round = 0;; ++round) {
+    const int b = it.b, kvh = it.kvh, t0 = it.t0, s0 = it.s0;
+    const int n_stile = it.n_stile, kmin = it.kmin, n_tiles = it.n_tiles;
+    const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
+    const int tq = q0w + i;                 // this lane's query
+    const int I = s0 + tq;                  // its absolute position
+    const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
+    // the next item, whose query rows go to the stage during this item
+    const int Ln = item_at(round + 1);
+    auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
 
     // ---- softmax state of each query column (one per head qb) ----
     // ref[qb]: reference of the exponentials, the running max of the scores
@@ -641,8 +667,6 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
-    // the next item, whose query rows go to the stage during this item
-    const int Ln = item_at(round + 1);
     // masked: 0 no mask, 1 the mask kind is looked up, 2 a band-edge or sink mask
     auto vphase = [&](int j, bool first, int masked) __attribute__((always_inline)) {
       if (masked == 1) {
@@ -678,7 +702,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
-    // all waves have read the stage (and the previous item's last operands)
+    // all waves are done with the stage (and the previous item's operands)
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -704,25 +728,54 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     mphase(n_tiles, false, true);
     if (lead) __builtin_amdgcn_s_barrier();
 
-    // ---- epilogue: O / l, LSE ----
+    // ---- switch: the next item's query rows leave the stage, O / l goes
+    // through it.  O is written to the stage as bf16 rows (the layout of
+    // the query rows), so that each wave then stores whole 1 KB rows (the 4
+    // heads of one position) to memory.
+    Item itn = it;
+    if (Ln >= 0) {
+      itn = item_params(Ln);
+      load_qf(itn);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // (lane indices through an empty asm: the addresses below are computed
+    // here, not held in registers across the tile loop)
+    int li_ = lane;
+    asm volatile("" : "+v"(li_));
+    const int ii = li_ & 15, gg = li_ >> 4;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float lt_ = lsum[qb][0];
-      const float inv = 1.f / lt_;
-      if (tq < C) {
-        uint16_t* dst = a.out + (((long long)b * C + tq) * sh.Hq + h0 + qb) * HD;
+      const float inv = 1.f / lsum[qb][0];
+      uint8_t* row = qstage + (16 * (w & 3) + ii) * QROWB + 8 * (gg & 1);
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          u32x2 val = {pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv),
-                       pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
-          *reinterpret_cast<u32x2*>(dst + 16 * db + 4 * g) = val;
+      for (int db = 0; db < 8; ++db) {
+        const int c = 16 * (QB * (w >> 2) + qb) + 2 * db + (gg >> 1);
+        const u32x2 val = {pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv),
+                           pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
+        *reinterpret_cast<u32x2*>(row + 16 * (c ^ ii)) = val;
+      }
+      if (a.lse && g == 0 && tq < C)
+        a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lsum[qb][0])) * 0.69314718055994531f;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    {
+      uint16_t* orow = a.out + ((long long)b * C * sh.Hq + 4 * kvh) * HD;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int q = 8 * w + m;
+        if (t0 + q < C) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qstage + q * QROWB + 16 * li_);
+          *reinterpret_cast<u32x4*>(orow + (long long)(t0 + q) * sh.Hq * HD + 8 * (li_ ^ (q & 15))) = v;
         }
-        if (a.lse && g == 0)
-          a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lt_)) * 0.69314718055994531f;
       }
     }
     base += (unsigned)n_tiles;
     if (Ln < 0) break;
+    it = itn;
     L = Ln;
   }  // items
   // the stream's last loads must land before the work-group's LDS is released
