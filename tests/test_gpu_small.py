@@ -103,6 +103,10 @@ PREFILL_CASES = [
     # over several items (288 and 272 items in the first and second chunk)
     (2, 32, 8, 128, 300, 0, torch.bfloat16, [1100, 1030]),
     (2, 32, 8, 128, 300, 4, torch.bfloat16, [1100, 1030]),
+    # many short items per work-group (2 or 3 tiles each): the tile loads run
+    # four tiles ahead across several items (576 and 1032 items)
+    (4, 32, 8, 128, 40, 0, torch.bfloat16, [1100, 300]),
+    (2, 32, 8, 128, 16, 3, torch.bfloat16, [4100, 50]),
     # generic path
     (2, 4, 2, 64, 100, 0, torch.bfloat16, [130, 1, 70]),
     (1, 6, 2, 128, 50, 3, torch.float32, [90, 7, 40]),
