@@ -316,7 +316,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       // cache band tile: the rolling-buffer slot of the wave's first row,
       // less n_sink, when all its rows lie past the sinks
       const int P0 = l_s0 + u0 + 4 * w;
-      l_cm = P0 >= nsink ? (P0 - nsink) % W : -1;
+      l_cm = P0 >= nsink ? (int)((unsigned)(P0 - nsink) % (unsigned)W) : -1;
     }
   };
   // load the prepared tile into its ring slot
@@ -324,6 +324,14 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     const unsigned lk = lds_ring + lslot;
     if (__builtin_expect(l_slow >= 0, 1)) {
       dma16x2(rkc, l_srow + vrk, lk, rvc, l_srow + vrv, lk + KTILEB);
+    } else if (lt >= l_ns && l_cm >= 0 && l_cm + 3 < W) {
+      // cache band tile whose 4 rows per wave are consecutive slots: the
+      // lane offsets of a chunk tile, the uniform part from the slot
+      // (a chunk without a cache has no cache rows: nrec_s = 0 reads zeros)
+      const int srow = (nsink + l_cm - 4 * w) * (int)rowbytes;
+      const long long e = a.kc ? l_es : 0;
+      dma16x2(rsrc(a.kc ? a.kc : a.kr, e, nrec_s), srow + vrk, lk,
+              rsrc(a.vc ? a.vc : a.v, e, nrec_s), srow + vrv, lk + KTILEB);
     } else {
       // (lane offsets recomputed here rather than held in registers)
       int ln_ = lane;
