@@ -15,13 +15,17 @@
 //   m* = max m_s,  l* = sum l_s 2^(m_s - m*),  o = sum o_s 2^(m_s - m*) / l*.
 //
 // Fast kernel (bf16, head_dim 128, GQA group 4):
-//  * A wave takes 32 slots at a time.  K is loaded straight from global
-//    memory in the A-operand layout of v_mfma_f32_16x16x32_bf16 (lane = slot,
-//    8 consecutive head-dim elements), S^T = K Q^T with the 4 query heads of
-//    the group as the B columns (the other 12 columns are zero).
-//  * Each lane loads 8 V rows (16 bytes at one head-dim offset) and
-//    transposes them in registers into the A operand of O^T += V^T P^T, so V
-//    needs no LDS round trip.  The score accumulator is the B operand.
+//  * A wave takes 32 slots at a time.  K goes global -> LDS directly (buffer
+//    loads with the lds modifier), 16 lanes per whole 256-byte row, into a
+//    per-wave double buffer, and is read back in the A-operand layout of
+//    v_mfma_f32_16x16x32_bf16 (lane = slot, 8 consecutive head-dim
+//    elements): S^T = K Q^T with the 4 query heads of the group as the B
+//    columns (the other 12 columns are zero).  Loading K in the operand
+//    layout straight from memory (16 rows x 64 bytes per instruction) reads
+//    the cache ~8% slower than whole rows.
+//  * Each lane loads 8 V rows (16 bytes at one head-dim offset; whole rows
+//    per instruction) and transposes them in registers into the A operand of
+//    O^T += V^T P^T.  The score accumulator is the B operand.
 //  * The 4 waves of a work-group interleave over the range and merge through
 //    LDS, so one partial per (sequence, query head, range) reaches memory.
 #include <math.h>
@@ -67,7 +71,41 @@ struct DecodeArgs {
   float* lse;
 };
 
+// K chunks in LDS: 32 rows of 256 bytes, the 16-byte chunk c of row r at
+// c ^ (r & 15), so that the 16 rows one operand read touches sit in 16
+// different bank groups.
+constexpr int DROWB = HD * 2;          // bytes per K row
+constexpr int DTILE = kChunk * DROWB;  // one 32-slot K chunk
+__device__ inline int dkswz(int r) { return r & 15; }
+typedef __attribute__((address_space(3))) uint8_t lds_du8;
+
+// Two direct global-to-LDS loads (each lane's 16 bytes at byte offset o of
+// the buffer r, zeros when out of range, land at LDS address l + 16 * lane:
+// 1 KB per instruction) with one save and restore of M0, which carries the
+// LDS address; one wait state separates each M0 write from its load.  The
+// loads are non-temporal, like the V loads: each cache byte is read once
+// per call (and, with the caches full of dirty lines, allocating would cost
+// their write-back).  The compiler does not count these loads: the loop
+// waits for them explicitly.
+__device__ inline void ddma2(__amdgpu_buffer_rsrc_t r0, int o0, unsigned l0,
+                             __amdgpu_buffer_rsrc_t r1, int o1, unsigned l1) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %5, %6, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(l0), "v"(o0), "s"(r0), "s"(l1), "v"(o1), "s"(r1)
+      : "memory");
+}
+
 __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[4 * 2 * DTILE];   // [wave][buffer] K
   __shared__ float sm_m[4][4], sm_l[4][4];
   __shared__ float sm_o[4][4][HD];
   __shared__ double rope_rev[kMaxPairs];
@@ -91,16 +129,19 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   const float c2 = sh.scale_log2;
 
   // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
-  // The RoPE frequencies are staged in LDS (one coalesced read instead of a
-  // dependent kernel-argument load per element).
   if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
   __syncthreads();
   bf16x8 qf[4];
   auto load_q = [&]() __attribute__((always_inline)) {
+    // (all four loads go out before the first is used; lanes i >= 4 load a
+    // row that exists and drop it)
+    u32x4 wq[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      wq[kk] = *reinterpret_cast<const u32x4*>(a.q + ((long long)b * sh.Hq + h0 + (i & 3)) * HD + 8 * (4 * kk + g));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (i < 4) wv = *reinterpret_cast<const u32x4*>(a.q + ((long long)b * sh.Hq + h0 + i) * HD + 8 * (4 * kk + g));
+      const u32x4 wv = i < 4 ? wq[kk] : u32x4{0u, 0u, 0u, 0u};
       u32x4 r;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -121,44 +162,55 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // K: A operand rows = slots c0+16kb+i, d = 8*(4kk+g) .. +7
-  // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
   // Buffer loads: the descriptors cover exactly this head's rows of the live
   // slots [0, vend), so rows past vend read as zeros (and are masked out of
-  // the softmax) with no per-lane branch or clamp; every address is a 32-bit
-  // lane offset plus the chunk's row offset.
+  // the softmax).  Each K/V byte is read once per call.
   const unsigned rowb = (unsigned)row_stride * 2u;
-  // (the descriptor inputs are made explicitly wave-uniform; otherwise the
-  // compiler keeps the descriptors in VGPRs and loops over lanes per load)
   const int nrec = __builtin_amdgcn_readfirstlane((vend - 1) * (int)rowb + HD * 2);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbase), (short)0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbase), (short)0, nrec, 0x00020000);
-  unsigned koff[2], voff[8];
+  // Load instruction e (0..7) of a chunk fills rows 4e .. 4e+3 (row 4e + g'
+  // for lane (i', g')): the lane fetches the 16-byte chunk that belongs at
+  // position i' under the swizzle.  The swizzles repeat every 4 instructions.
+  int ko[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) koff[kb] = (unsigned)(16 * kb + i) * rowb + 16u * g;
+  for (int e = 0; e < 4; ++e) ko[e] = g * (int)rowb + 16 * (i ^ dkswz(4 * e + g));
+  const unsigned lds_w = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((lds_du8*)kvs) + (unsigned)w * (2u * DTILE));
+  auto dma_chunk = [&](int c0, int buf) __attribute__((always_inline)) {
+    const int cb = c0 * (int)rowb;
+    const unsigned lb = lds_w + (unsigned)buf * DTILE;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      ddma2(rk, cb + 4 * e * (int)rowb + ko[e & 3], lb + 1024u * e,
+            rk, cb + 4 * (e + 1) * (int)rowb + ko[(e + 1) & 3], lb + 1024u * (e + 1));
+  };
+  // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
+  unsigned voff[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) voff[e] = (unsigned)(e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) * rowb + 16u * i;
-  // Each K/V byte is read once per call: the loads are non-temporal (nt).
   constexpr int kNT = 2;
-  auto load_chunk = [&](int c0, u32x4 (&kr)[2][4], u32x4 (&vr)[8]) __attribute__((always_inline)) {
+  auto load_v = [&](int c0, u32x4 (&vr)[8]) __attribute__((always_inline)) {
     const unsigned cb = (unsigned)c0 * rowb;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kr[kb][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(cb + koff[kb] + 64u * kk), 0, kNT));
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vr[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(cb + voff[e]), 0, kNT));
   };
-  auto do_chunk = [&](int c0, const u32x4 (&kr)[2][4], const u32x4 (&vr)[8]) __attribute__((always_inline)) {
+  // operand reads (as the chunk layout above): K rows 16kb + i, d-chunk 4kk+g
+  int kofs[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kofs[kk] = i * DROWB + 16 * ((4 * kk + g) ^ dkswz(i));
+  auto do_chunk = [&](int c0, int buf, const u32x4 (&vr)[8]) __attribute__((always_inline)) {
+    const uint8_t* Kb = kvs + (w * 2 + buf) * DTILE;
     floatx4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kb][kk]), qf[kk], s[kb], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(Kb + kofs[kk] + 16 * kb * DROWB);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[kk], s[kb], 0, 0, 0);
+      }
     }
     // mask slots past the live range
     if (c0 + kChunk > vend) {
@@ -203,37 +255,47 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
       const int wd = db >> 1;
       u32x4 va;
 #pragma unroll
-      for (int m2 = 0; m2 < 4; ++m2) {
-        // low halves (even db) or high halves (odd db) of two packed pairs
+      for (int m2 = 0; m2 < 4; ++m2)
         va[m2] = __builtin_amdgcn_perm(vr[2 * m2 + 1][wd], vr[2 * m2][wd], (db & 1) ? 0x07060302u : 0x05040100u);
-      }
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[db], 0, 0, 0);
     }
   };
-  // Each wave takes chunks c0, c0 + 4*kChunk, ... of the range; the loads of
-  // the next chunk are in flight while the current one is computed (two
-  // register buffers, alternating).  The prefetch is unconditional (past the
-  // range it reads slot vend-1 again), so the compiler's count of outstanding
-  // loads stays exact and it waits for the current chunk only.
+  // Each wave takes chunks c0, c0 + 4*kChunk, ... of the range; the next
+  // chunk's 16 loads go out before the current chunk is computed (past the
+  // range they read zeros).  The buffer a load fills was last read by the
+  // previous chunk's products, which have consumed their operands.
+  // Step m: K(m+1) to LDS (8 loads), the products of chunk m, then V(m+2)
+  // into the registers V(m) held.  K(m) is complete once at most the 16
+  // younger loads (V(m+1), K(m+1)) are outstanding; the compiler's own wait
+  // for V(m) (8 younger register loads in its count) leaves K(m+1) in flight.
   {
     const int cstep = 4 * kChunk;
-    u32x4 krA[2][4], vrA[8], krB[2][4], vrB[8];
     int c0 = sp0 + kChunk * w;
-    // the first chunk's loads go out before the query is prepared
-    if (c0 < vend) load_chunk(c0, krA, vrA);
-    load_q();
+    u32x4 vA[8], vB[8];
     if (c0 < vend) {
-      while (true) {
-        load_chunk(c0 + cstep, krB, vrB);
-        do_chunk(c0, krA, vrA);
-        c0 += cstep;
-        if (c0 >= vend) break;
-        load_chunk(c0 + cstep, krA, vrA);
-        do_chunk(c0, krB, vrB);
-        c0 += cstep;
-        if (c0 >= vend) break;
-      }
+      dma_chunk(c0, 0);
+      load_v(c0, vA);
+      load_v(c0 + cstep, vB);
     }
+    load_q();
+    int buf = 0;
+    while (c0 < vend) {
+      dma_chunk(c0 + cstep, buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      do_chunk(c0, buf, vA);
+      load_v(c0 + 2 * cstep, vA);
+      c0 += cstep;
+      buf ^= 1;
+      if (c0 >= vend) break;
+      dma_chunk(c0 + cstep, buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      do_chunk(c0, buf, vB);
+      load_v(c0 + 2 * cstep, vB);
+      c0 += cstep;
+      buf ^= 1;
+    }
+    // the last loads must land before the work-group's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // ---- merge the 4 waves through LDS ----
