@@ -568,20 +568,25 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       if (j < n_stile) return 2;
       return (j >= jlo && j <= jhi) ? 0 : 1;
     };
+    // Each kind is one interval test per key: sink key P (absolute) is kept
+    // iff P <= min(n_sink - 1, I - W); band key u (chunk-relative) iff
+    // max(tq - W + 1, -s0) <= u <= tq (a non-empty interval: tq >= 0 >= -s0).
     auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
+      int k0, lo, span;   // key index of row 0 of this lane, interval [lo, lo + span]
+      if (mk == 2) {
+        k0 = BN * j + 4 * g;
+        lo = INT_MIN / 2;
+        span = min(nsink - 1, I - W) - lo;
+      } else {
+        k0 = band_u0(j) + 4 * g;
+        lo = max(tq - W + 1, -s0);
+        span = tq - lo;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int kr_ = 16 * kb + 4 * g + r;
-          bool ok;
-          if (mk == 2) {
-            const int P = BN * j + kr_;
-            ok = P < nsink && P <= I - W;
-          } else {
-            const int u = band_u0(j) + kr_;
-            ok = (u <= tq) && (u > tq - W) && (s0 + u >= 0);
-          }
+          const bool ok = (unsigned)(k0 + 16 * kb + r - lo) <= (unsigned)span;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
         }
