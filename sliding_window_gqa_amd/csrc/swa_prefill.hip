@@ -475,6 +475,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // then the rare path moves ref to the new max, rescales O and l by
     // exp2(ref_old - ref_new) and shifts s.
     float ref[QB], thr[QB];
+    float thrm = -INFINITY;   // min(thr[0], thr[1])
     floatx4 negoff[QB];
     floatx4 o[8][QB];
     // row sums of P accumulate on the matrix core: an all-ones A operand makes
@@ -600,10 +601,23 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       pk[3] = pack_bf16(__builtin_amdgcn_exp2f(s[1][qb][2]), __builtin_amdgcn_exp2f(s[1][qb][3]));
       p[qb] = __builtin_bit_cast(bf16x8, pk);
     };
-    // whether some s of head qb in this lane exceeds its column's threshold
-    auto over = [&](const floatx4 (&s)[2][QB], int qb) __attribute__((always_inline)) {
-      const float mx = __builtin_elementwise_maximum(vmax4(s[0][qb]), vmax4(s[1][qb]));
-      return mx > thr[qb];
+    // v_maximum3_f32 (IEEE maximum, NaN-propagating, of three)
+    auto mx3 = [](float x, float y, float z) __attribute__((always_inline)) {
+      float m;
+      asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(x), "v"(y), "v"(z));
+      return m;
+    };
+    // Whether some s in this lane may exceed its column's threshold: the
+    // largest s of both heads against the smaller threshold (a head whose
+    // reference is still -inf sends every tile to the rare path, which checks
+    // each head on its own); 8 three-input maxima for the 16 values.
+    auto over2 = [&](const floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
+      const floatx4 &a0 = s[0][0], &a1 = s[1][0], &b0 = s[0][1], &b1 = s[1][1];
+      const float u0 = mx3(a0[0], a0[1], a0[2]), u1 = mx3(a0[3], a1[0], a1[1]);
+      const float u2 = mx3(a1[2], a1[3], b0[0]), u3 = mx3(b0[1], b0[2], b0[3]);
+      const float u4 = mx3(b1[0], b1[1], b1[2]);
+      const float v0 = mx3(u0, u1, u2), v1 = mx3(u3, u4, b1[3]);
+      return __builtin_elementwise_maximum(v0, v1) > thrm;
     };
     // the rare path: new references, rescaled O and l, shifted s
     auto rebase = [&](floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
@@ -626,6 +640,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         negoff[qb] = floatx4{-noff, -noff, -noff, -noff};
         thr[qb] = ref[qb] == -INFINITY ? -INFINITY : kTau;
       }
+      thrm = __builtin_elementwise_minimum(thr[0], thr[1]);
     };
 
     // ---- software pipeline over tiles: two phases per tile ----
@@ -688,10 +703,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       } else if (masked == 2) {
         apply_mask(j, j < n_stile ? 2 : 1, s);
       }
-      bool rare = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) rare |= over(s, qb);
-      if (__builtin_expect(__any(rare), 0)) rebase(s);
+      if (__builtin_expect(__any(over2(s)), 0)) rebase(s);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sexp(s, p, qb);
       // the empty asm keeps the exponentials in this phase
