@@ -204,8 +204,8 @@ def main():
         vc4 = torch.randn((B4, S4, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
         T = args.decode_steps
         qs = torch.randn((T, B4, Hq, D), generator=g, device=dev, dtype=torch.float32).to(bf)
-        ks = torch.randn((T, B4, 1, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
-        vs = torch.randn((T, B4, 1, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        ks = torch.randn((T, B4, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        vs = torch.randn((T, B4, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
         p0 = synth.positions(4, B4, wl4.pos_lo, wl4.pos_hi).to(torch.int64)
         pos = (p0[None, :] + torch.arange(T)[:, None]).to(torch.int32).to(dev)    # [T][B]
         o4 = torch.empty((B4, Hq, D), dtype=bf, device=dev)
@@ -218,10 +218,10 @@ def main():
         dec_bytes = kv_bytes + qo_bytes
 
         def dstep(s, ev=None):
-            swa.swa_cache_write(p4, ks[s], vs[s], pos[s], kc4, vc4)
+            # one launch: the new entry into slot(pos), then attention
             if ev is not None:
                 ev[0].record()
-            swa.swa_decode(p4, qs[s], kc4, vc4, pos[s], o4, l4, ws4)
+            swa.swa_decode_step(p4, qs[s], ks[s], vs[s], kc4, vc4, pos[s], o4, l4, ws4)
             if ev is not None:
                 ev[1].record()
 
@@ -240,22 +240,22 @@ def main():
         total_ms = t0.elapsed_time(t1)
         dec_times = sorted(a.elapsed_time(b) for a, b in evs)
         dec_ms = sum(dec_times)
-        dec_achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+        dec_achieved = (dec_bytes + write_bytes) / (dec_ms * 1e-3) / 1e9
         result["decode"] = {
             "workload": wl4.name, "batch": B4, "steps": T, "window": wl4.window,
             "value": round((dec_bytes + write_bytes) / (total_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "ms_per_step": round(total_ms / T, 4),
-            "step": "cache_write + decode (split + combine)",
+            "step": "decode_step (cache write + attention, one launch)",
             "algorithmic_bytes_per_step": round((dec_bytes + write_bytes) / T),
-            "roofline": {"bound": "hbm", "kernel": "decode_bf16_d128_g4_kernel + decode_combine_kernel",
+            "roofline": {"bound": "hbm", "kernel": "decode_bf16_d128_g4_kernel",
                          "achieved": round(dec_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(dec_achieved / PEAK_HBM_GBPS, 4),
                          "traffic": profiled_traffic("decode_bf16_d128_g4_kernel.decode_b64_w4096",
                                                      ["swa_decode.hip", "swa_device.hpp"]),
-                         "algorithmic_bytes": round(dec_bytes / T),
+                         "algorithmic_bytes": round((dec_bytes + write_bytes) / T),
                          "avg_call_ms": round(dec_ms / T, 4),
                          "median_call_ms": round(dec_times[len(dec_times) // 2], 4),
-                         "bytes": "valid K/V slots read once + Q + O"},
+                         "bytes": "valid K/V slots read once + Q + O + new k/v read and stored"},
         }
         del kc4, vc4, qs, ks, vs
 
@@ -264,6 +264,7 @@ def main():
     # ------------------------------------------------------------------
     if not args.no_context and args.only == "all":
         result["context"] = context_timings(swa, synth, torch, dev)
+        result["context"]["decode_32_layers"] = decode_layers(swa, synth, torch, dev)
 
     # ------------------------------------------------------------------
     # CPU baseline: the oracle on a bounded sample of the prefill workload
@@ -274,6 +275,66 @@ def main():
     result["host"] = {"cpu": cpu_model(), "os_cpu_count": os.cpu_count(),
                       "affinity_cpus": len(os.sched_getaffinity(0))}
     print(json.dumps(result), flush=True)
+
+
+def decode_layers(swa, synth, torch, dev, n_layers=32, tokens=16):
+    """A decode token through a stack of n_layers attention layers, each with
+    its own rolling K/V buffers (the batched-decode shape: 64 sequences,
+    window 4096, positions U[1, 32768]): per layer one swa_decode_step
+    (cache write + attention).  Reports the per-token latency of the stack
+    and the KV memory of the rolling buffers against full caches."""
+    bf = torch.bfloat16
+    wl = synth.workload(4)
+    B, Hq, Hkv, D, W = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    p = swa.make_params(B, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+    g = torch.Generator(device=dev).manual_seed(4032)
+    kcs, vcs = [], []
+    for _ in range(n_layers):
+        kcs.append(torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf))
+        vcs.append(torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf))
+    qs = torch.randn((n_layers, B, Hq, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    ks = torch.randn((n_layers, B, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    vs = torch.randn((n_layers, B, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    p0 = synth.positions(4, B, wl.pos_lo, wl.pos_hi).to(torch.int64)
+    pos = (p0[None, :] + torch.arange(tokens + 4)[:, None]).to(torch.int32).to(dev)
+    out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(swa.swa_decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+
+    def token(t):
+        for layer in range(n_layers):
+            swa.swa_decode_step(p, qs[layer], ks[layer], vs[layer], kcs[layer], vcs[layer], pos[t],
+                                out, lse, ws)
+
+    for t in range(4):
+        token(t)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for t in range(4, 4 + tokens):
+        token(t)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / tokens
+    slot_bytes = Hkv * D * 2 * 2                      # K and V of one position, one layer
+    read = sum(min(int(x) + 1, W) for x in pos[4:4 + tokens].cpu().flatten()) * slot_bytes * n_layers
+    moved = read / tokens + n_layers * B * (Hq * D * 2 * 2 + Hkv * D * 2 * 2 * 2)
+    rolling = n_layers * B * W * slot_bytes
+    full_now = n_layers * sum(int(x) + 1 for x in pos[3 + tokens].cpu()) * slot_bytes
+    full_32k = n_layers * B * 32768 * slot_bytes
+    res = {
+        "workload": f"decode_b{B}_w{W}_x{n_layers}_layers", "layers": n_layers, "tokens": tokens,
+        "ms_per_token": round(ms, 4), "ms_per_layer": round(ms / n_layers, 4),
+        "gbps": round(moved / (ms * 1e-3) / 1e9, 1),
+        "step": "per layer one decode_step (cache write + attention)",
+        "kv_bytes_rolling": rolling,
+        "kv_bytes_full_cache_at_current_positions": full_now,
+        "kv_bytes_full_cache_at_32k": full_32k,
+        "full_32k_over_rolling": round(full_32k / rolling, 3),
+    }
+    del kcs, vcs
+    return res
 
 
 def context_timings(swa, synth, torch, dev):
@@ -349,8 +410,8 @@ def context_timings(swa, synth, torch, dev):
     vc5 = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(bf)
     T = 256
     qs5 = torch.randn((T, B, Hq, D), generator=g, device=dev).to(bf)
-    ks5 = torch.randn((T, B, 1, Hkv, D), generator=g, device=dev).to(bf)
-    vs5 = torch.randn((T, B, 1, Hkv, D), generator=g, device=dev).to(bf)
+    ks5 = torch.randn((T, B, Hkv, D), generator=g, device=dev).to(bf)
+    vs5 = torch.randn((T, B, Hkv, D), generator=g, device=dev).to(bf)
     p0 = synth.positions(5, B, wl5.pos_lo, wl5.pos_hi).to(torch.int64)
     pos = (p0[None, :] + torch.arange(T)[:, None]).to(torch.int32).to(dev)
     o5 = torch.empty((B, Hq, D), dtype=bf, device=dev)
@@ -359,24 +420,24 @@ def context_timings(swa, synth, torch, dev):
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
 
     def run5(flush_each):
-        tot = 0.0
+        # flushed: a 512 MiB fill before each step; warm: the steps back to back
+        evs = []
         for s in range(T):
             if flush_each:
                 flush.fill_(s & 255)
-            swa.swa_cache_write(p5, ks5[s], vs5[s], pos[s], kc5, vc5)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
-            swa.swa_decode(p5, qs5[s], kc5, vc5, pos[s], o5, l5, ws5)
+            swa.swa_decode_step(p5, qs5[s], ks5[s], vs5[s], kc5, vc5, pos[s], o5, l5, ws5)
             b.record()
-            torch.cuda.synchronize()
-            tot += a.elapsed_time(b)
-        return tot / T
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / T
 
     run5(False)
     ms_flushed = run5(True)
     ms_warm = run5(False)
-    bytes5 = B * S * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2
+    bytes5 = B * S * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2 + B * Hkv * D * 2 * 2 * 2
     # sink workload's prefill chunk: one 4096-token chunk per sequence after
     # the decode steps, against the rolling cache with its 4 sink slots
     C5 = wl5.chunk
@@ -401,6 +462,7 @@ def context_timings(swa, synth, torch, dev):
     }
     ctx["sink_decode"] = {
         "workload": wl5.name, "bytes_per_step": bytes5,
+        "step": "decode_step (cache write + split attention + combine)",
         "ms_per_decode_mall_flushed": round(ms_flushed, 4),
         "gbps_mall_flushed": round(bytes5 / (ms_flushed * 1e-3) / 1e9, 1),
         "ms_per_decode_warm": round(ms_warm, 4),

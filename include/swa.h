@@ -182,6 +182,29 @@ int swa_decode(const swa_params* params, const void* q, const void* k_cache, con
                const int32_t* pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
 
+/*
+ * swa_decode_step — a whole decode step per sequence: store the new token's
+ * entry, then attend.  Digest "쓰기(write) 단계" then "읽기(read) 단계": the
+ * key/value of position pos[b] go to slot(pos[b]) (the key rotated at
+ * pos[b]), and the query at pos[b] reads positions pos[b]-W+1 .. pos[b]
+ * (plus sinks), the new entry included.  The result, and the cache contents
+ * afterwards, are those of swa_cache_write (n_tok = 1) followed by
+ * swa_decode.  With bf16, head_dim 128 and 4 query heads per KV head this is
+ * one launch (plus the combine when the slots are split over several
+ * ranges): the work-group whose slot range holds slot(pos[b]) stores the
+ * entry before it streams its range.  Other shapes run the two calls.
+ *   q       : [batch][n_q_heads][head_dim] raw queries.
+ *   k, v    : [batch][n_kv_heads][head_dim] raw new key / value of the token
+ *             at pos[b] (the key is rotated here, the value stored as is).
+ *   k_cache, v_cache : [batch][n_sink + window][n_kv_heads][head_dim],
+ *             read and written (slot(pos[b]) of each sequence).
+ *   pos, out, lse, workspace : as swa_decode (same workspace size).
+ * Errors as swa_decode; nothing is launched when an argument is rejected.
+ */
+int swa_decode_step(const swa_params* params, const void* q, const void* k, const void* v,
+                    void* k_cache, void* v_cache, const int32_t* pos, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a swa_status value. */
 const char* swa_status_string(int status);
 

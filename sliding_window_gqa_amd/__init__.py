@@ -14,7 +14,7 @@ import os
 __all__ = [
     "SwaError", "swa_params", "make_params", "library", "LIB_PATH",
     "swa_cache_write", "swa_prefill_chunk", "swa_prefill_workspace_bytes",
-    "swa_decode", "swa_decode_workspace_bytes", "swa_status_string",
+    "swa_decode", "swa_decode_step", "swa_decode_workspace_bytes", "swa_status_string",
     "swa_rope_keys", "swa_prefill_attention",
     "swa_debug_slots", "swa_debug_mask",
     "SWA_OK", "SWA_ERR_NULL", "SWA_ERR_SHAPE", "SWA_ERR_DTYPE", "SWA_ERR_UNSUPPORTED",
@@ -61,6 +61,7 @@ _SIGNATURES = {
     "swa_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "swa_decode_workspace_bytes": (_sz, [_P]),
     "swa_decode": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "swa_decode_step": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "swa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "swa_debug_slots": (ctypes.c_int, [_P, _vp, _i32, _vp, _vp]),
     "swa_debug_mask": (ctypes.c_int, [_P, _i32, _vp, _i32, _vp, _vp]),
@@ -252,6 +253,32 @@ def swa_decode(params, q, k_cache, v_cache, pos, out=None, lse=None, workspace=N
         _ptr(out, "out", dt, qshp), _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads)),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "swa_decode")
+    return out, lse
+
+
+def swa_decode_step(params, q, k, v, k_cache, v_cache, pos, out=None, lse=None, workspace=None,
+                    want_lse=True, stream=None):
+    """One whole decode step per sequence: stores the new token's k/v
+    ([B][Hkv][D], raw) at slot(pos[b]) of the caches, then attends; returns
+    (out, lse)."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    qshp = (params.batch, params.n_q_heads, params.head_dim)
+    kshp = (params.batch, params.n_kv_heads, params.head_dim)
+    cshp = (params.batch, params.n_sink + params.window, params.n_kv_heads, params.head_dim)
+    if out is None:
+        out = torch.empty(qshp, dtype=dt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((params.batch, params.n_q_heads), dtype=torch.float32, device=q.device)
+    need = swa_decode_workspace_bytes(params)
+    workspace = _workspace(need, q.device, workspace)
+    st = library().swa_decode_step(
+        ctypes.byref(params), _ptr(q, "q", dt, qshp), _ptr(k, "k", dt, kshp), _ptr(v, "v", dt, kshp),
+        _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp),
+        _ptr(pos, "pos", torch.int32, (params.batch,)),
+        _ptr(out, "out", dt, qshp), _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads)),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "swa_decode_step")
     return out, lse
 
 

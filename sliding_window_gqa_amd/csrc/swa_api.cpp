@@ -68,6 +68,27 @@ bool fast_prefill(const swa_params* p, int32_t chunk_len) {
 
 int launched(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
 
+// Split-K decode (+ combine when there are several ranges); with fw the fast
+// kernel also stores the new entry first.  Arguments are already checked.
+int decode_launch(const swa_params* params, const Shape& sh, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* pos, void* out, float* lse,
+                  void* workspace, const swa::FusedWrite* fw, hipStream_t stream) {
+  const int n = swa::decode_splits(sh);
+  const RopeTab rt = rope_table(params);
+  const bool f32 = params->dtype == SWA_F32;
+  float* part = static_cast<float*>(workspace);
+  hipError_t e;
+  if (fast_path(params)) {
+    e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, out, lse, fw,
+                                        stream);
+    if (n == 1) return launched(e);   // the kernel wrote out and lse
+  } else {
+    e = swa::launch_decode_generic(sh, rt, f32, q, k_cache, v_cache, pos, part, n, stream);
+  }
+  if (e != hipSuccess) return SWA_ERR_LAUNCH;
+  return launched(swa::launch_decode_combine(sh, f32, part, n, out, lse, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,19 +181,27 @@ int swa_decode(const swa_params* params, const void* q, const void* k_cache, con
   if (!q || !k_cache || !v_cache || !pos || !out) return SWA_ERR_NULL;
   const size_t need = swa_decode_workspace_bytes(params);
   if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
-  const int n = swa::decode_splits(sh);
-  const RopeTab rt = rope_table(params);
-  const bool f32 = params->dtype == SWA_F32;
-  float* part = static_cast<float*>(workspace);
-  hipError_t e;
+  return decode_launch(params, sh, q, k_cache, v_cache, pos, out, lse, workspace, nullptr, stream);
+}
+
+int swa_decode_step(const swa_params* params, const void* q, const void* k, const void* v,
+                    void* k_cache, void* v_cache, const int32_t* pos, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k || !v || !k_cache || !v_cache || !pos || !out) return SWA_ERR_NULL;
+  const size_t need = swa_decode_workspace_bytes(params);
+  if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
   if (fast_path(params)) {
-    e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, out, lse, stream);
-    if (n == 1) return launched(e);   // the kernel wrote out and lse
-  } else {
-    e = swa::launch_decode_generic(sh, rt, f32, q, k_cache, v_cache, pos, part, n, stream);
+    const swa::FusedWrite fw{k, v, k_cache, v_cache};
+    return decode_launch(params, sh, q, k_cache, v_cache, pos, out, lse, workspace, &fw, stream);
   }
+  // other shapes: the cache write, then the decode, on the same stream
+  hipError_t e = swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k, v, pos,
+                                         1, k_cache, v_cache, swa::kToCache, stream);
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
-  return launched(swa::launch_decode_combine(sh, f32, part, n, out, lse, stream));
+  return decode_launch(params, sh, q, k_cache, v_cache, pos, out, lse, workspace, nullptr, stream);
 }
 
 const char* swa_status_string(int status) {

@@ -69,6 +69,12 @@ struct DecodeArgs {
   int split_len;
   uint16_t* out;   // written directly (normalised) when n_splits == 1
   float* lse;
+  // fused step: the new token's raw key and value [B][Hkv][D] (knew null
+  // when there is none) and the caches to store them in (the ones read)
+  const uint16_t* knew;
+  const uint16_t* vnew;
+  uint16_t* kdst;
+  uint16_t* vdst;
 };
 
 // K chunks in LDS: 32 rows of 256 bytes, the 16-byte chunk c of row r at
@@ -131,6 +137,41 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
   if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
   __syncthreads();
+
+  // ---- fused step: the range that holds slot(p) first stores the new entry
+  // of this head (key rotated at p, as the cache write does it; value as
+  // is).  No other work-group reads that slot.  The stores complete before
+  // the barrier, so every load of the work-group issued after it sees them.
+  if (a.knew != nullptr) {
+    const int slot = slot_of(p, sh.W, sh.n_sink);
+    if (slot >= sp0 && slot < sp0 + a.split_len) {
+      if (tid < 32) {
+        const int c = tid & 15;   // 16-byte chunk: head-dim elements 8c .. 8c+7
+        const long long src = ((long long)b * sh.Hkv + kvh) * HD + 8 * c;
+        const long long dst = ((long long)b * S + slot) * row_stride + kvh * HD + 8 * c;
+        if (tid < 16) {
+          const u32x4 wk = *reinterpret_cast<const u32x4*>(a.knew + src);
+          u32x4 r;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            float x0 = bf16_lo(wk[jj]), x1 = bf16_hi(wk[jj]);
+            if (sh.rope) {
+              float cs, sn;
+              rope_cs(p, rope_rev[4 * c + jj], cs, sn);
+              rotate(x0, x1, cs, sn);
+            }
+            r[jj] = pack_bf16(x0, x1);
+          }
+          *reinterpret_cast<u32x4*>(a.kdst + dst) = r;
+        } else {
+          *reinterpret_cast<u32x4*>(a.vdst + dst) =
+              *reinterpret_cast<const u32x4*>(a.vnew + src);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  }
   bf16x8 qf[4];
   auto load_q = [&]() __attribute__((always_inline)) {
     // (all four loads go out before the first is used; lanes i >= 4 load a
@@ -476,7 +517,7 @@ static int split_len_of(const Shape& sh, int n_splits) {
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
                                       float* partial, int n_splits, void* out, float* lse,
-                                      hipStream_t st) {
+                                      const FusedWrite* fw, hipStream_t st) {
   DecodeArgs a;
   a.sh = sh;
   a.rt = rt;
@@ -489,6 +530,10 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
   a.split_len = split_len_of(sh, n_splits);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.knew = fw ? static_cast<const uint16_t*>(fw->k) : nullptr;
+  a.vnew = fw ? static_cast<const uint16_t*>(fw->v) : nullptr;
+  a.kdst = fw ? static_cast<uint16_t*>(fw->k_cache) : nullptr;
+  a.vdst = fw ? static_cast<uint16_t*>(fw->v_cache) : nullptr;
   decode_bf16_d128_g4_kernel<<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }

@@ -33,11 +33,19 @@ hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, 
 
 // Split-K decode.  Partials: [B][Hq][n_splits][D + 2] float.  The fast
 // kernel writes out and lse itself when n_splits == 1 (no combine pass).
+// With a FusedWrite it first stores the new token's entry (raw k, v:
+// [B][Hkv][D]) into k_cache / v_cache (the caches it reads) at slot(pos).
+struct FusedWrite {
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+};
 int decode_splits(const Shape& sh);
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
                                       float* partial, int n_splits, void* out, float* lse,
-                                      hipStream_t st);
+                                      const FusedWrite* fw, hipStream_t st);
 hipError_t launch_decode_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
                                  const void* kc, const void* vc, const int32_t* pos,
                                  float* partial, int n_splits, hipStream_t st);

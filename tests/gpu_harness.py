@@ -46,10 +46,13 @@ class GpuSide:
         self.has_cache = True
         return out, lse
 
-    def decode(self, q, k, v, pos):
+    def decode(self, q, k, v, pos, fused=False):
+        """Cache write + decode: two calls, or the one-call swa_decode_step."""
         st = torch.as_tensor(pos, dtype=torch.int32).to(DEV)
-        swa.swa_cache_write(self.p, k.to(DEV)[:, None], v.to(DEV)[:, None], st, self.kc, self.vc)
         self.has_cache = True
+        if fused:
+            return swa.swa_decode_step(self.p, q.to(DEV), k.to(DEV), v.to(DEV), self.kc, self.vc, st)
+        swa.swa_cache_write(self.p, k.to(DEV)[:, None], v.to(DEV)[:, None], st, self.kc, self.vc)
         return swa.swa_decode(self.p, q.to(DEV), self.kc, self.vc, st)
 
 

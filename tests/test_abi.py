@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert {"swa_cache_write", "swa_prefill_chunk", "swa_decode", "swa_decode_workspace_bytes",
+    assert {"swa_cache_write", "swa_prefill_chunk", "swa_decode", "swa_decode_step",
+            "swa_decode_workspace_bytes",
             "swa_rope_keys", "swa_prefill_attention",
             "swa_prefill_workspace_bytes", "swa_status_string", "swa_debug_slots",
             "swa_debug_mask"} <= set(names)
@@ -64,6 +65,7 @@ def test_bad_params_rejected_everywhere(bad, code):
     assert lib.swa_cache_write(bp, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == code
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
+    assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_debug_slots(bp, FAKE, 4, FAKE, None) == code
     assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, FAKE, None) == code
     assert lib.swa_prefill_attention(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None) == code
@@ -82,6 +84,10 @@ def test_null_pointers_rejected():
     # exactly one cache pointer given
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
+    for i in range(7):   # q, k, v, k_cache, v_cache, pos, out
+        args = [FAKE] * 7
+        args[i] = None
+        assert lib.swa_decode_step(bp, *args, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL, i
     assert lib.swa_debug_mask(bp, 5, None, 4, FAKE, None) == swa.SWA_ERR_NULL
     assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, None, None) == swa.SWA_ERR_NULL
     assert lib.swa_prefill_attention(bp, FAKE, None, FAKE, None, None, FAKE, 16, FAKE, None, None) == swa.SWA_ERR_NULL
@@ -99,6 +105,8 @@ def test_sizes_and_workspace_rejected():
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None, need, None) == swa.SWA_ERR_WORKSPACE
     dneed = lib.swa_decode_workspace_bytes(bp)
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE
+    assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE
+    assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, dneed, None) == swa.SWA_ERR_WORKSPACE
     assert lib.swa_debug_slots(bp, FAKE, 0, FAKE, None) == swa.SWA_ERR_SHAPE
     assert lib.swa_debug_mask(bp, -1, FAKE, 4, FAKE, None) == swa.SWA_ERR_SHAPE
 

@@ -224,6 +224,52 @@ def test_decode_steps(case):
             assert_lse(lse[b], ref[b][1], latol, f"step {st} seq {b} lse")
 
 
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}{str(c[6])[6:]}" for c in DECODE_CASES])
+def test_decode_step_fused(case):
+    """swa_decode_step against the oracle, and bit for bit against the cache
+    write + decode pair it replaces (outputs, LSE and both caches), from the
+    first position through the buffer's wrap."""
+    B, Hq, Hkv, D, W, S, dtype = case
+    print(f"fused decode step {case}", flush=True)
+    theta = 10000.0
+    one = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype)
+    two = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta)
+    atol, rrms, latol = tol(dtype)
+    p0 = [0, 40, 5][:B] if W < 1000 else [4090, 0][:B]
+    steps = 120 if W < 1000 else 12
+    for st in range(steps):
+        q = rnd((B, Hq, D), "step_q", st, dtype, index=91)
+        k = rnd((B, Hkv, D), "step_k", st, dtype, index=91)
+        v = rnd((B, Hkv, D), "step_v", st, dtype, index=91)
+        pos = [p0[b] + st for b in range(B)]
+        if st == 0:   # earlier positions of the sequences that do not start at 0
+            for b in range(B):
+                if p0[b] == 0:
+                    continue
+                kh = rnd((1, p0[b], Hkv, D), "hist_k", b, dtype, index=91)
+                vh = rnd((1, p0[b], Hkv, D), "hist_v", b, dtype, index=91)
+                for side in (one, two):
+                    sub = GpuSide(1, Hq, Hkv, D, W, S, theta, dtype)
+                    sub.write(kh, vh, [0])
+                    side.kc[b] = sub.kc[0]
+                    side.vc[b] = sub.vc[0]
+                orc.caches[b].write(so.rope(np64(kh[0]), np.arange(p0[b]), theta), np64(vh[0]), np.arange(p0[b]))
+        o1, l1 = one.decode(q, k, v, pos, fused=True)
+        o2, l2 = two.decode(q, k, v, pos)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"step {st}: fused and two-call results differ"
+        # as bytes: slots never written hold the same NaN fill on both sides
+        assert torch.equal(one.kc.view(torch.uint8), two.kc.view(torch.uint8)), f"step {st} k cache"
+        assert torch.equal(one.vc.view(torch.uint8), two.vc.view(torch.uint8)), f"step {st} v cache"
+        if st % 7 == 0 or st == steps - 1:
+            ref = orc.decode(q, k, v, pos)
+            for b in range(B):
+                assert_close(o1[b], ref[b][0], atol, rrms, f"step {st} seq {b} out")
+                assert_lse(l1[b], ref[b][1], latol, f"step {st} seq {b} lse")
+        else:
+            orc.decode(q, k, v, pos, compute=False)
+
+
 def test_decode_key_counts_exact():
     print("decode key counts", flush=True)
     B, Hq, Hkv, D, W, S = 3, 8, 2, 128, 100, 3
