@@ -265,6 +265,7 @@ def main():
     if not args.no_context and args.only == "all":
         result["context"] = context_timings(swa, synth, torch, dev)
         result["context"]["decode_32_layers"] = decode_layers(swa, synth, torch, dev)
+        result["context"]["varlen_mixed_batch"] = varlen_mixed(swa, synth, torch, dev)
 
     # ------------------------------------------------------------------
     # CPU baseline: the oracle on a bounded sample of the prefill workload
@@ -334,6 +335,77 @@ def decode_layers(swa, synth, torch, dev, n_layers=32, tokens=16):
         "full_32k_over_rolling": round(full_32k / rolling, 3),
     }
     del kcs, vcs
+    return res
+
+
+def varlen_mixed(swa, synth, torch, dev, n_prefill=4, chunk=1024, reps=10):
+    """One step of a mixed batch of 64 sequences at the batched-decode shape
+    (window 4096, full windows): n_prefill sequences prefill a chunk of
+    `chunk` tokens, the others decode one token.  As one varlen call (key
+    rotation + attention, then the cache write) against the fixed-length
+    calls it replaces (prefill chunk + cache write, then decode steps)."""
+    bf = torch.bfloat16
+    wl = synth.workload(4)
+    B, Hq, Hkv, D, W = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    nd = B - n_prefill
+    lens = [chunk] * n_prefill + [1] * nd
+    T = sum(lens)
+    p = swa.make_params(B, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+    pp = swa.make_params(n_prefill, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+    pd = swa.make_params(nd, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+    g = torch.Generator(device=dev).manual_seed(4064)
+    kc = torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    vc = torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    q = torch.randn((T, Hq, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    k = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    v = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+    st = synth.positions(4, B, W, 32768).to(torch.int32).to(dev)   # every window full
+    out = torch.empty((T, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(swa.swa_prefill_varlen_workspace_bytes(p, lens), dtype=torch.uint8, device=dev)
+    P = n_prefill * chunk
+    qp, kp, vp = (x[:P].reshape(n_prefill, chunk, *x.shape[1:]) for x in (q, k, v))
+    qd, kd, vd = q[P:], k[P:], v[P:]
+    outp = torch.empty((n_prefill, chunk, Hq, D), dtype=bf, device=dev)
+    lsep = torch.empty((n_prefill, Hq, chunk), dtype=torch.float32, device=dev)
+    wsp = torch.empty(swa.swa_prefill_workspace_bytes(pp, chunk), dtype=torch.uint8, device=dev)
+    outd = torch.empty((nd, Hq, D), dtype=bf, device=dev)
+    lsed = torch.empty((nd, Hq), dtype=torch.float32, device=dev)
+    wsd = torch.empty(swa.swa_decode_workspace_bytes(pd), dtype=torch.uint8, device=dev)
+
+    def one_call():
+        swa.swa_prefill_chunk_varlen(p, q, k, v, kc, vc, st, lens, out, lse, ws)
+        swa.swa_cache_write_varlen(p, k, v, st, lens, kc, vc)
+
+    def separate():
+        swa.swa_prefill_chunk(pp, qp, kp, vp, kc[:n_prefill], vc[:n_prefill], st[:n_prefill], outp, lsep, wsp)
+        swa.swa_cache_write(pp, kp, vp, st[:n_prefill], kc[:n_prefill], vc[:n_prefill])
+        swa.swa_decode_step(pd, qd, kd, vd, kc[n_prefill:], vc[n_prefill:], st[n_prefill:], outd, lsed, wsd)
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms_one = timeit(one_call)
+    ms_sep = timeit(separate)
+    pairs = n_prefill * chunk * W + nd * W
+    res = {
+        "workload": f"mixed_b{B}_{n_prefill}x{chunk}_prefill_{nd}_decode_w{W}",
+        "lens": f"{n_prefill} x {chunk} + {nd} x 1", "tokens": T,
+        "ms_varlen_one_call": round(ms_one, 4), "ms_fixed_length_calls": round(ms_sep, 4),
+        "tflops_varlen": round(attn_flops(pairs) / (ms_one * 1e-3) / 1e12, 1),
+        "step": "prefill_chunk_varlen + cache_write_varlen vs prefill_chunk + cache_write + decode_step",
+    }
+    del kc, vc
     return res
 
 

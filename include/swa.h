@@ -160,6 +160,41 @@ int swa_prefill_attention(const swa_params* params, const void* q, const void* k
                           const int32_t* start_pos, int32_t chunk_len, void* out, float* lse,
                           hipStream_t stream);
 
+/*
+ * Varlen (ragged) batches: each sequence brings its own chunk length.
+ * Essay §4.1 and digest "Pre-fill과의 상호작용": the chunk size is a free
+ * choice, so the sequences of one batch may each prefill a different number
+ * of tokens, and a sequence that decodes one token is a chunk of length 1.
+ *   chunk_lens : HOST int32[batch], chunk_lens[b] in 0 .. 2^24 (0: the
+ *                sequence takes no part), at least one token in all;
+ *                total = sum of chunk_lens.
+ *   q, out     : [total][n_q_heads][head_dim], k, v, k_rot :
+ *                [total][n_kv_heads][head_dim]: the sequences packed one
+ *                after the other in batch order (sequence b at rows
+ *                chunk_lens[0] + .. + chunk_lens[b-1] onwards).
+ *   lse        : float32 [n_q_heads][total], or NULL.
+ *   start_pos, k_cache, v_cache : as in the calls above, per sequence.
+ * Every other rule is that of the fixed-length call of the same name: the
+ * result for sequence b is what that call gives with batch 1, chunk_len =
+ * chunk_lens[b].  Errors as there, and SWA_ERR_SHAPE for a length out of
+ * range or an empty batch; SWA_ERR_NULL when chunk_lens is NULL.  Up to 64
+ * sequences go to one launch (more take several, on the same stream).
+ */
+size_t swa_prefill_varlen_workspace_bytes(const swa_params* params, const int32_t* chunk_lens);
+int swa_rope_keys_varlen(const swa_params* params, const void* k, const int32_t* start_pos,
+                         const int32_t* chunk_lens, void* k_rot, hipStream_t stream);
+int swa_prefill_attention_varlen(const swa_params* params, const void* q, const void* k_rot,
+                                 const void* v, const void* k_cache, const void* v_cache,
+                                 const int32_t* start_pos, const int32_t* chunk_lens, void* out,
+                                 float* lse, hipStream_t stream);
+int swa_prefill_chunk_varlen(const swa_params* params, const void* q, const void* k, const void* v,
+                             const void* k_cache, const void* v_cache, const int32_t* start_pos,
+                             const int32_t* chunk_lens, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+int swa_cache_write_varlen(const swa_params* params, const void* k, const void* v,
+                           const int32_t* start_pos, const int32_t* chunk_lens, void* k_cache,
+                           void* v_cache, hipStream_t stream);
+
 /* Bytes of workspace swa_decode needs (split-K partial results). */
 size_t swa_decode_workspace_bytes(const swa_params* params);
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/swa.h"
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
@@ -68,6 +70,54 @@ bool fast_prefill(const swa_params* p, int32_t chunk_len) {
 
 int launched(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
 
+// Varlen batches: chunk_lens is a host array of batch lengths (each 0 ..
+// 2^24, at least one token in all); the sequences are packed one after the
+// other.  The total and the longest length are returned.
+int check_lens(const swa_params* p, const int32_t* lens, long long* total, int* longest) {
+  if (!lens) return SWA_ERR_NULL;
+  long long t = 0;
+  int mx = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    if (lens[b] < 0 || lens[b] > (1 << 24)) return SWA_ERR_SHAPE;
+    t += lens[b];
+    if (lens[b] > mx) mx = lens[b];
+  }
+  if (t < 1 || t > (1LL << 30)) return SWA_ERR_SHAPE;
+  *total = t;
+  *longest = mx;
+  return SWA_OK;
+}
+
+// Runs f(first sequence, VarTab, first row, longest length, group shape) for
+// each run of at most kVarMax sequences that holds any token.
+template <class F>
+int for_var_groups(const Shape& sh, const int32_t* lens, long long total, F&& f) {
+  long long row = 0;
+  for (int g0 = 0; g0 < sh.B; g0 += swa::kVarMax) {
+    swa::VarTab vt{};
+    vt.n = sh.B - g0 < swa::kVarMax ? sh.B - g0 : swa::kVarMax;
+    vt.total = (int)total;
+    int mx = 0;
+    for (int j = 0; j < vt.n; ++j) {
+      vt.row_off[j + 1] = vt.row_off[j] + lens[g0 + j];
+      if (lens[g0 + j] > mx) mx = lens[g0 + j];
+    }
+    if (vt.row_off[vt.n] > 0) {
+      Shape gs = sh;
+      gs.B = vt.n;
+      if (f(g0, vt, row, mx, gs) != hipSuccess) return SWA_ERR_LAUNCH;
+    }
+    row += vt.row_off[vt.n];
+  }
+  return SWA_OK;
+}
+
+template <class T>
+T* rows_at(T* p, long long rows, long long row_elems, size_t es) {
+  using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+  return p ? (T*)((B*)p + rows * row_elems * (long long)es) : nullptr;
+}
+
 // Split-K decode (+ combine when there are several ranges); with fw the fast
 // kernel also stores the new entry first.  Arguments are already checked.
 int decode_launch(const swa_params* params, const Shape& sh, const void* q, const void* k_cache,
@@ -104,7 +154,7 @@ int swa_cache_write(const swa_params* params, const void* k, const void* v,
   if ((long long)sh.B * n_tok * sh.Hkv * (sh.D / 8) >= (1LL << 40)) return SWA_ERR_SHAPE;
   return launched(swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k, v,
                                           start_pos, n_tok, k_cache, v_cache, swa::kToCache,
-                                          stream));
+                                          nullptr, stream));
 }
 
 size_t swa_prefill_workspace_bytes(const swa_params* params, int32_t chunk_len) {
@@ -122,7 +172,7 @@ int swa_rope_keys(const swa_params* params, const void* k, const int32_t* start_
   if (n_tok < 1 || n_tok > (1 << 24)) return SWA_ERR_SHAPE;
   return launched(swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k,
                                           nullptr, start_pos, n_tok, k_rot, nullptr,
-                                          swa::kToDense, stream));
+                                          swa::kToDense, nullptr, stream));
 }
 
 int swa_prefill_attention(const swa_params* params, const void* q, const void* k_rot,
@@ -139,10 +189,10 @@ int swa_prefill_attention(const swa_params* params, const void* q, const void* k
   hipError_t e;
   if (fast_prefill(params, chunk_len))
     e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, k_rot, v, k_cache, v_cache, start_pos,
-                                         chunk_len, out, lse, stream);
+                                         chunk_len, out, lse, nullptr, stream);
   else
     e = swa::launch_prefill_generic(sh, rt, params->dtype == SWA_F32, q, k_rot, v, k_cache,
-                                    v_cache, start_pos, chunk_len, out, lse, stream);
+                                    v_cache, start_pos, chunk_len, out, lse, nullptr, stream);
   return launched(e);
 }
 
@@ -199,9 +249,119 @@ int swa_decode_step(const swa_params* params, const void* q, const void* k, cons
   }
   // other shapes: the cache write, then the decode, on the same stream
   hipError_t e = swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k, v, pos,
-                                         1, k_cache, v_cache, swa::kToCache, stream);
+                                         1, k_cache, v_cache, swa::kToCache, nullptr, stream);
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
   return decode_launch(params, sh, q, k_cache, v_cache, pos, out, lse, workspace, nullptr, stream);
+}
+
+size_t swa_prefill_varlen_workspace_bytes(const swa_params* params, const int32_t* chunk_lens) {
+  long long total;
+  int longest;
+  if (check_params(params, nullptr) != SWA_OK) return 0;
+  if (check_lens(params, chunk_lens, &total, &longest) != SWA_OK) return 0;
+  return (size_t)total * params->n_kv_heads * params->head_dim * elem_size(params->dtype);
+}
+
+int swa_rope_keys_varlen(const swa_params* params, const void* k, const int32_t* start_pos,
+                         const int32_t* chunk_lens, void* k_rot, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k || !start_pos || !k_rot) return SWA_ERR_NULL;
+  long long total;
+  int longest;
+  st = check_lens(params, chunk_lens, &total, &longest);
+  if (st != SWA_OK) return st;
+  const RopeTab rt = rope_table(params);
+  const bool f32 = params->dtype == SWA_F32;
+  const size_t es = elem_size(params->dtype);
+  const long long kv_row = (long long)sh.Hkv * sh.D;
+  return for_var_groups(sh, chunk_lens, total, [&](int g0, const swa::VarTab& vt, long long row, int mx,
+                                                   const Shape& gs) {
+    return swa::launch_cache_write(gs, rt, f32, rows_at(k, row, kv_row, es), nullptr, start_pos + g0,
+                                   mx, rows_at(k_rot, row, kv_row, es), nullptr, swa::kToDense, &vt,
+                                   stream);
+  });
+}
+
+int swa_cache_write_varlen(const swa_params* params, const void* k, const void* v,
+                           const int32_t* start_pos, const int32_t* chunk_lens, void* k_cache,
+                           void* v_cache, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k || !v || !start_pos || !k_cache || !v_cache) return SWA_ERR_NULL;
+  long long total;
+  int longest;
+  st = check_lens(params, chunk_lens, &total, &longest);
+  if (st != SWA_OK) return st;
+  const RopeTab rt = rope_table(params);
+  const bool f32 = params->dtype == SWA_F32;
+  const size_t es = elem_size(params->dtype);
+  const long long kv_row = (long long)sh.Hkv * sh.D;
+  return for_var_groups(sh, chunk_lens, total, [&](int g0, const swa::VarTab& vt, long long row, int mx,
+                                                   const Shape& gs) {
+    return swa::launch_cache_write(gs, rt, f32, rows_at(k, row, kv_row, es), rows_at(v, row, kv_row, es),
+                                   start_pos + g0, mx, rows_at(k_cache, (long long)g0 * sh.S, kv_row, es),
+                                   rows_at(v_cache, (long long)g0 * sh.S, kv_row, es), swa::kToCache,
+                                   &vt, stream);
+  });
+}
+
+int swa_prefill_attention_varlen(const swa_params* params, const void* q, const void* k_rot,
+                                 const void* v, const void* k_cache, const void* v_cache,
+                                 const int32_t* start_pos, const int32_t* chunk_lens, void* out,
+                                 float* lse, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k_rot || !v || !start_pos || !out) return SWA_ERR_NULL;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return SWA_ERR_NULL;
+  long long total;
+  int longest;
+  st = check_lens(params, chunk_lens, &total, &longest);
+  if (st != SWA_OK) return st;
+  const RopeTab rt = rope_table(params);
+  const bool f32 = params->dtype == SWA_F32;
+  const bool fast = fast_prefill(params, longest);
+  const size_t es = elem_size(params->dtype);
+  const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
+  return for_var_groups(sh, chunk_lens, total, [&](int g0, const swa::VarTab& vt, long long row, int mx,
+                                                   const Shape& gs) {
+    const void* qg = rows_at(q, row, q_row, es);
+    const void* kg = rows_at(k_rot, row, kv_row, es);
+    const void* vg = rows_at(v, row, kv_row, es);
+    const void* kcg = rows_at(k_cache, (long long)g0 * sh.S, kv_row, es);
+    const void* vcg = rows_at(v_cache, (long long)g0 * sh.S, kv_row, es);
+    void* og = rows_at(out, row, q_row, es);
+    float* lg = lse ? lse + row : nullptr;   // [Hq][total]: this run's columns
+    if (fast)
+      return swa::launch_prefill_bf16_d128_g4(gs, rt, qg, kg, vg, kcg, vcg, start_pos + g0, mx, og, lg,
+                                              &vt, stream);
+    return swa::launch_prefill_generic(gs, rt, f32, qg, kg, vg, kcg, vcg, start_pos + g0, mx, og, lg,
+                                       &vt, stream);
+  });
+}
+
+int swa_prefill_chunk_varlen(const swa_params* params, const void* q, const void* k, const void* v,
+                             const void* k_cache, const void* v_cache, const int32_t* start_pos,
+                             const int32_t* chunk_lens, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k || !v || !start_pos || !out) return SWA_ERR_NULL;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return SWA_ERR_NULL;
+  long long total;
+  int longest;
+  st = check_lens(params, chunk_lens, &total, &longest);
+  if (st != SWA_OK) return st;
+  if (!workspace || workspace_bytes < swa_prefill_varlen_workspace_bytes(params, chunk_lens))
+    return SWA_ERR_WORKSPACE;
+  st = swa_rope_keys_varlen(params, k, start_pos, chunk_lens, workspace, stream);
+  if (st != SWA_OK) return st;
+  return swa_prefill_attention_varlen(params, q, workspace, v, k_cache, v_cache, start_pos,
+                                      chunk_lens, out, lse, stream);
 }
 
 const char* swa_status_string(int status) {

@@ -15,21 +15,35 @@ enum WriteMode {
   kToDense = 1,  // rotated K into a dense [B][n_tok][Hkv][D] buffer (V untouched)
 };
 
+// Sequences of different chunk lengths, packed one after the other (rows of
+// sequence j: row_off[j] .. row_off[j+1]-1), at most kVarMax per launch.
+// With a VarTab the launchers below take n_tok / C as the longest length,
+// sh.B as the number of sequences, and every pointer at the launch's first
+// sequence; LSE rows are then [head][total] with total the row count of the
+// whole packed batch.
+constexpr int kVarMax = 64;
+struct VarTab {
+  int n;
+  int total;
+  int row_off[kVarMax + 1];
+  int item_off[kVarMax + 1];   // prefill work items, filled by the launcher
+};
+
 hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
                               const void* v, const int32_t* start, int n_tok, void* kdst,
-                              void* vdst, WriteMode mode, hipStream_t st);
+                              void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st);
 
 // Fast bf16 prefill: head_dim 128, group size 4, n_sink <= 64.
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
-                                       float* lse, hipStream_t st);
+                                       float* lse, const VarTab* vt, hipStream_t st);
 
 // Generic prefill (float32 or bf16, head_dim 64 or 128, any group size).
 hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
                                   const void* k_rot, const void* v, const void* kc,
                                   const void* vc, const int32_t* start, int C, void* out,
-                                  float* lse, hipStream_t st);
+                                  float* lse, const VarTab* vt, hipStream_t st);
 
 // Split-K decode.  Partials: [B][Hq][n_splits][D + 2] float.  The fast
 // kernel writes out and lse itself when n_splits == 1 (no combine pass).

@@ -158,9 +158,10 @@ struct PrefillArgs {
   const int32_t* start;
   int C;
   int n_qtiles;
-  int n_items;          // n_qtiles * Hkv * B
+  int n_items;          // n_qtiles * Hkv * B, or the VarTab's item count
   uint16_t* out;
   float* lse;
+  VarTab vt;            // packed sequences of their own lengths (varlen kernel)
 };
 
 // One work-group: 64 query positions x the 4 query heads of one KV head,
@@ -175,6 +176,7 @@ struct PrefillArgs {
 // first tiles of the next one into the ring, and the next item's query rows
 // go to an LDS stage while the current item runs, so that an item starts
 // without waiting for memory.
+template <bool VAR>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
@@ -226,6 +228,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // n_sink-1 for queries whose window no longer contains them.
   struct Item {
     int b, kvh, t0, s0, n_stile, kmin, n_tiles;
+    int row0, len;   // varlen: the sequence's first packed row, its length
   };
   // The start positions are read through the constant address space, so
   // that they come in with scalar loads, which the wait for the tile loads
@@ -234,13 +237,33 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   c_i32* start_c = (c_i32*)a.start;
   auto item_params = [&](int L) __attribute__((always_inline)) {
     Item it;
-    const int per_b = sh.Hkv * a.n_qtiles;
-    it.b = L / per_b;
-    const int rem = L - it.b * per_b;
-    it.kvh = rem / a.n_qtiles;
-    it.t0 = (a.n_qtiles - 1 - (rem - it.kvh * a.n_qtiles)) * BM;
+    if (VAR) {
+      // the sequence whose items hold L: the number of sequences that end
+      // at or before L, counted over the lanes
+      int io_;
+      {
+        int ln_ = lane;
+        asm volatile("" : "+v"(ln_));
+        io_ = ln_ < a.vt.n ? a.vt.item_off[ln_ + 1] : INT_MAX;
+      }
+      it.b = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(io_ <= L)));
+      it.row0 = a.vt.row_off[it.b];
+      it.len = a.vt.row_off[it.b + 1] - it.row0;
+      const int nqt = (it.len + BM - 1) / BM;
+      const int rem = L - a.vt.item_off[it.b];
+      it.kvh = rem / nqt;
+      it.t0 = (nqt - 1 - (rem - it.kvh * nqt)) * BM;
+    } else {
+      const int per_b = sh.Hkv * a.n_qtiles;
+      it.b = L / per_b;
+      const int rem = L - it.b * per_b;
+      it.kvh = rem / a.n_qtiles;
+      it.t0 = (a.n_qtiles - 1 - (rem - it.kvh * a.n_qtiles)) * BM;
+      it.row0 = it.b * C;
+      it.len = C;
+    }
     it.s0 = start_c[it.b];
-    const int tq_last = min(it.t0 + BM, C) - 1;
+    const int tq_last = min(it.t0 + BM, it.len) - 1;
     it.n_stile = (nsink > 0 && (it.s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
     const int k_lo = -((W - 1 + BN - 1) / BN);
     const int k_clip = -((it.s0 + it.t0 + BN - 1) / BN);
@@ -286,10 +309,11 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     l_ns = it.n_stile;
     l_u0 = it.t0 + BN * (it.kmin - it.n_stile);
     l_s0 = it.s0;
-    l_ec = ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
+    l_ec = VAR ? ((long long)it.row0 * sh.Hkv + it.kvh) * HD : ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
     l_es = ((long long)it.b * S * sh.Hkv + it.kvh) * HD;
-    rkc = rsrc(a.kr, l_ec, nrec_c);
-    rvc = rsrc(a.v, l_ec, nrec_c);
+    const int nrec = VAR ? (it.len - 1) * (int)rowbytes + HD * 2 : nrec_c;
+    rkc = rsrc(a.kr, l_ec, nrec);
+    rvc = rsrc(a.v, l_ec, nrec);
   };
   set_cursor(item_at(0));
   // The next load is prepared one step ahead (prepare(), run while the
@@ -377,8 +401,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // operand read touches fall in 16 different bank groups.  Rows past the
   // chunk read as zeros.
   auto load_q = [&](const Item& it) __attribute__((always_inline)) {
+    const long long qrow = VAR ? (long long)it.row0 : (long long)it.b * C;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(a.q + ((long long)it.b * C * sh.Hq + 4 * it.kvh) * HD), (short)0, nrec_q, 0x00020000);
+        uniform_ptr(a.q + (qrow * sh.Hq + 4 * it.kvh) * HD), (short)0,
+        VAR ? (it.len - 1) * (int)qrowbytes + QROWB : nrec_q, 0x00020000);
     int ln_ = lane;   // (computed here, not held in registers across the loop)
     asm volatile("" : "+v"(ln_));
 #pragma unroll
@@ -781,18 +807,21 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
                            pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
         *reinterpret_cast<u32x2*>(row + 16 * (c ^ ii)) = val;
       }
-      if (a.lse && g == 0 && tq < C)
-        a.lse[((long long)b * sh.Hq + h0 + qb) * C + tq] = (ref[qb] + log2f(lsum[qb][0])) * 0.69314718055994531f;
+      if (a.lse && g == 0 && tq < it.len) {
+        const long long lo = VAR ? (long long)(h0 + qb) * a.vt.total + it.row0 + tq
+                                 : ((long long)b * sh.Hq + h0 + qb) * C + tq;
+        a.lse[lo] = (ref[qb] + log2f(lsum[qb][0])) * 0.69314718055994531f;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     {
-      uint16_t* orow = a.out + ((long long)b * C * sh.Hq + 4 * kvh) * HD;
+      uint16_t* orow = a.out + ((VAR ? (long long)it.row0 : (long long)b * C) * sh.Hq + 4 * kvh) * HD;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int q = 8 * w + m;
-        if (t0 + q < C) {
+        if (t0 + q < it.len) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(qstage + q * QROWB + 16 * li_);
           *reinterpret_cast<u32x4*>(orow + (long long)(t0 + q) * sh.Hq * HD + 8 * (li_ ^ (q & 15))) = v;
         }
@@ -828,15 +857,18 @@ __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab r
                                                              const void* kr, const void* v,
                                                              const void* kc, const void* vc,
                                                              const int32_t* start, int C, void* out,
-                                                             float* lse) {
+                                                             float* lse, VarTab vt) {
   const int t = blockIdx.x * 64 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  if (t >= C) return;
+  // the sequence's rows: b * C .. + C, or its packed run (vt.n > 0)
+  const long long r0 = vt.n ? (long long)vt.row_off[b] : (long long)b * C;
+  const int len = vt.n ? vt.row_off[b + 1] - vt.row_off[b] : C;
+  if (t >= len) return;
   const int kvh = h / (sh.Hq / sh.Hkv);
   const int s0 = start[b];
   const int I = s0 + t;
   float qv[D];
-  const long long qoff = (((long long)b * C + t) * sh.Hq + h) * D;
+  const long long qoff = ((r0 + t) * sh.Hq + h) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) qv[d] = ld<F32>(q, qoff + d);
   if (sh.rope) {
@@ -862,7 +894,7 @@ __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab r
     if (j >= s0) {
       kb = kr;
       vb = v;
-      off = (((long long)b * C + (j - s0)) * sh.Hkv + kvh) * D;
+      off = ((r0 + (j - s0)) * sh.Hkv + kvh) * D;
     } else {
       if (!kc) return;
       kb = kc;
@@ -885,10 +917,13 @@ __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab r
   for (int j = 0; j < min(sh.n_sink, lo); ++j) visit(j);
   for (int j = lo; j <= I; ++j) visit(j);
   const float inv = 1.f / l;
-  const long long ooff = (((long long)b * C + t) * sh.Hq + h) * D;
+  const long long ooff = ((r0 + t) * sh.Hq + h) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) st<F32>(out, ooff + d, o[d] * inv);
-  if (lse) lse[((long long)b * sh.Hq + h) * C + t] = (m + log2f(l)) * 0.69314718055994531f;
+  if (lse) {
+    const long long lo = vt.n ? (long long)h * vt.total + r0 + t : ((long long)b * sh.Hq + h) * C + t;
+    lse[lo] = (m + log2f(l)) * 0.69314718055994531f;
+  }
 }
 
 }  // namespace
@@ -907,7 +942,7 @@ static int device_cu_count() {
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
-                                       float* lse, hipStream_t st) {
+                                       float* lse, const VarTab* vt, hipStream_t st) {
   PrefillArgs a;
   a.sh = sh;
   a.rt = rt;
@@ -921,31 +956,51 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.n_qtiles = (C + BM - 1) / BM;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  const long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B;
+  long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B;
+  if (vt) {
+    // items of sequence j: Hkv x its own query tiles, numbered after those of 0 .. j-1
+    a.vt = *vt;
+    a.vt.item_off[0] = 0;
+    for (int j = 0; j < vt->n; ++j) {
+      const int len = vt->row_off[j + 1] - vt->row_off[j];
+      const long long next = a.vt.item_off[j] + (long long)sh.Hkv * ((len + BM - 1) / BM);
+      if (next > INT32_MAX) return hipErrorInvalidValue;
+      a.vt.item_off[j + 1] = (int)next;
+    }
+    n_items = a.vt.item_off[vt->n];
+    if (n_items == 0) return hipSuccess;
+  } else {
+    a.vt = VarTab{};
+  }
   if (n_items > INT32_MAX) return hipErrorInvalidValue;
   a.n_items = (int)n_items;
   // one work-group per CU (a multiple of 8), each looping over its items
   const long long ncu = (long long)(device_cu_count() & ~7);
   const long long nwg = (ncu >= 8 && n_items > ncu) ? ncu : n_items;
-  prefill_bf16_d128_g4_kernel<<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+  if (vt)
+    prefill_bf16_d128_g4_kernel<true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+  else
+    prefill_bf16_d128_g4_kernel<false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
                                   const void* k_rot, const void* v, const void* kc,
                                   const void* vc, const int32_t* start, int C, void* out,
-                                  float* lse, hipStream_t st) {
+                                  float* lse, const VarTab* vt, hipStream_t st) {
   dim3 grid((C + 63) / 64, sh.Hq, sh.B);
+  const VarTab none{};
+  const VarTab& t = vt ? *vt : none;
   if (f32) {
     if (sh.D == 64)
-      prefill_generic_kernel<true, 64><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse);
+      prefill_generic_kernel<true, 64><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse, t);
     else
-      prefill_generic_kernel<true, 128><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse);
+      prefill_generic_kernel<true, 128><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse, t);
   } else {
     if (sh.D == 64)
-      prefill_generic_kernel<false, 64><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse);
+      prefill_generic_kernel<false, 64><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse, t);
     else
-      prefill_generic_kernel<false, 128><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse);
+      prefill_generic_kernel<false, 128><<<grid, 64, 0, st>>>(sh, rt, q, k_rot, v, kc, vc, start, C, out, lse, t);
   }
   return hipGetLastError();
 }

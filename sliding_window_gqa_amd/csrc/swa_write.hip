@@ -6,6 +6,9 @@
 // is applied to keys here, at their absolute position, so the cache holds
 // rotated keys and values verbatim.
 //
+// Varlen batches (a VarTab) take each sequence's rows from its packed run and
+// its own length; the rule for survivors is the same per sequence.
+//
 // One thread moves 8 consecutive elements (one 16-byte bf16 chunk, or two
 // 16-byte float chunks) of one (token, kv-head) row.  A block covers whole
 // tokens of one sequence (blockIdx.y): thread x handles chunk x mod cpt of
@@ -23,23 +26,26 @@
 namespace swa {
 namespace {
 
-template <bool F32>
+template <bool F32, bool VAR>
 __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, const void* __restrict__ k,
                                                          const void* __restrict__ v,
                                                          const int32_t* __restrict__ start, int n_tok,
                                                          void* __restrict__ kdst, void* __restrict__ vdst,
-                                                         int mode, int tok_per_block) {
+                                                         int mode, int tok_per_block, VarTab vt) {
   const int cpr = sh.D / 8;           // chunks per (token, head) row: 8 or 16
   const int cpt = sh.Hkv * cpr;       // chunks per token
   const int b = blockIdx.y;
-  const int s0 = start[b];
-  const int last = s0 + n_tok - 1;
+  // the sequence's rows: b * n_tok .. + n_tok, or its packed run
+  const int len = VAR ? vt.row_off[b + 1] - vt.row_off[b] : n_tok;
+  const long long srow = VAR ? (long long)vt.row_off[b] : (long long)b * n_tok;
   const int tb = (int)threadIdx.x / cpt;  // token of this thread within the block's run
   const int t = blockIdx.x * tok_per_block + tb;
-  if (tb >= tok_per_block || t >= n_tok) return;
+  if (tb >= tok_per_block || t >= len) return;
+  const int s0 = start[b];
+  const int last = s0 + len - 1;
   const int p = s0 + t;
   if (mode == kToCache && p >= sh.n_sink && p + sh.W <= last) return;  // overwritten later in this call
-  const long long row0 = (long long)b * n_tok + t;                      // source token row
+  const long long row0 = srow + t;                                      // source token row
   const long long drow0 = mode == kToCache ? (long long)b * sh.S + slot_of(p, sh.W, sh.n_sink) : row0;
   for (int ct = (int)threadIdx.x - tb * cpt; ct < cpt; ct += (int)blockDim.x) {
     const int h = ct / cpr, c = ct - h * cpr;
@@ -95,19 +101,30 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
 
 hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
                               const void* v, const int32_t* start, int n_tok, void* kdst,
-                              void* vdst, WriteMode mode, hipStream_t st) {
+                              void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st) {
   const int threads = 256;
   const int cpt = sh.Hkv * (sh.D / 8);
   const int tok_per_block = cpt <= threads ? threads / cpt : 1;
   const long long bx = ((long long)n_tok + tok_per_block - 1) / tok_per_block;
   if (bx > INT32_MAX || sh.B > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)bx, (unsigned)sh.B);
-  if (f32)
-    cache_write_kernel<true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                             (int)mode, tok_per_block);
-  else
-    cache_write_kernel<false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                              (int)mode, tok_per_block);
+  const VarTab none{};
+  const VarTab& t = vt ? *vt : none;
+  if (f32) {
+    if (vt)
+      cache_write_kernel<true, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
+                                                                     (int)mode, tok_per_block, t);
+    else
+      cache_write_kernel<true, false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
+                                                                      (int)mode, tok_per_block, t);
+  } else {
+    if (vt)
+      cache_write_kernel<false, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
+                                                                      (int)mode, tok_per_block, t);
+    else
+      cache_write_kernel<false, false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
+                                                                       (int)mode, tok_per_block, t);
+  }
   return hipGetLastError();
 }
 

@@ -30,7 +30,9 @@ def test_every_declared_symbol_is_exported():
             "swa_decode_workspace_bytes",
             "swa_rope_keys", "swa_prefill_attention",
             "swa_prefill_workspace_bytes", "swa_status_string", "swa_debug_slots",
-            "swa_debug_mask"} <= set(names)
+            "swa_debug_mask", "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen",
+            "swa_prefill_attention_varlen", "swa_prefill_chunk_varlen",
+            "swa_cache_write_varlen"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -140,3 +142,38 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(swa, "LIB_PATH", str(tmp_path / "libswa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         swa.library()
+
+
+def _lens(*xs):
+    return (ctypes.c_int32 * len(xs))(*xs)
+
+
+def test_varlen_arguments_rejected():
+    lib = swa.library()
+    p = P(batch=3)
+    bp = ctypes.byref(p)
+    good = _lens(5, 0, 7)
+    calls = [
+        lambda L: lib.swa_rope_keys_varlen(bp, FAKE, FAKE, L, FAKE, None),
+        lambda L: lib.swa_cache_write_varlen(bp, FAKE, FAKE, FAKE, L, FAKE, FAKE, None),
+        lambda L: lib.swa_prefill_attention_varlen(bp, FAKE, FAKE, FAKE, None, None, FAKE, L, FAKE, None, None),
+        lambda L: lib.swa_prefill_chunk_varlen(bp, FAKE, FAKE, FAKE, None, None, FAKE, L, FAKE, None, FAKE,
+                                               1 << 30, None),
+    ]
+    for call in calls:
+        assert call(None) == swa.SWA_ERR_NULL
+        assert call(_lens(0, 0, 0)) == swa.SWA_ERR_SHAPE       # no token at all
+        assert call(_lens(5, -1, 7)) == swa.SWA_ERR_SHAPE
+        assert call(_lens(5, (1 << 24) + 1, 7)) == swa.SWA_ERR_SHAPE
+    # bad params come first, before the lengths are read
+    bad = ctypes.byref(P(batch=3, head_dim=96))
+    assert lib.swa_rope_keys_varlen(bad, FAKE, FAKE, good, FAKE, None) == swa.SWA_ERR_SHAPE
+    assert lib.swa_prefill_varlen_workspace_bytes(bad, good) == 0
+    assert lib.swa_prefill_varlen_workspace_bytes(bp, None) == 0
+    # workspace: the packed rotated keys
+    need = lib.swa_prefill_varlen_workspace_bytes(bp, good)
+    assert need == 12 * 8 * 128 * 2
+    assert lib.swa_prefill_chunk_varlen(bp, FAKE, FAKE, FAKE, None, None, FAKE, good, FAKE, None, FAKE,
+                                        need - 1, None) == swa.SWA_ERR_WORKSPACE
+    assert lib.swa_prefill_chunk_varlen(bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, good, FAKE, None, FAKE,
+                                        need, None) == swa.SWA_ERR_NULL   # one cache pointer only

@@ -312,3 +312,81 @@ def test_bitwise_determinism_and_resume():
     second = [gpu.decode(*steps[s], [300 + s] * B) for s in range(10, 20)]
     for (a, la), (b, lb) in zip(first, second):
         assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------------------
+# varlen batches: chunks of their own lengths, packed
+# ---------------------------------------------------------------------------
+def _varlen_lens_starts(B, seed):
+    g = np.random.default_rng(seed)
+    lens = [int(x) for x in np.where(g.random(B) < 0.2, g.integers(20, 90, B), 1)]
+    starts = [int(x) for x in g.integers(0, 200, B)]
+    return lens, starts
+
+
+VARLEN_CASES = [
+    # B, Hq, Hkv, D, W, sinks, dtype, chunk lengths, start positions
+    (5, 8, 2, 128, 100, 3, torch.bfloat16, [0, 1, 130, 64, 7], [0, 250, 40, 0, 300]),
+    (4, 8, 2, 128, 4096, 0, torch.bfloat16, [300, 1, 65, 129], [0, 70, 3, 0]),
+    (3, 4, 1, 64, 100, 0, torch.float32, [3, 0, 70], [10, 5, 0]),       # generic path
+    (70, 8, 2, 128, 64, 0, torch.bfloat16) + _varlen_lens_starts(70, 7),  # two launches, mixed with decodes
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}{str(c[6])[6:]}" for c in VARLEN_CASES])
+def test_prefill_varlen(case):
+    """Packed chunks of different lengths (length 1 = a decode token) against
+    the oracle per sequence, and bit for bit against each sequence alone
+    through the fixed-length calls: attention output, LSE and the cache write."""
+    B, Hq, Hkv, D, W, S, dtype, lens, starts = case
+    print(f"varlen prefill B={B} lens={lens[:8]} starts={starts[:8]}", flush=True)
+    theta = 10000.0
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta)
+    for b in range(B):   # every earlier position of each sequence
+        if starts[b] == 0:
+            continue
+        kh = rnd((1, starts[b], Hkv, D), "hist_k", b, dtype, index=92)
+        vh = rnd((1, starts[b], Hkv, D), "hist_v", b, dtype, index=92)
+        sub = GpuSide(1, Hq, Hkv, D, W, S, theta, dtype)
+        sub.write(kh, vh, [0])
+        gpu.kc[b] = sub.kc[0]
+        gpu.vc[b] = sub.vc[0]
+        orc.caches[b].write(so.rope(np64(kh[0]), np.arange(starts[b]), theta), np64(vh[0]), np.arange(starts[b]))
+    T = sum(lens)
+    q = rnd((T, Hq, D), "chunk_q", 0, dtype, index=92)
+    k = rnd((T, Hkv, D), "chunk_k", 0, dtype, index=92)
+    v = rnd((T, Hkv, D), "chunk_v", 0, dtype, index=92)
+    st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = swa.swa_prefill_chunk_varlen(gpu.p, qd, kd, vd, gpu.kc, gpu.vc, st, lens)
+    p1 = swa.make_params(1, Hq, Hkv, D, W, S, 0.0, theta, dtype)
+    atol, rrms, latol = tol(dtype)
+    r = 0
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            continue
+        o1, l1 = swa.swa_prefill_chunk(p1, qd[r:r + n][None].contiguous(), kd[r:r + n][None].contiguous(),
+                                       vd[r:r + n][None].contiguous(), gpu.kc[b:b + 1], gpu.vc[b:b + 1],
+                                       st[b:b + 1])
+        assert torch.equal(o1[0], out[r:r + n]), f"seq {b}: varlen output differs from the fixed-length call"
+        assert torch.equal(l1[0], lse[:, r:r + n]), f"seq {b}: varlen LSE differs from the fixed-length call"
+        if b < 12 or n > 1:   # the oracle on every chunk and the first decode-like rows
+            ro, rl = so.prefill_chunk(orc.caches[b], np64(q[r:r + n]), np64(k[r:r + n]), np64(v[r:r + n]),
+                                      starts[b], theta)
+            assert_close(out[r:r + n].cpu(), ro, atol, rrms, f"seq {b} out")
+            assert_lse(lse[:, r:r + n].cpu(), rl, latol, f"seq {b} lse")
+        r += n
+    # the cache write of the packed chunks = each sequence's own write, byte for byte
+    ref_k, ref_v = gpu.kc.clone(), gpu.vc.clone()
+    swa.swa_cache_write_varlen(gpu.p, kd, vd, st, lens, gpu.kc, gpu.vc)
+    r = 0
+    for b in range(B):
+        n = lens[b]
+        if n:
+            swa.swa_cache_write(p1, kd[r:r + n][None].contiguous(), vd[r:r + n][None].contiguous(), st[b:b + 1],
+                                ref_k[b:b + 1], ref_v[b:b + 1])
+        r += n
+    assert torch.equal(gpu.kc.view(torch.uint8), ref_k.view(torch.uint8))
+    assert torch.equal(gpu.vc.view(torch.uint8), ref_v.view(torch.uint8))
