@@ -195,6 +195,24 @@ int swa_cache_write_varlen(const swa_params* params, const void* k, const void* 
                            const int32_t* start_pos, const int32_t* chunk_lens, void* k_cache,
                            void* v_cache, hipStream_t stream);
 
+/*
+ * swa_step_varlen — one whole step of a mixed batch: every sequence's chunk
+ * attends (the sequences of one token decode it), then every chunk goes
+ * into the rolling buffers.  Same arguments and layouts as above; k_cache
+ * and v_cache are read and written.  The result is that of
+ * swa_prefill_chunk_varlen followed by swa_cache_write_varlen, up to
+ * rounding: with bf16, head_dim 128 and 4 query heads per KV head, the
+ * sequences of one token go to the decode kernel after the cache write
+ * (the rest to the prefill kernel, before it), so that a decode token costs
+ * a decode, not a 64-query prefill tile.
+ *   workspace : >= swa_step_varlen_workspace_bytes(params, chunk_lens) bytes.
+ */
+size_t swa_step_varlen_workspace_bytes(const swa_params* params, const int32_t* chunk_lens);
+int swa_step_varlen(const swa_params* params, const void* q, const void* k, const void* v,
+                    void* k_cache, void* v_cache, const int32_t* start_pos,
+                    const int32_t* chunk_lens, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace swa_decode needs (split-K partial results). */
 size_t swa_decode_workspace_bytes(const swa_params* params);
 

@@ -17,7 +17,8 @@ __all__ = [
     "swa_decode", "swa_decode_step", "swa_decode_workspace_bytes", "swa_status_string",
     "swa_rope_keys", "swa_prefill_attention",
     "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen", "swa_prefill_attention_varlen",
-    "swa_prefill_chunk_varlen", "swa_cache_write_varlen",
+    "swa_prefill_chunk_varlen", "swa_cache_write_varlen", "swa_step_varlen",
+    "swa_step_varlen_workspace_bytes",
     "swa_debug_slots", "swa_debug_mask",
     "SWA_OK", "SWA_ERR_NULL", "SWA_ERR_SHAPE", "SWA_ERR_DTYPE", "SWA_ERR_UNSUPPORTED",
     "SWA_ERR_WORKSPACE", "SWA_ERR_LAUNCH", "SWA_BF16", "SWA_F32",
@@ -69,6 +70,8 @@ _SIGNATURES = {
     "swa_prefill_attention_varlen": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "swa_prefill_chunk_varlen": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "swa_cache_write_varlen": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "swa_step_varlen_workspace_bytes": (_sz, [_P, _vp]),
+    "swa_step_varlen": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "swa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "swa_debug_slots": (ctypes.c_int, [_P, _vp, _i32, _vp, _vp]),
     "swa_debug_mask": (ctypes.c_int, [_P, _i32, _vp, _i32, _vp, _vp]),
@@ -380,6 +383,38 @@ def swa_cache_write_varlen(params, k, v, start_pos, chunk_lens, k_cache, v_cache
         _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), lens,
         _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp), _stream(stream))
     _check(st, "swa_cache_write_varlen")
+
+
+def swa_step_varlen_workspace_bytes(params, chunk_lens) -> int:
+    lens, _ = _lens(params, chunk_lens)
+    return int(library().swa_step_varlen_workspace_bytes(ctypes.byref(params), lens))
+
+
+def swa_step_varlen(params, q, k, v, k_cache, v_cache, start_pos, chunk_lens, out=None, lse=None,
+                    workspace=None, want_lse=True, stream=None):
+    """One whole step of a mixed batch (attention of every packed chunk, the
+    one-token sequences as decodes, then the cache write); returns (out
+    [total][Hq][D], lse [Hq][total])."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    lens, total = _lens(params, chunk_lens)
+    qshp = (total, params.n_q_heads, params.head_dim)
+    kshp = (total, params.n_kv_heads, params.head_dim)
+    cshp = (params.batch, params.n_sink + params.window, params.n_kv_heads, params.head_dim)
+    if out is None:
+        out = torch.empty(qshp, dtype=dt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((params.n_q_heads, total), dtype=torch.float32, device=q.device)
+    need = int(library().swa_step_varlen_workspace_bytes(ctypes.byref(params), lens))
+    workspace = _workspace(need, q.device, workspace)
+    st = library().swa_step_varlen(
+        ctypes.byref(params), _ptr(q, "q", dt, qshp), _ptr(k, "k", dt, kshp), _ptr(v, "v", dt, kshp),
+        _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp),
+        _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), lens,
+        _ptr(out, "out", dt, qshp), _ptr(lse, "lse", torch.float32, (params.n_q_heads, total)),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "swa_step_varlen")
+    return out, lse
 
 
 def swa_debug_slots(params, positions, stream=None):

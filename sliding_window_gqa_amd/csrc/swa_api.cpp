@@ -130,13 +130,44 @@ int decode_launch(const swa_params* params, const Shape& sh, const void* q, cons
   hipError_t e;
   if (fast_path(params)) {
     e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, out, lse, fw,
-                                        stream);
+                                        nullptr, stream);
     if (n == 1) return launched(e);   // the kernel wrote out and lse
   } else {
     e = swa::launch_decode_generic(sh, rt, f32, q, k_cache, v_cache, pos, part, n, stream);
   }
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
-  return launched(swa::launch_decode_combine(sh, f32, part, n, out, lse, stream));
+  return launched(swa::launch_decode_combine(sh, f32, part, n, out, lse, nullptr, stream));
+}
+
+// The decode launches of a mixed varlen step: the sequences of one token, at
+// most kVarMax per launch.  f(map, sub-shape) for each.
+template <class F>
+int for_decode_groups(const Shape& sh, const int32_t* lens, long long total, F&& f) {
+  swa::DecodeMap m{};
+  m.lse_hs = (int)total;
+  long long row = 0;
+  for (int b = 0; b < sh.B; ++b) {
+    if (lens[b] == 1) {
+      m.seq[m.n] = b;
+      m.row[m.n] = (int)row;
+      ++m.n;
+    }
+    row += lens[b];
+    if (m.n == swa::kVarMax || (b == sh.B - 1 && m.n > 0)) {
+      Shape gs = sh;
+      gs.B = m.n;
+      const int st = f(m, gs);
+      if (st != SWA_OK) return st;
+      m.n = 0;
+    }
+  }
+  return SWA_OK;
+}
+
+// Bytes of the rotated keys of a varlen step, rounded up to 256.
+size_t step_keys_bytes(const swa_params* p, long long total) {
+  const size_t kb = (size_t)total * p->n_kv_heads * p->head_dim * elem_size(p->dtype);
+  return (kb + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -362,6 +393,74 @@ int swa_prefill_chunk_varlen(const swa_params* params, const void* q, const void
   if (st != SWA_OK) return st;
   return swa_prefill_attention_varlen(params, q, workspace, v, k_cache, v_cache, start_pos,
                                       chunk_lens, out, lse, stream);
+}
+
+size_t swa_step_varlen_workspace_bytes(const swa_params* params, const int32_t* chunk_lens) {
+  Shape sh;
+  long long total;
+  int longest;
+  if (check_params(params, &sh) != SWA_OK) return 0;
+  if (check_lens(params, chunk_lens, &total, &longest) != SWA_OK) return 0;
+  size_t part = 0;
+  for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap&, const Shape& gs) {
+    const size_t need = (size_t)gs.B * gs.Hq * swa::decode_splits(gs) * (gs.D + 2) * sizeof(float);
+    if (need > part) part = need;
+    return SWA_OK;
+  });
+  return step_keys_bytes(params, total) + part;
+}
+
+int swa_step_varlen(const swa_params* params, const void* q, const void* k, const void* v,
+                    void* k_cache, void* v_cache, const int32_t* start_pos,
+                    const int32_t* chunk_lens, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!q || !k || !v || !k_cache || !v_cache || !start_pos || !out) return SWA_ERR_NULL;
+  long long total;
+  int longest;
+  st = check_lens(params, chunk_lens, &total, &longest);
+  if (st != SWA_OK) return st;
+  if (!workspace || workspace_bytes < swa_step_varlen_workspace_bytes(params, chunk_lens))
+    return SWA_ERR_WORKSPACE;
+  if (!fast_prefill(params, longest)) {
+    // one path for every sequence: the prefill chunk, then the cache write
+    st = swa_prefill_chunk_varlen(params, q, k, v, k_cache, v_cache, start_pos, chunk_lens, out, lse,
+                                  workspace, workspace_bytes, stream);
+    if (st != SWA_OK) return st;
+    return swa_cache_write_varlen(params, k, v, start_pos, chunk_lens, k_cache, v_cache, stream);
+  }
+  // 1. every chunk's keys rotated into the workspace
+  st = swa_rope_keys_varlen(params, k, start_pos, chunk_lens, workspace, stream);
+  if (st != SWA_OK) return st;
+  // 2. attention of the sequences of more than one token (they read the caches as they stand)
+  const RopeTab rt = rope_table(params);
+  const size_t es = elem_size(params->dtype);
+  const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
+  st = for_var_groups(sh, chunk_lens, total, [&](int g0, swa::VarTab& vt, long long row, int mx,
+                                                 const Shape& gs) {
+    vt.skip_len1 = 1;
+    return swa::launch_prefill_bf16_d128_g4(
+        gs, rt, rows_at(q, row, q_row, es), rows_at((const void*)workspace, row, kv_row, es),
+        rows_at(v, row, kv_row, es), rows_at((const void*)k_cache, (long long)g0 * sh.S, kv_row, es),
+        rows_at((const void*)v_cache, (long long)g0 * sh.S, kv_row, es), start_pos + g0, mx,
+        rows_at(out, row, q_row, es), lse ? lse + row : nullptr, &vt, stream);
+  });
+  if (st != SWA_OK) return st;
+  // 3. every chunk into the rolling buffers
+  st = swa_cache_write_varlen(params, k, v, start_pos, chunk_lens, k_cache, v_cache, stream);
+  if (st != SWA_OK) return st;
+  // 4. the one-token sequences through the decode kernel, which now finds
+  //    their entries in the caches
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + step_keys_bytes(params, total));
+  return for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap& m, const Shape& gs) {
+    const int n = swa::decode_splits(gs);
+    hipError_t e = swa::launch_decode_bf16_d128_g4(gs, rt, q, k_cache, v_cache, start_pos, part, n, out,
+                                                   lse, nullptr, &m, stream);
+    if (e == hipSuccess && n > 1) e = swa::launch_decode_combine(gs, false, part, n, out, lse, &m, stream);
+    return launched(e);
+  });
 }
 
 const char* swa_status_string(int status) {

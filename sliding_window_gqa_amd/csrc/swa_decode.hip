@@ -75,6 +75,7 @@ struct DecodeArgs {
   const uint16_t* vnew;
   uint16_t* kdst;
   uint16_t* vdst;
+  DecodeMap map;   // varlen batches: sequence and packed row of each column
 };
 
 // K chunks in LDS: 32 rows of 256 bytes, the 16-byte chunk c of row r at
@@ -117,7 +118,10 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, kvh = blockIdx.y, z = blockIdx.z;
+  // b: the sequence (position, caches); r: the row of its token in q / out
+  const int b = a.map.n ? a.map.seq[z] : z;
+  const int r = a.map.n ? a.map.row[z] : z;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, i = lane & 15, g = lane >> 4;
@@ -147,7 +151,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
     if (slot >= sp0 && slot < sp0 + a.split_len) {
       if (tid < 32) {
         const int c = tid & 15;   // 16-byte chunk: head-dim elements 8c .. 8c+7
-        const long long src = ((long long)b * sh.Hkv + kvh) * HD + 8 * c;
+        const long long src = ((long long)r * sh.Hkv + kvh) * HD + 8 * c;
         const long long dst = ((long long)b * S + slot) * row_stride + kvh * HD + 8 * c;
         if (tid < 16) {
           const u32x4 wk = *reinterpret_cast<const u32x4*>(a.knew + src);
@@ -179,7 +183,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
     u32x4 wq[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      wq[kk] = *reinterpret_cast<const u32x4*>(a.q + ((long long)b * sh.Hq + h0 + (i & 3)) * HD + 8 * (4 * kk + g));
+      wq[kk] = *reinterpret_cast<const u32x4*>(a.q + ((long long)r * sh.Hq + h0 + (i & 3)) * HD + 8 * (4 * kk + g));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const u32x4 wv = i < 4 ? wq[kk] : u32x4{0u, 0u, 0u, 0u};
@@ -368,11 +372,14 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
     }
     if (a.n_splits == 1) {
       // one range covers the sequence: this is the final result
-      const long long off = ((long long)b * sh.Hq + h0 + hh) * HD + d;
+      const long long off = ((long long)r * sh.Hq + h0 + hh) * HD + d;
       a.out[off] = to_bf16_bits(O / Lsum);
-      if (a.lse && d == 0) a.lse[(long long)b * sh.Hq + h0 + hh] = (M + log2f(Lsum)) * 0.69314718055994531f;
+      if (a.lse && d == 0) {
+        const long long lo = a.map.n ? (long long)(h0 + hh) * a.map.lse_hs + r : (long long)b * sh.Hq + h0 + hh;
+        a.lse[lo] = (M + log2f(Lsum)) * 0.69314718055994531f;
+      }
     } else {
-      float* dst = a.part + (((long long)b * sh.Hq + h0 + hh) * a.n_splits + split) * (HD + 2);
+      float* dst = a.part + (((long long)z * sh.Hq + h0 + hh) * a.n_splits + split) * (HD + 2);
       dst[d] = O;
       if (d == 0) {
         dst[HD] = M;
@@ -471,10 +478,11 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(Shape sh, RopeTab rt
 // ---------------------------------------------------------------------------
 template <bool F32>
 __global__ void decode_combine_kernel(Shape sh, const float* part, int n_splits, void* out,
-                                      float* lse) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+                                      float* lse, DecodeMap map) {
+  const int h = blockIdx.x, z = blockIdx.y, d = threadIdx.x;
+  const int r = map.n ? map.row[z] : z;   // the token's row in out
   const int D = sh.D;
-  const float* src = part + ((long long)b * sh.Hq + h) * n_splits * (D + 2);
+  const float* src = part + ((long long)z * sh.Hq + h) * n_splits * (D + 2);
   float M = -INFINITY;
   for (int s = 0; s < n_splits; ++s) M = fmaxf(M, src[s * (D + 2) + D]);
   float L = 0.f, O = 0.f;
@@ -485,12 +493,15 @@ __global__ void decode_combine_kernel(Shape sh, const float* part, int n_splits,
     O += src[s * (D + 2) + d] * f;
   }
   const float val = O / L;
-  const long long off = ((long long)b * sh.Hq + h) * D + d;
+  const long long off = ((long long)r * sh.Hq + h) * D + d;
   if (F32)
     static_cast<float*>(out)[off] = val;
   else
     static_cast<uint16_t*>(out)[off] = to_bf16_bits(val);
-  if (lse && d == 0) lse[(long long)b * sh.Hq + h] = (M + log2f(L)) * 0.69314718055994531f;
+  if (lse && d == 0) {
+    const long long lo = map.n ? (long long)h * map.lse_hs + r : (long long)r * sh.Hq + h;
+    lse[lo] = (M + log2f(L)) * 0.69314718055994531f;
+  }
 }
 
 }  // namespace
@@ -517,7 +528,7 @@ static int split_len_of(const Shape& sh, int n_splits) {
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
                                       float* partial, int n_splits, void* out, float* lse,
-                                      const FusedWrite* fw, hipStream_t st) {
+                                      const FusedWrite* fw, const DecodeMap* map, hipStream_t st) {
   DecodeArgs a;
   a.sh = sh;
   a.rt = rt;
@@ -534,6 +545,10 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
   a.vnew = fw ? static_cast<const uint16_t*>(fw->v) : nullptr;
   a.kdst = fw ? static_cast<uint16_t*>(fw->k_cache) : nullptr;
   a.vdst = fw ? static_cast<uint16_t*>(fw->v_cache) : nullptr;
+  if (map)
+    a.map = *map;
+  else
+    a.map = DecodeMap{};
   decode_bf16_d128_g4_kernel<<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
@@ -558,12 +573,14 @@ hipError_t launch_decode_generic(const Shape& sh, const RopeTab& rt, bool f32, c
 }
 
 hipError_t launch_decode_combine(const Shape& sh, bool f32, const float* partial, int n_splits,
-                                 void* out, float* lse, hipStream_t st) {
+                                 void* out, float* lse, const DecodeMap* map, hipStream_t st) {
   dim3 grid(sh.Hq, sh.B);
+  const DecodeMap none{};
+  const DecodeMap& m = map ? *map : none;
   if (f32)
-    decode_combine_kernel<true><<<grid, sh.D, 0, st>>>(sh, partial, n_splits, out, lse);
+    decode_combine_kernel<true><<<grid, sh.D, 0, st>>>(sh, partial, n_splits, out, lse, m);
   else
-    decode_combine_kernel<false><<<grid, sh.D, 0, st>>>(sh, partial, n_splits, out, lse);
+    decode_combine_kernel<false><<<grid, sh.D, 0, st>>>(sh, partial, n_splits, out, lse, m);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ constexpr int kVarMax = 64;
 struct VarTab {
   int n;
   int total;
+  int skip_len1;               // prefill: sequences of one token get no work items
   int row_off[kVarMax + 1];
   int item_off[kVarMax + 1];   // prefill work items, filled by the launcher
 };
@@ -49,6 +50,16 @@ hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, 
 // kernel writes out and lse itself when n_splits == 1 (no combine pass).
 // With a FusedWrite it first stores the new token's entry (raw k, v:
 // [B][Hkv][D]) into k_cache / v_cache (the caches it reads) at slot(pos).
+// A decode launch over some sequences of a varlen batch: work-group column
+// z decodes sequence seq[z] (its position, its caches) whose token is row
+// row[z] of the packed q / out; LSE is then [head][lse_hs].  n = 0: column
+// z is sequence z and row z, LSE [B][Hq].
+struct DecodeMap {
+  int n;
+  int lse_hs;
+  int seq[kVarMax];
+  int row[kVarMax];
+};
 struct FusedWrite {
   const void* k;
   const void* v;
@@ -59,12 +70,12 @@ int decode_splits(const Shape& sh);
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
                                       float* partial, int n_splits, void* out, float* lse,
-                                      const FusedWrite* fw, hipStream_t st);
+                                      const FusedWrite* fw, const DecodeMap* map, hipStream_t st);
 hipError_t launch_decode_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,
                                  const void* kc, const void* vc, const int32_t* pos,
                                  float* partial, int n_splits, hipStream_t st);
 hipError_t launch_decode_combine(const Shape& sh, bool f32, const float* partial, int n_splits,
-                                 void* out, float* lse, hipStream_t st);
+                                 void* out, float* lse, const DecodeMap* map, hipStream_t st);
 
 hipError_t launch_debug_slots(const Shape& sh, const int32_t* pos, int n, int32_t* slots,
                               hipStream_t st);

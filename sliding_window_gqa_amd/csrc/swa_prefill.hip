@@ -963,7 +963,8 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
     a.vt.item_off[0] = 0;
     for (int j = 0; j < vt->n; ++j) {
       const int len = vt->row_off[j + 1] - vt->row_off[j];
-      const long long next = a.vt.item_off[j] + (long long)sh.Hkv * ((len + BM - 1) / BM);
+      const int qt = (vt->skip_len1 && len == 1) ? 0 : (len + BM - 1) / BM;
+      const long long next = a.vt.item_off[j] + (long long)sh.Hkv * qt;
       if (next > INT32_MAX) return hipErrorInvalidValue;
       a.vt.item_off[j + 1] = (int)next;
     }

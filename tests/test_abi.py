@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported():
             "swa_prefill_workspace_bytes", "swa_status_string", "swa_debug_slots",
             "swa_debug_mask", "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen",
             "swa_prefill_attention_varlen", "swa_prefill_chunk_varlen",
-            "swa_cache_write_varlen"} <= set(names)
+            "swa_cache_write_varlen", "swa_step_varlen",
+            "swa_step_varlen_workspace_bytes"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -159,6 +160,7 @@ def test_varlen_arguments_rejected():
         lambda L: lib.swa_prefill_attention_varlen(bp, FAKE, FAKE, FAKE, None, None, FAKE, L, FAKE, None, None),
         lambda L: lib.swa_prefill_chunk_varlen(bp, FAKE, FAKE, FAKE, None, None, FAKE, L, FAKE, None, FAKE,
                                                1 << 30, None),
+        lambda L: lib.swa_step_varlen(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L, FAKE, None, FAKE, 1 << 30, None),
     ]
     for call in calls:
         assert call(None) == swa.SWA_ERR_NULL
@@ -177,3 +179,22 @@ def test_varlen_arguments_rejected():
                                         need - 1, None) == swa.SWA_ERR_WORKSPACE
     assert lib.swa_prefill_chunk_varlen(bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, good, FAKE, None, FAKE,
                                         need, None) == swa.SWA_ERR_NULL   # one cache pointer only
+
+
+def test_step_varlen_workspace():
+    lib = swa.library()
+    p = P(batch=4)
+    bp = ctypes.byref(p)
+    # no one-token sequence: the rotated keys only (rounded up to 256 bytes)
+    assert lib.swa_step_varlen_workspace_bytes(bp, _lens(5, 3, 0, 9)) == -(-(17 * 8 * 128 * 2) // 256) * 256
+    assert lib.swa_step_varlen_workspace_bytes(bp, _lens(5, 3, 0, 2)) == -(-(10 * 8 * 128 * 2) // 256) * 256
+    # two one-token sequences: plus their split-K partials
+    nbytes = lib.swa_step_varlen_workspace_bytes(bp, _lens(1, 30, 1, 0))
+    keys = 32 * 8 * 128 * 2
+    assert nbytes > keys and (nbytes - keys) % (2 * 32 * 130 * 4) == 0
+    for i in range(3):
+        args = [FAKE] * 6    # q, k, v, k_cache, v_cache, start_pos
+        args[3 + i] = None
+        assert lib.swa_step_varlen(bp, *args, _lens(1, 30, 1, 0), FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
+    assert lib.swa_step_varlen(bp, *([FAKE] * 6), _lens(1, 30, 1, 0), FAKE, None, FAKE, nbytes - 1,
+                               None) == swa.SWA_ERR_WORKSPACE

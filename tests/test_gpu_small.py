@@ -333,17 +333,14 @@ VARLEN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", VARLEN_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}{str(c[6])[6:]}" for c in VARLEN_CASES])
-def test_prefill_varlen(case):
-    """Packed chunks of different lengths (length 1 = a decode token) against
-    the oracle per sequence, and bit for bit against each sequence alone
-    through the fixed-length calls: attention output, LSE and the cache write."""
+def _varlen_setup(case):
+    """Caches holding every position before each sequence's start (GPU and
+    oracle), and the packed chunks."""
     B, Hq, Hkv, D, W, S, dtype, lens, starts = case
-    print(f"varlen prefill B={B} lens={lens[:8]} starts={starts[:8]}", flush=True)
     theta = 10000.0
     gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype)
     orc = OracleSide(range(B), Hkv, D, W, S, theta)
-    for b in range(B):   # every earlier position of each sequence
+    for b in range(B):
         if starts[b] == 0:
             continue
         kh = rnd((1, starts[b], Hkv, D), "hist_k", b, dtype, index=92)
@@ -358,6 +355,21 @@ def test_prefill_varlen(case):
     k = rnd((T, Hkv, D), "chunk_k", 0, dtype, index=92)
     v = rnd((T, Hkv, D), "chunk_v", 0, dtype, index=92)
     st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    return gpu, orc, q, k, v, st
+
+
+VARLEN_IDS = [f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}{str(c[6])[6:]}" for c in VARLEN_CASES]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=VARLEN_IDS)
+def test_prefill_varlen(case):
+    """Packed chunks of different lengths (length 1 = a decode token) against
+    the oracle per sequence, and bit for bit against each sequence alone
+    through the fixed-length calls: attention output, LSE and the cache write."""
+    B, Hq, Hkv, D, W, S, dtype, lens, starts = case
+    print(f"varlen prefill B={B} lens={lens[:8]} starts={starts[:8]}", flush=True)
+    theta = 10000.0
+    gpu, orc, q, k, v, st = _varlen_setup(case)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     out, lse = swa.swa_prefill_chunk_varlen(gpu.p, qd, kd, vd, gpu.kc, gpu.vc, st, lens)
     p1 = swa.make_params(1, Hq, Hkv, D, W, S, 0.0, theta, dtype)
@@ -390,3 +402,35 @@ def test_prefill_varlen(case):
         r += n
     assert torch.equal(gpu.kc.view(torch.uint8), ref_k.view(torch.uint8))
     assert torch.equal(gpu.vc.view(torch.uint8), ref_v.view(torch.uint8))
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=VARLEN_IDS)
+def test_step_varlen(case):
+    """A whole mixed step (one-token sequences through the decode kernel)
+    against the oracle per sequence; chunks of more than one token bit for bit
+    against swa_prefill_chunk_varlen; the caches afterwards byte for byte
+    against swa_cache_write_varlen."""
+    B, Hq, Hkv, D, W, S, dtype, lens, starts = case
+    print(f"varlen step B={B} lens={lens[:8]} starts={starts[:8]}", flush=True)
+    theta = 10000.0
+    gpu, orc, q, k, v, st = _varlen_setup(case)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ref_o, ref_l = swa.swa_prefill_chunk_varlen(gpu.p, qd, kd, vd, gpu.kc, gpu.vc, st, lens)
+    ref_k, ref_v = gpu.kc.clone(), gpu.vc.clone()
+    swa.swa_cache_write_varlen(gpu.p, kd, vd, st, lens, ref_k, ref_v)
+    out, lse = swa.swa_step_varlen(gpu.p, qd, kd, vd, gpu.kc, gpu.vc, st, lens)
+    assert torch.equal(gpu.kc.view(torch.uint8), ref_k.view(torch.uint8))
+    assert torch.equal(gpu.vc.view(torch.uint8), ref_v.view(torch.uint8))
+    atol, rrms, latol = tol(dtype)
+    r = 0
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            continue
+        if n > 1:
+            assert torch.equal(out[r:r + n], ref_o[r:r + n]) and torch.equal(lse[:, r:r + n], ref_l[:, r:r + n]), b
+        ro, rl = so.prefill_chunk(orc.caches[b], np64(q[r:r + n]), np64(k[r:r + n]), np64(v[r:r + n]),
+                                  starts[b], theta)
+        assert_close(out[r:r + n].cpu(), ro, atol, rrms, f"seq {b} out")
+        assert_lse(lse[:, r:r + n].cpu(), rl, latol, f"seq {b} lse")
+        r += n
