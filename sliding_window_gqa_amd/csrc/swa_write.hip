@@ -7,7 +7,8 @@
 // rotated keys and values verbatim.
 //
 // Varlen batches (a VarTab) take each sequence's rows from its packed run and
-// its own length; the rule for survivors is the same per sequence.
+// its own length, in one grid row of exactly the blocks the sequences need;
+// the rule for survivors is the same per sequence.
 //
 // One thread moves 8 consecutive elements (one 16-byte bf16 chunk, or two
 // 16-byte float chunks) of one (token, kv-head) row.  A block covers whole
@@ -34,12 +35,25 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
                                                          int mode, int tok_per_block, VarTab vt) {
   const int cpr = sh.D / 8;           // chunks per (token, head) row: 8 or 16
   const int cpt = sh.Hkv * cpr;       // chunks per token
-  const int b = blockIdx.y;
+  int b, blk;
+  if (VAR) {
+    // one grid row: block L is block L - item_off[b] of sequence b, the
+    // number of sequences whose blocks end at or before L (counted over
+    // the lanes; every lane of the block is still active here)
+    const int L = blockIdx.x;
+    const int ln = (int)threadIdx.x & 63;
+    const int io = ln < vt.n ? vt.item_off[ln + 1] : INT_MAX;
+    b = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(io <= L)));
+    blk = L - vt.item_off[b];
+  } else {
+    b = blockIdx.y;
+    blk = blockIdx.x;
+  }
   // the sequence's rows: b * n_tok .. + n_tok, or its packed run
   const int len = VAR ? vt.row_off[b + 1] - vt.row_off[b] : n_tok;
   const long long srow = VAR ? (long long)vt.row_off[b] : (long long)b * n_tok;
   const int tb = (int)threadIdx.x / cpt;  // token of this thread within the block's run
-  const int t = blockIdx.x * tok_per_block + tb;
+  const int t = blk * tok_per_block + tb;
   if (tb >= tok_per_block || t >= len) return;
   const int s0 = start[b];
   const int last = s0 + len - 1;
@@ -105,11 +119,23 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
   const int threads = 256;
   const int cpt = sh.Hkv * (sh.D / 8);
   const int tok_per_block = cpt <= threads ? threads / cpt : 1;
-  const long long bx = ((long long)n_tok + tok_per_block - 1) / tok_per_block;
+  long long bx = ((long long)n_tok + tok_per_block - 1) / tok_per_block;
   if (bx > INT32_MAX || sh.B > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)bx, (unsigned)sh.B);
-  const VarTab none{};
-  const VarTab& t = vt ? *vt : none;
+  dim3 grid((unsigned)bx, (unsigned)sh.B);
+  VarTab t{};
+  if (vt) {
+    // varlen: exactly the blocks each sequence needs, numbered in sequence order
+    t = *vt;
+    t.item_off[0] = 0;
+    for (int j = 0; j < t.n; ++j) {
+      const long long len = t.row_off[j + 1] - t.row_off[j];
+      const long long next = t.item_off[j] + (len + tok_per_block - 1) / tok_per_block;
+      if (next > INT32_MAX) return hipErrorInvalidValue;
+      t.item_off[j + 1] = (int)next;
+    }
+    if (t.item_off[t.n] == 0) return hipSuccess;
+    grid = dim3((unsigned)t.item_off[t.n], 1u);
+  }
   if (f32) {
     if (vt)
       cache_write_kernel<true, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
