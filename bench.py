@@ -266,6 +266,8 @@ def main():
         result["context"] = context_timings(swa, synth, torch, dev)
         result["context"]["decode_32_layers"] = decode_layers(swa, synth, torch, dev)
         result["context"]["varlen_mixed_batch"] = varlen_mixed(swa, synth, torch, dev)
+        result["context"]["vanilla_vs_swa_16k"] = vanilla_vs_swa_decode(swa, synth, torch, dev,
+                                                                        result["context"])
 
     # ------------------------------------------------------------------
     # CPU baseline: the oracle on a bounded sample of the prefill workload
@@ -416,6 +418,52 @@ def varlen_mixed(swa, synth, torch, dev, n_prefill=4, chunk=1024, reps=10):
     }
     del kc, vc
     return res
+
+
+def vanilla_vs_swa_decode(swa, synth, torch, dev, ctx16, B=64, steps=64, n_gen=256):
+    """Decode at 16K context, full cache (window 16384 = every position: plain
+    causal attention) against the 4096-slot rolling buffer, 64 sequences;
+    with the 16K prefill timings, the time of prefilling 16K tokens and
+    generating n_gen more, both ways."""
+    bf = torch.bfloat16
+    wl = synth.workload(3)
+    N, Hq, Hkv, D = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    g = torch.Generator(device=dev).manual_seed(3016)
+    res = {}
+    for name, W in (("swa", wl.window), ("full", N)):
+        p = swa.make_params(B, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+        kc = torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        vc = torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        q = torch.randn((B, Hq, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        k = torch.randn((B, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        v = torch.randn((B, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(swa.swa_decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        # positions 16384 - steps .. 16383: the last tokens of a 16K context
+        pos = [torch.full((B,), N - steps + s, dtype=torch.int32, device=dev) for s in range(steps)]
+        for s in range(4):
+            swa.swa_decode_step(p, q, k, v, kc, vc, pos[s], out, lse, ws)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for s in range(steps):
+            swa.swa_decode_step(p, q, k, v, kc, vc, pos[s], out, lse, ws)
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / steps
+        del kc, vc
+    swa_total = ctx16["chunked_swa_prefill"]["ms"] + n_gen * res["swa"]
+    full_total = ctx16["full_causal_prefill"]["ms"] + n_gen * res["full"]
+    return {
+        "batch": B, "context": N, "window": wl.window,
+        "ms_per_decode_step_swa": round(res["swa"], 4), "ms_per_decode_step_full": round(res["full"], 4),
+        "decode_full_over_swa_time": round(res["full"] / res["swa"], 3),
+        "note": f"end to end = the 16K prefill (batch 1) + {n_gen} decode steps of the batch",
+        "end_to_end_ms_swa": round(swa_total, 3), "end_to_end_ms_full": round(full_total, 3),
+        "end_to_end_full_over_swa_time": round(full_total / swa_total, 3),
+    }
 
 
 def context_timings(swa, synth, torch, dev):
