@@ -91,7 +91,7 @@ typedef struct swa_params {
   int32_t n_kv_heads;  /* key/value heads, >= 1                                 */
   int32_t head_dim;    /* 64 or 128                                             */
   int32_t window;      /* W >= 1: rolling slots; keys i-W < j <= i              */
-  int32_t n_sink;      /* 0 <= n_sink <= 64 sink positions with fixed slots     */
+  int32_t n_sink;      /* 0 <= n_sink <= 4096 global prefix positions (sinks)   */
   float scale;         /* softmax scale; 0 means 1/sqrt(head_dim)               */
   float rope_theta;    /* RoPE base; 0 disables RoPE                            */
   int32_t dtype;       /* swa_dtype of q, k, v, out and the caches              */

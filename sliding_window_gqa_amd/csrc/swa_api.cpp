@@ -25,7 +25,7 @@ int check_params(const swa_params* p, Shape* sh) {
   if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1) return SWA_ERR_SHAPE;
   if (p->n_q_heads % p->n_kv_heads != 0) return SWA_ERR_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return SWA_ERR_SHAPE;
-  if (p->window < 1 || p->n_sink < 0 || p->n_sink > 64) return SWA_ERR_SHAPE;
+  if (p->window < 1 || p->n_sink < 0 || p->n_sink > 4096) return SWA_ERR_SHAPE;
   if ((long long)p->n_sink + p->window > (1LL << 30)) return SWA_ERR_SHAPE;
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return SWA_ERR_SHAPE;
   if (!(p->rope_theta >= 0.f) || !isfinite(p->rope_theta)) return SWA_ERR_SHAPE;

@@ -34,7 +34,7 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
                               const void* v, const int32_t* start, int n_tok, void* kdst,
                               void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st);
 
-// Fast bf16 prefill: head_dim 128, group size 4, n_sink <= 64.
+// Fast bf16 prefill: head_dim 128, group size 4.
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,

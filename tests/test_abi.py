@@ -51,7 +51,7 @@ BAD_PARAMS = [
     (dict(head_dim=96), swa.SWA_ERR_SHAPE),
     (dict(window=0), swa.SWA_ERR_SHAPE),
     (dict(n_sink=-1), swa.SWA_ERR_SHAPE),
-    (dict(n_sink=65), swa.SWA_ERR_SHAPE),
+    (dict(n_sink=4097), swa.SWA_ERR_SHAPE),
     (dict(batch=0), swa.SWA_ERR_SHAPE),
     (dict(scale=-1.0), swa.SWA_ERR_SHAPE),
     (dict(scale=float("nan")), swa.SWA_ERR_SHAPE),

@@ -24,7 +24,7 @@ def rnd(shape, tag, seq=0, dtype=torch.bfloat16, index=90):
 # ---------------------------------------------------------------------------
 # integer index work, bit-exact
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("W,S", [(4096, 0), (4092, 4), (100, 3), (4, 0), (1, 0), (64, 64)])
+@pytest.mark.parametrize("W,S", [(4096, 0), (4092, 4), (100, 3), (4, 0), (1, 0), (64, 64), (64, 300)])
 def test_debug_slots_and_mask_bit_exact(W, S):
     print(f"debug slots/mask W={W} n_sink={S}", flush=True)
     p = swa.make_params(1, 4, 1, 128, W, S)
@@ -107,6 +107,8 @@ PREFILL_CASES = [
     # four tiles ahead across several items (576 and 1032 items)
     (4, 32, 8, 128, 40, 0, torch.bfloat16, [1100, 300]),
     (2, 32, 8, 128, 16, 3, torch.bfloat16, [4100, 50]),
+    # a global prefix longer than the window: 4 sink tiles, the last one ragged
+    (2, 8, 2, 128, 64, 100, torch.bfloat16, [300, 77, 130]),
     # generic path
     (2, 4, 2, 64, 100, 0, torch.bfloat16, [130, 1, 70]),
     (1, 6, 2, 128, 50, 3, torch.float32, [90, 7, 40]),
@@ -181,6 +183,7 @@ DECODE_CASES = [
     (2, 4, 1, 128, 4092, 4, torch.bfloat16),
     (3, 4, 2, 64, 100, 0, torch.bfloat16),   # generic path
     (2, 4, 1, 64, 100, 2, torch.float32),    # generic path
+    (2, 8, 2, 128, 64, 100, torch.bfloat16),  # a global prefix longer than the window
 ]
 
 
