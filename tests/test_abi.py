@@ -198,3 +198,20 @@ def test_step_varlen_workspace():
         assert lib.swa_step_varlen(bp, *args, _lens(1, 30, 1, 0), FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     assert lib.swa_step_varlen(bp, *([FAKE] * 6), _lens(1, 30, 1, 0), FAKE, None, FAKE, nbytes - 1,
                                None) == swa.SWA_ERR_WORKSPACE
+
+
+def test_step_varlen_workspace_over_several_decode_launches():
+    """70 one-token sequences decode in two launches (64 + 6); the smaller
+    launch takes more splits, and the workspace holds the larger need."""
+    lib = swa.library()
+    p = P(batch=70)
+
+    def splits(b):   # one round of ~512 work-groups, at most one per 128 slots
+        return max(1, min(-(-512 // (b * 8)), -(-4096 // 128)))
+
+    part = max(b * 32 * splits(b) * 130 * 4 for b in (64, 6))
+    keys = -(-(70 * 8 * 128 * 2) // 256) * 256
+    assert lib.swa_step_varlen_workspace_bytes(ctypes.byref(p), _lens(*([1] * 70))) == keys + part
+    # float32: keys at 4 bytes per element
+    p32 = P(batch=3, dtype=swa.SWA_F32)
+    assert lib.swa_prefill_varlen_workspace_bytes(ctypes.byref(p32), _lens(5, 0, 7)) == 12 * 8 * 128 * 4
