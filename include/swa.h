@@ -47,7 +47,8 @@
  *
  * OWNERSHIP: the caller allocates and owns every buffer, including the
  * workspaces whose sizes the *_workspace_bytes functions return.  The library
- * keeps no state between calls and allocates nothing; calls on different
+ * keeps no state between calls (beyond each device's compute-unit count,
+ * read once) and allocates nothing; calls on different
  * streams with disjoint buffers may run concurrently.
  *
  * ERRORS: arguments are checked on the host before any HIP call; a bad
