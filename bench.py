@@ -268,6 +268,7 @@ def main():
         result["context"]["varlen_mixed_batch"] = varlen_mixed(swa, synth, torch, dev)
         result["context"]["vanilla_vs_swa_16k"] = vanilla_vs_swa_decode(swa, synth, torch, dev,
                                                                         result["context"])
+        result["context"]["decode_small_batches"] = decode_small_batches(swa, synth, torch, dev)
 
     # ------------------------------------------------------------------
     # CPU baseline: the oracle on a bounded sample of the prefill workload
@@ -464,6 +465,64 @@ def vanilla_vs_swa_decode(swa, synth, torch, dev, ctx16, B=64, steps=64, n_gen=2
         "end_to_end_ms_swa": round(swa_total, 3), "end_to_end_ms_full": round(full_total, 3),
         "end_to_end_full_over_swa_time": round(full_total / swa_total, 3),
     }
+
+
+def decode_small_batches(swa, synth, torch, dev, batches=(1, 8), steps=64):
+    """Per-token latency of one decode step (swa_decode_step: cache write +
+    split-K attention + combine) at small batches, full windows of 4096."""
+    bf = torch.bfloat16
+    wl = synth.workload(4)
+    Hq, Hkv, D, W = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    g = torch.Generator(device=dev).manual_seed(4100)
+    res = {}
+    for B in batches:
+        p = swa.make_params(B, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf)
+        kc = torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        vc = torch.randn((B, W, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        q = torch.randn((B, Hq, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        k = torch.randn((B, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        v = torch.randn((B, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(bf)
+        out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(swa.swa_decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        pos = [torch.full((B,), 10000 + s, dtype=torch.int32, device=dev) for s in range(steps)]
+
+        def run():
+            for s in range(steps):
+                swa.swa_decode_step(p, q, k, v, kc, vc, pos[s], out, lse, ws)
+
+        def timed(fn):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps * 1e3
+
+        run()
+        torch.cuda.synchronize()
+        us_eager = timed(run)
+        # the same steps captured once in a graph (no host work per step)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            run()
+        graph.replay()
+        torch.cuda.synchronize()
+        us = timed(graph.replay)
+        nbytes = B * W * Hkv * D * 2 * 2
+        res[f"b{B}"] = {"us_per_step_graph": round(us, 2), "gbps_graph": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "us_per_step_eager_launches": round(us_eager, 2), "kv_bytes": nbytes}
+        del graph, kc, vc
+    res["note"] = ("4096-slot windows full; each step = decode_step (+ combine); graph: the steps captured "
+                   "in one HIP graph and replayed; eager: one Python call per step (host-bound at batch 1)")
+    return res
 
 
 def context_timings(swa, synth, torch, dev):

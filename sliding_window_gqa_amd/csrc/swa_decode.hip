@@ -476,22 +476,41 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(Shape sh, RopeTab rt
 // ---------------------------------------------------------------------------
 // Combine: one work-group per (query head, sequence), one thread per head dim.
 // ---------------------------------------------------------------------------
+// Combine: one block of D threads per (sequence, query head); thread d owns
+// element d.  The splits' maxima and sums come in with one load per split,
+// spread over the block, and each split's weight 2^(m_s - m*) is formed
+// once; the partial outputs are then loaded eight splits at a time, so that
+// the block waits for memory a few times rather than once per split.  The
+// sums run over the splits in ascending order.
+constexpr int kMaxSplits = 512;   // decode_splits() never exceeds it
 template <bool F32>
-__global__ void decode_combine_kernel(Shape sh, const float* part, int n_splits, void* out,
-                                      float* lse, DecodeMap map) {
+__global__ void __launch_bounds__(128) decode_combine_kernel(Shape sh, const float* part, int n_splits,
+                                                             void* out, float* lse, DecodeMap map) {
+  __shared__ float sm_m[kMaxSplits], sm_l[kMaxSplits], sm_f[kMaxSplits];
   const int h = blockIdx.x, z = blockIdx.y, d = threadIdx.x;
   const int r = map.n ? map.row[z] : z;   // the token's row in out
   const int D = sh.D;
   const float* src = part + ((long long)z * sh.Hq + h) * n_splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, src[s * (D + 2) + D]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float ms = src[s * (D + 2) + D];
-    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    L += src[s * (D + 2) + D + 1] * f;
-    O += src[s * (D + 2) + d] * f;
+  for (int s = d; s < n_splits; s += D) {
+    sm_m[s] = src[s * (D + 2) + D];
+    sm_l[s] = src[s * (D + 2) + D + 1];
   }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, sm_m[s]);
+  for (int s = d; s < n_splits; s += D) sm_f[s] = (sm_m[s] == -INFINITY) ? 0.f : exp2f(sm_m[s] - M);
+  __syncthreads();
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < n_splits; ++s) L += sm_l[s] * sm_f[s];
+  int s = 0;
+  for (; s + 8 <= n_splits; s += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = src[(s + u) * (D + 2) + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) O += x[u] * sm_f[s + u];
+  }
+  for (; s < n_splits; ++s) O += src[s * (D + 2) + d] * sm_f[s];
   const float val = O / L;
   const long long off = ((long long)r * sh.Hq + h) * D + d;
   if (F32)
@@ -515,6 +534,7 @@ int decode_splits(const Shape& sh) {
   int n = (512 + units - 1) / units;
   const int max_n = (sh.S + 4 * kChunk - 1) / (4 * kChunk);
   if (n > max_n) n = max_n;
+  if (n > kMaxSplits) n = kMaxSplits;   // (the combine's LDS; 512 / units never exceeds it)
   if (n < 1) n = 1;
   return n;
 }

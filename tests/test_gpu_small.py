@@ -437,3 +437,53 @@ def test_step_varlen(case):
         assert_close(out[r:r + n].cpu(), ro, atol, rrms, f"seq {b} out")
         assert_lse(lse[:, r:r + n].cpu(), rl, latol, f"seq {b} lse")
         r += n
+
+
+def test_decode_step_graph_replay():
+    """Decode steps captured in a HIP graph (the library allocates nothing
+    and records no memset): every replay, started from the caches the eager
+    steps started from (restored by eager copies between replays, with a
+    synchronisation), reproduces the eager outputs, LSE and caches bit for
+    bit."""
+    print("decode step graph replay", flush=True)
+    B, Hq, Hkv, D, W, S = 3, 8, 2, 128, 100, 2
+    gpu = GpuSide(B, Hq, Hkv, D, W, S)
+    hist = rnd((B, 150, Hkv, D), "hist_k", 0), rnd((B, 150, Hkv, D), "hist_v", 0)
+    gpu.write(hist[0], hist[1], [0] * B)
+    steps = [(rnd((B, Hq, D), "step_q", s, index=93).to(DEV), rnd((B, Hkv, D), "step_k", s, index=93).to(DEV),
+              rnd((B, Hkv, D), "step_v", s, index=93).to(DEV),
+              torch.tensor([150 + s, 160 + s, 170 + s], dtype=torch.int32, device=DEV)) for s in range(6)]
+    kc0, vc0 = gpu.kc.clone(), gpu.vc.clone()
+    ws = torch.empty(swa.swa_decode_workspace_bytes(gpu.p), dtype=torch.uint8, device=DEV)
+    eager = [swa.swa_decode_step(gpu.p, q, k, v, gpu.kc, gpu.vc, pos, workspace=ws) for q, k, v, pos in steps]
+    kc_e, vc_e = gpu.kc.clone(), gpu.vc.clone()
+    outs = [(torch.empty_like(o), torch.empty_like(l)) for o, l in eager]
+    gpu.kc.copy_(kc0)
+    gpu.vc.copy_(vc0)
+
+    def run():
+        for (q, k, v, pos), (o, l) in zip(steps, outs):
+            swa.swa_decode_step(gpu.p, q, k, v, gpu.kc, gpu.vc, pos, o, l, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        gpu.kc.copy_(kc0)
+        gpu.vc.copy_(vc0)
+        for o, l in outs:
+            o.zero_()
+            l.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s, ((o, l), (eo, el)) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, eo) and torch.equal(l, el), f"replay {rep} step {s}"
+        assert torch.equal(gpu.kc.view(torch.uint8), kc_e.view(torch.uint8)), f"replay {rep} k cache"
+        assert torch.equal(gpu.vc.view(torch.uint8), vc_e.view(torch.uint8)), f"replay {rep} v cache"
+        _ = (gpu.kc.float().sum() + 1).item()   # eager work between replays
