@@ -166,3 +166,57 @@ def test_workload5_sink_streaming():
             for b, r in ref.items():
                 check_rows(o[b], l[b], r, rows, torch.bfloat16, f"chunk seq {b}")
             p = p + C
+
+
+def test_mixed_varlen_step_b64():
+    """The mixed batch of the benchmark's context at full size: 64 sequences
+    with full 4096-slot windows, 4 of them prefill a 1024-token chunk and 60
+    decode one token, in one swa_step_varlen.  The oracle follows 8 sequences
+    (the 4 chunks on sampled rows, 4 decodes) through their history and the
+    step."""
+    wl = synth.workload(4)
+    print("mixed varlen step b64", flush=True)
+    B, Hq, Hkv, D, W = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    n_pre, chunk = 4, 1024
+    lens = [chunk] * n_pre + [1] * (B - n_pre)
+    starts = synth.positions(94, B, W, 32768).numpy().astype(np.int64)
+    seqs = [0, 1, 2, 3, 4, 17, 40, 63]
+    gpu = GpuSide(B, Hq, Hkv, D, W)
+    orc = OracleSide(seqs, Hkv, D, W)
+    # history: the W positions before each start (N(0,1) keys taken as already rotated)
+    p_one = swa.make_params(1, Hq, Hkv, D, W, 0, 0.0, 0.0)
+    for b in range(B):
+        kh = synth.normal((1, W, Hkv, D), 94, "hist_k", b)
+        vh = synth.normal((1, W, Hkv, D), 94, "hist_v", b)
+        lo = int(starts[b]) - W
+        swa.swa_cache_write(p_one, kh.to(DEV), vh.to(DEV), torch.tensor([lo], dtype=torch.int32, device=DEV),
+                            gpu.kc[b:b + 1], gpu.vc[b:b + 1])
+        if b in orc.caches:
+            orc.caches[b].write(np64(kh[0]), np64(vh[0]), np.arange(lo, int(starts[b])))
+    T = sum(lens)
+    q = synth.normal((T, Hq, D), 94, "chunk_q")
+    k = synth.normal((T, Hkv, D), 94, "chunk_k")
+    v = synth.normal((T, Hkv, D), 94, "chunk_v")
+    st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    out, lse = swa.swa_step_varlen(gpu.p, q.to(DEV), k.to(DEV), v.to(DEV), gpu.kc, gpu.vc, st, lens)
+    o, l = out.cpu(), lse.cpu()
+    rows = sample_rows(chunk, 6, 94, [0, 1, 63, 64, 1023])
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for b in seqs:
+        r0, n = int(offs[b]), lens[b]
+        if n > 1:
+            ref = so.prefill_chunk(orc.caches[b], np64(q[r0:r0 + n]), np64(k[r0:r0 + n]), np64(v[r0:r0 + n]),
+                                   int(starts[b]), 10000.0, rows=rows)
+            check_rows(o[r0:r0 + n], l[:, r0:r0 + n], ref, rows, torch.bfloat16, f"chunk seq {b}")
+        else:
+            ref = so.prefill_chunk(orc.caches[b], np64(q[r0:r0 + 1]), np64(k[r0:r0 + 1]), np64(v[r0:r0 + 1]),
+                                   int(starts[b]), 10000.0)
+            check_rows(o[r0:r0 + 1], l[:, r0:r0 + 1], ref, np.array([0]), torch.bfloat16, f"decode seq {b}")
+        # the rolling buffer after the step holds the oracle's entries (which
+        # now include the step's): values verbatim, keys to bf16 rounding
+        c = orc.caches[b]
+        held = c.tag >= 0
+        kc_b, vc_b = np64(gpu.kc[b]), np64(gpu.vc[b])
+        np.testing.assert_array_equal(vc_b[held], c.v[held])
+        err = np.abs(kc_b[held] - c.k[held])
+        assert (err <= 2.0 ** -8 * np.abs(c.k[held]) + 1e-6).all(), (b, err.max())
