@@ -487,3 +487,28 @@ def test_decode_step_graph_replay():
         assert torch.equal(gpu.kc.view(torch.uint8), kc_e.view(torch.uint8)), f"replay {rep} k cache"
         assert torch.equal(gpu.vc.view(torch.uint8), vc_e.view(torch.uint8)), f"replay {rep} v cache"
         _ = (gpu.kc.float().sum() + 1).item()   # eager work between replays
+
+
+def test_decode_long_window_wrap():
+    """A 16384-slot buffer (the window of the 16K full-cache comparison)
+    filled to its last slot and wrapping to slot 0, through both decode forms,
+    against the oracle."""
+    print("decode long window wrap", flush=True)
+    B, Hq, Hkv, D, W = 1, 8, 2, 128, 16384
+    gpu = GpuSide(B, Hq, Hkv, D, W)
+    orc = OracleSide(range(B), Hkv, D, W)
+    p0 = W - 6
+    kh = rnd((1, p0, Hkv, D), "hist_k", 0, index=95)
+    vh = rnd((1, p0, Hkv, D), "hist_v", 0, index=95)
+    gpu.write(kh, vh, [0])
+    orc.write(kh, vh, [0])
+    atol, rrms, latol = tol(torch.bfloat16)
+    for st in range(12):   # positions W-6 .. W+5: the fill point, then slots 0..5 overwritten
+        q = rnd((B, Hq, D), "step_q", st, index=95)
+        k = rnd((B, Hkv, D), "step_k", st, index=95)
+        v = rnd((B, Hkv, D), "step_v", st, index=95)
+        pos = [p0 + st]
+        out, lse = gpu.decode(q, k, v, pos, fused=st % 2 == 1)
+        ref = orc.decode(q, k, v, pos)
+        assert_close(out[0], ref[0][0], atol, rrms, f"step {st} out")
+        assert_lse(lse[0], ref[0][1], latol, f"step {st} lse")
