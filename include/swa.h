@@ -79,7 +79,7 @@ typedef enum swa_status {
   SWA_ERR_NULL = -1,        /* a required pointer is NULL                        */
   SWA_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes                */
   SWA_ERR_DTYPE = -3,       /* unknown dtype                                     */
-  SWA_ERR_UNSUPPORTED = -4, /* valid request this build does not implement        */
+  SWA_ERR_UNSUPPORTED = -4, /* valid request the library does not implement      */
   SWA_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required   */
   SWA_ERR_LAUNCH = -6       /* a kernel launch failed (hipGetLastError)          */
 } swa_status;
