@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
                                                          const void* __restrict__ v,
                                                          const int32_t* __restrict__ start, int n_tok,
                                                          void* __restrict__ kdst, void* __restrict__ vdst,
-                                                         int mode, int tok_per_block, VarTab vt) {
+                                                         int mode, int tok_per_block, int t_lo, VarTab vt) {
   const int cpr = sh.D / 8;           // chunks per (token, head) row: 8 or 16
   const int cpt = sh.Hkv * cpr;       // chunks per token
   int b, blk;
@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
   const int len = VAR ? vt.row_off[b + 1] - vt.row_off[b] : n_tok;
   const long long srow = VAR ? (long long)vt.row_off[b] : (long long)b * n_tok;
   const int tb = (int)threadIdx.x / cpt;  // token of this thread within the block's run
-  const int t = blk * tok_per_block + tb;
+  const int t = t_lo + blk * tok_per_block + tb;
   if (tb >= tok_per_block || t >= len) return;
   const int s0 = start[b];
   const int last = s0 + len - 1;
@@ -119,7 +119,10 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
   const int threads = 256;
   const int cpt = sh.Hkv * (sh.D / 8);
   const int tok_per_block = cpt <= threads ? threads / cpt : 1;
-  long long bx = ((long long)n_tok + tok_per_block - 1) / tok_per_block;
+  // Without sinks only the last W tokens of a run can survive it, whatever
+  // its start: the grid begins there (the per-token test stays exact).
+  const int t_lo = (!vt && mode == kToCache && sh.n_sink == 0 && n_tok > sh.W) ? n_tok - sh.W : 0;
+  long long bx = ((long long)(n_tok - t_lo) + tok_per_block - 1) / tok_per_block;
   if (bx > INT32_MAX || sh.B > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)bx, (unsigned)sh.B);
   VarTab t{};
@@ -139,17 +142,17 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
   if (f32) {
     if (vt)
       cache_write_kernel<true, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                     (int)mode, tok_per_block, t);
+                                                                     (int)mode, tok_per_block, t_lo, t);
     else
       cache_write_kernel<true, false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                      (int)mode, tok_per_block, t);
+                                                                      (int)mode, tok_per_block, t_lo, t);
   } else {
     if (vt)
       cache_write_kernel<false, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                      (int)mode, tok_per_block, t);
+                                                                      (int)mode, tok_per_block, t_lo, t);
     else
       cache_write_kernel<false, false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                       (int)mode, tok_per_block, t);
+                                                                       (int)mode, tok_per_block, t_lo, t);
   }
   return hipGetLastError();
 }
