@@ -28,7 +28,22 @@ def rope_brute(vec, p, theta):
     return out
 
 
-def attend_brute(q, k, v, window, n_sink=0, scale=None):
+def _keys_of(i, window, n_sink, dilation):
+    """Positions a query at i attends, built by walking back from i in steps
+    of `dilation` while inside the window, then adding the sink positions not
+    already listed."""
+    keys = []
+    j = i
+    while j >= 0 and j > i - window:
+        keys.append(j)
+        j -= dilation
+    for s in range(min(n_sink, i + 1)):
+        if s not in keys:
+            keys.append(s)
+    return sorted(keys)
+
+
+def attend_brute(q, k, v, window, n_sink=0, scale=None, dilation=1):
     """q: [N][Hq][D], k, v: [N][Hkv][D] nested lists for positions 0..N-1
     (already rotated).  Returns (out [N][Hq][D], lse [Hq][N])."""
     N = len(q)
@@ -41,7 +56,7 @@ def attend_brute(q, k, v, window, n_sink=0, scale=None):
     out = [[[0.0] * D for _ in range(Hq)] for _ in range(N)]
     lse = [[0.0] * N for _ in range(Hq)]
     for i in range(N):
-        keys = [j for j in range(0, i + 1) if (i - window < j) or (j < n_sink)]
+        keys = _keys_of(i, window, n_sink, dilation)
         for h in range(Hq):
             g = h // G
             scores = [scale * math.fsum(q[i][h][d] * k[j][g][d] for d in range(D)) for j in keys]

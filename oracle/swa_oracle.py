@@ -43,6 +43,14 @@ Readings of the pages (each is also listed in the design notes):
 * Softmax scale: 1/sqrt(D) unless given.
 * Chunked prefill: the chunk's queries attend to the cache as it stood before
   the chunk plus the chunk itself (causal); the chunk is written afterwards.
+* Dilation (the digest names Longformer's dilated sliding window as the
+  hybrid to try next: "Longformer vs Mistral SWA — 구조적 비교", Open
+  Questions (ii), "Discussion"; no page defines it): with dilation d >= 1 the
+  window part keeps only the keys j with i - W < j <= i and (i - j) divisible
+  by d, i.e. i, i-d, i-2d, ...: ceil(W/d) keys once the history is long
+  enough.  W stays the span in positions, so the W-slot rolling buffer still
+  holds every key a query can read; Longformer's "w keys with gaps d" is the
+  case W = w*d.  Sinks are unaffected.  d = 1 is plain SWA.
 """
 from __future__ import annotations
 
@@ -93,19 +101,22 @@ def rope(x, pos, theta):
 # ---------------------------------------------------------------------------
 # The key set A(i)
 # ---------------------------------------------------------------------------
-def key_mask(qpos, kpos, window, n_sink=0):
+def key_mask(qpos, kpos, window, n_sink=0, dilation=1):
     """Boolean [Tq, Tk]: key at position kpos[j] is in the key set of the query
     at qpos[i].
 
     SWA mask of the digest page ("핵심 구성요소") and the explainer's SWA
     equation, read as  i - W < j <= i  (W keys including the query itself),
     joined with the sink prefix j < n_sink of the aionda page.  Keys with a
-    negative position (an empty cache slot) are never in the set.
+    negative position (an empty cache slot) are never in the set.  With
+    dilation d the window part keeps only the keys whose distance i - j is a
+    multiple of d (the dilated sliding window the digest lists for
+    Longformer; reading in the module header).
     """
     qi = np.asarray(qpos, dtype=np.int64)[:, None]
     kj = np.asarray(kpos, dtype=np.int64)[None, :]
     causal = (kj <= qi) & (kj >= 0)
-    in_window = kj > qi - int(window)
+    in_window = (kj > qi - int(window)) & ((qi - kj) % int(dilation) == 0)
     is_sink = kj < int(n_sink)
     return causal & (in_window | is_sink)
 
@@ -113,12 +124,13 @@ def key_mask(qpos, kpos, window, n_sink=0):
 # ---------------------------------------------------------------------------
 # Attention over an explicit set of keys
 # ---------------------------------------------------------------------------
-def swa_attention(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256):
+def swa_attention(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256, dilation=1):
     """Sliding-window GQA attention, by definition.
 
     q [Tq, Hq, D], k and v [Tk, Hkv, D] (already rotated if RoPE is used),
-    qpos [Tq], kpos [Tk] absolute positions.  Returns (out [Tq, Hq, D],
-    lse [Hq, Tq]) where, for query head h and KV head g = h // (Hq/Hkv),
+    qpos [Tq], kpos [Tk] absolute positions; A(i) is key_mask's set (with
+    ``dilation``).  Returns (out [Tq, Hq, D], lse [Hq, Tq]) where, for query
+    head h and KV head g = h // (Hq/Hkv),
         s_ij = scale * q_i . k_j          for j in A(i)
         o_i  = sum_j softmax_j(s_i) v_j   (two-pass: subtract the row max)
         lse_i = log sum_j exp(s_ij)       (natural log)
@@ -140,7 +152,7 @@ def swa_attention(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pa
     lse = np.empty((Hq, Tq), dtype=np.float64)
     for r0 in range(0, Tq, rows_per_pass):
         r1 = min(Tq, r0 + rows_per_pass)
-        mask = key_mask(qpos[r0:r1], kpos, window, n_sink)
+        mask = key_mask(qpos[r0:r1], kpos, window, n_sink, dilation)
         if not mask.any(axis=1).all():
             raise ValueError("a query has an empty key set")
         for h in range(Hq):
@@ -171,9 +183,11 @@ class RollingCache:
     by that tag, never by inverting the slot map.
     """
 
-    def __init__(self, n_kv_heads, head_dim, window, n_sink=0):
+    def __init__(self, n_kv_heads, head_dim, window, n_sink=0, dilation=1):
         self.window = int(window)
         self.n_sink = int(n_sink)
+        # the key set the sequence's queries use (the slots do not depend on it)
+        self.dilation = int(dilation)
         S = self.n_sink + self.window
         self.k = np.zeros((S, n_kv_heads, head_dim), dtype=np.float64)
         self.v = np.zeros((S, n_kv_heads, head_dim), dtype=np.float64)
@@ -241,7 +255,8 @@ def prefill_chunk(cache, q, k, v, start, theta=10000.0, scale=None, rows=None):
     kpos = np.concatenate([cpos, pos])
     sel = np.arange(C) if rows is None else np.asarray(rows, dtype=np.int64)
     q_rot = rope(np.asarray(q)[sel], pos[sel], theta)
-    out, lse = swa_attention(q_rot, keys, vals, pos[sel], kpos, cache.window, cache.n_sink, scale)
+    out, lse = swa_attention(q_rot, keys, vals, pos[sel], kpos, cache.window, cache.n_sink, scale,
+                             dilation=cache.dilation)
     cache.write(k_rot, np.asarray(v, dtype=np.float64), pos)
     return out, lse
 
@@ -258,5 +273,6 @@ def decode_step(cache, q, k, v, p, theta=10000.0, scale=None):
     cache.write(k_rot, np.asarray(v, dtype=np.float64)[None], pos)
     q_rot = rope(np.asarray(q)[None], pos, theta)
     ck, cv, cpos = cache.entries()
-    out, lse = swa_attention(q_rot, ck, cv, pos, cpos, cache.window, cache.n_sink, scale)
+    out, lse = swa_attention(q_rot, ck, cv, pos, cpos, cache.window, cache.n_sink, scale,
+                             dilation=cache.dilation)
     return out[0], lse[:, 0]

@@ -12,18 +12,35 @@ _real_rope = so.rope
 _real_attention = so.swa_attention
 
 
-def mask_wide(qpos, kpos, window, n_sink=0):            # i - W <= j <= i  (W + 1 keys)
-    return _real_mask(qpos, kpos, window + 1, n_sink)
+def mask_wide(qpos, kpos, window, n_sink=0, dilation=1):       # i - W <= j <= i  (W + 1 keys)
+    return _real_mask(qpos, kpos, window + 1, n_sink, dilation)
 
 
-def mask_excl_self(qpos, kpos, window, n_sink=0):       # i - W <= j < i  (self excluded)
+def mask_excl_self(qpos, kpos, window, n_sink=0, dilation=1):  # i - W <= j < i  (self excluded)
     qi = np.asarray(qpos)[:, None]
     kj = np.asarray(kpos)[None, :]
     return (kj < qi) & (kj >= qi - window) & (kj >= 0) | ((kj < n_sink) & (kj < qi) & (kj >= 0))
 
 
-def mask_no_sinks(qpos, kpos, window, n_sink=0):
-    return _real_mask(qpos, kpos, window, 0)
+def mask_no_sinks(qpos, kpos, window, n_sink=0, dilation=1):
+    return _real_mask(qpos, kpos, window, 0, dilation)
+
+
+def mask_dil_span(qpos, kpos, window, n_sink=0, dilation=1):   # the span grows to W*d (W keys)
+    return _real_mask(qpos, kpos, window * dilation, n_sink, dilation)
+
+
+def mask_dil_phase(qpos, kpos, window, n_sink=0, dilation=1):  # keys at distance 1 (mod d) instead of 0
+    qi = np.asarray(qpos, dtype=np.int64)[:, None]
+    kj = np.asarray(kpos, dtype=np.int64)[None, :]
+    causal = (kj <= qi) & (kj >= 0)
+    d = int(dilation)
+    win = (kj > qi - int(window)) & (((qi - kj) % d == (1 % d)) | (kj == qi))
+    return causal & (win | (kj < int(n_sink)))
+
+
+def mask_dil_ignored(qpos, kpos, window, n_sink=0, dilation=1):
+    return _real_mask(qpos, kpos, window, n_sink, 1)
 
 
 def rope_sign(x, pos, theta):                           # clockwise rotation
@@ -49,23 +66,24 @@ def rope_halves(x, pos, theta):                         # pairs (k, k + D/2) ins
     return out
 
 
-def attention_gqa_mod(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256):
+def attention_gqa_mod(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256, dilation=1):
     # head h uses KV head h % Hkv instead of h // G
     q = np.asarray(q, dtype=np.float64)
     Hq, Hkv = q.shape[1], np.asarray(k).shape[1]
     G = Hq // Hkv
     perm = np.array([(h % Hkv) * G + h // Hkv for h in range(Hq)])
     inv = np.argsort(perm)
-    o, l = _real_attention(q[:, inv], k, v, qpos, kpos, window, n_sink, scale, rows_per_pass)
+    o, l = _real_attention(q[:, inv], k, v, qpos, kpos, window, n_sink, scale, rows_per_pass, dilation)
     return o[:, perm], l[perm]
 
 
-def attention_no_scale(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256):
-    return _real_attention(q, k, v, qpos, kpos, window, n_sink, 1.0 if scale is None else scale, rows_per_pass)
+def attention_no_scale(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256, dilation=1):
+    return _real_attention(q, k, v, qpos, kpos, window, n_sink, 1.0 if scale is None else scale, rows_per_pass,
+                           dilation)
 
 
-def attention_kv_swapped(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256):
-    return _real_attention(q, v, k, qpos, kpos, window, n_sink, scale, rows_per_pass)
+def attention_kv_swapped(q, k, v, qpos, kpos, window, n_sink=0, scale=None, rows_per_pass=256, dilation=1):
+    return _real_attention(q, v, k, qpos, kpos, window, n_sink, scale, rows_per_pass, dilation)
 
 
 def prefill_write_first(cache, q, k, v, start, theta=10000.0, scale=None):
@@ -75,7 +93,8 @@ def prefill_write_first(cache, q, k, v, start, theta=10000.0, scale=None):
     k_rot = so.rope(k, pos, theta)
     cache.write(k_rot, np.asarray(v, dtype=np.float64), pos)
     ck, cv, cpos = cache.entries()
-    return so.swa_attention(so.rope(q, pos, theta), ck, cv, pos, cpos, cache.window, cache.n_sink, scale)
+    return so.swa_attention(so.rope(q, pos, theta), ck, cv, pos, cpos, cache.window, cache.n_sink, scale,
+                            dilation=cache.dilation)
 
 
 class CacheFirstWriterWins(so.RollingCache):
@@ -105,6 +124,10 @@ MUTATIONS = [
     ("prefill_chunk", prefill_write_first, lambda: pins.test_chunked_prefill_equals_unchunked(16, 0)),
     ("RollingCache", CacheFirstWriterWins, lambda: pins.test_rolling_buffer_w4_worked_example()),
     ("RollingCache", CacheSlotModFull, lambda: pins.test_rolling_decode_reproduces_full_sequence(3)),
+    ("key_mask", mask_dil_span, lambda: pins.test_dilated_scale_zero_counts_and_mean_position(12, 0, 3)),
+    ("key_mask", mask_dil_phase, lambda: pins.test_dilation_is_swa_within_each_residue(3)),
+    ("key_mask", mask_dil_ignored, lambda: pins.test_dilated_matches_brute_force(14, 4, 2, 4, 9, 0, 2)),
+    ("key_mask", mask_dil_span, lambda: pins.test_dilated_rolling_decode_reproduces_full_sequence(0, 3)),
 ]
 
 

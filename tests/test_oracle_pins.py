@@ -371,3 +371,114 @@ def test_decode_is_invariant_under_slot_permutation():
     perm = rng.permutation(len(cpos))
     o2, _ = swa_attention(q, ck[perm], cv[perm], [30 - 1], cpos[perm], W)
     np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-13)
+
+
+def test_kv_cache_bytes_absolute():
+    """The byte count itself, not only the 32K / 4096 ratio: K and V buffers of
+    shape (W, n_kv_heads, head_dim) per layer (digest "핵심 구성요소"), bf16,
+    32 layers (the architecture table of the digest's "Methods").  Measured
+    against the bytes of a real RollingCache's two arrays, rescaled from
+    float64 to a 2-byte element, and against the product written out."""
+    shape = {r[0]: int(r[1]) for r in _golden_rows("mistral7b_attention_shape.txt")}
+    W, L, H, D = 4096, shape["n_layers"], shape["n_kv_heads"], shape["head_dim"]
+    cache = RollingCache(H, D, window=W)
+    per_layer = (cache.k.nbytes + cache.v.nbytes) // cache.k.itemsize * 2
+    assert kv_cache_bytes(W, 1, H, D, 2) == per_layer
+    assert kv_cache_bytes(W, L, H, D, 2) == L * per_layer == 536_870_912
+
+
+# ---------------------------------------------------------------------------
+# Dilation (the dilated sliding window the digest lists for Longformer): the
+# window part keeps the keys i, i-d, i-2d, ... inside i - W < j <= i
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,Hq,Hkv,D,W,S,d", [
+    (14, 4, 2, 4, 9, 0, 2), (17, 2, 1, 6, 12, 2, 3), (11, 4, 1, 4, 5, 1, 5), (13, 4, 2, 4, 20, 0, 4),
+    (9, 2, 1, 4, 4, 0, 1),
+])
+def test_dilated_matches_brute_force(N, Hq, Hkv, D, W, S, d):
+    rng = np.random.default_rng(N * 13 + W + 7 * d)
+    q, k, v = _rand(rng, N, Hq, D), _rand(rng, N, Hkv, D), _rand(rng, N, Hkv, D)
+    pos = np.arange(N)
+    out, lse = swa_attention(q, k, v, pos, pos, W, n_sink=S, dilation=d)
+    bo, bl = attend_brute(q.tolist(), k.tolist(), v.tolist(), W, n_sink=S, dilation=d)
+    np.testing.assert_allclose(out, np.array(bo), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("W,S,d", [(12, 0, 3), (10, 0, 4), (4096, 0, 2), (4092, 4, 3), (9, 5, 2), (7, 0, 1)])
+def test_dilated_scale_zero_counts_and_mean_position(W, S, d):
+    """scale = 0: exp(lse) counts the keys.  The window part is the progression
+    i, i-d, ..., with n = min(ceil(W/d), floor(i/d) + 1) terms and mean
+    i - d(n-1)/2; the sinks add the positions below min(S, i+1) that the
+    progression does not hit (those of its terms that are below S)."""
+    N = 3 * W + 5 if W < 100 else W + 300
+    pos = np.arange(N)
+    q = np.ones((N, 1, 2))
+    k = np.ones((N, 1, 2))
+    v = np.repeat(pos.astype(np.float64)[:, None, None], 2, axis=2)
+    out, lse = swa_attention(q, k, v, pos, pos, W, n_sink=S, scale=0.0, rows_per_pass=512, dilation=d)
+    for i in range(N):
+        n = min(-(-W // d), i // d + 1)
+        win_sum = n * i - d * n * (n - 1) // 2
+        # progression terms below S: k with i - k d < S, i.e. k >= floor((i - S) / d) + 1
+        k_lo = 0 if i < S else min(n, (i - S) // d + 1)
+        n_low = n - k_lo
+        low_sum = sum(i - kk * d for kk in range(k_lo, n))     # (at most S terms)
+        m = min(S, i + 1)
+        n_extra = m - n_low
+        extra_sum = m * (m - 1) // 2 - low_sum
+        count = n + n_extra
+        assert round(math.exp(lse[0, i])) == count, (i, count)
+        assert abs(lse[0, i] - math.log(count)) < 1e-12
+        assert abs(out[i, 0, 0] - (win_sum + extra_sum) / count) < 1e-9
+
+
+@pytest.mark.parametrize("d", [2, 3, 5])
+def test_dilation_is_swa_within_each_residue(d):
+    """Without sinks, dilated attention never mixes positions of different
+    residues mod d: its rows of residue r equal plain SWA (same W, absolute
+    positions) over the positions of residue r alone."""
+    W, N, Hq, Hkv, D = 11, 47, 4, 2, 8
+    rng = np.random.default_rng(100 + d)
+    q, k, v = _rand(rng, N, Hq, D), _rand(rng, N, Hkv, D), _rand(rng, N, Hkv, D)
+    pos = np.arange(N)
+    out, lse = swa_attention(q, k, v, pos, pos, W, dilation=d)
+    for r in range(d):
+        sub = pos[pos % d == r]
+        o_r, l_r = swa_attention(q[sub], k[sub], v[sub], sub, sub, W)
+        np.testing.assert_allclose(out[sub], o_r, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[:, sub], l_r, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("S,d", [(0, 3), (2, 2), (3, 4)])
+def test_dilated_rolling_decode_reproduces_full_sequence(S, d):
+    """With W the span in positions, the W-slot rolling buffer holds every key
+    of a dilated query: rolling decode of 0..N-1 gives the full-sequence rows."""
+    W, N, Hq, Hkv, D, theta = 9, 40, 4, 1, 8, 10000.0
+    rng = np.random.default_rng(20 + S + 10 * d)
+    q, k, v = _sequence(rng, N, Hq, Hkv, D)
+    pos = np.arange(N)
+    ref, ref_lse = swa_attention(rope(q, pos, theta), rope(k, pos, theta), v, pos, pos, W, n_sink=S, dilation=d)
+    cache = RollingCache(Hkv, D, W, n_sink=S, dilation=d)
+    for p in range(N):
+        o, l = decode_step(cache, q[p], k[p], v[p], p, theta)
+        np.testing.assert_allclose(o, ref[p], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(l, ref_lse[:, p], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,d", [(16, 2), (5, 3), (1, 2)])
+def test_dilated_chunked_prefill_equals_unchunked(C, d):
+    W, N, Hq, Hkv, D, theta, S = 14, 53, 4, 2, 8, 10000.0, 2
+    rng = np.random.default_rng(C * 5 + d)
+    q, k, v = _sequence(rng, N, Hq, Hkv, D)
+    pos = np.arange(N)
+    ref, ref_lse = swa_attention(rope(q, pos, theta), rope(k, pos, theta), v, pos, pos, W, n_sink=S, dilation=d)
+    cache = RollingCache(Hkv, D, W, n_sink=S, dilation=d)
+    outs, lses = [], []
+    for s in range(0, N, C):
+        e = min(N, s + C)
+        o, l = prefill_chunk(cache, q[s:e], k[s:e], v[s:e], s, theta)
+        outs.append(o)
+        lses.append(l)
+    np.testing.assert_allclose(np.concatenate(outs), ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(lses, axis=1), ref_lse, rtol=1e-11, atol=1e-12)
