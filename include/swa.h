@@ -127,7 +127,9 @@ size_t swa_prefill_workspace_bytes(const swa_params* params, int32_t chunk_len);
  *   q         : [batch][chunk_len][n_q_heads][head_dim] raw queries.
  *   k, v      : [batch][chunk_len][n_kv_heads][head_dim] raw keys, values.
  *   k_cache, v_cache : the caches as they stand before the chunk (positions
- *               < start_pos[b]); may both be NULL when every start_pos is 0.
+ *               < start_pos[b]); both NULL means no position before the
+ *               chunk exists (a sequence's first chunk): the queries then
+ *               attend only the chunk's keys.
  *   start_pos : device int32[batch], position of the chunk's first token.
  *   out       : [batch][chunk_len][n_q_heads][head_dim].
  *   lse       : float32 [batch][n_q_heads][chunk_len], or NULL.

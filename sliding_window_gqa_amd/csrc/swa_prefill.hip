@@ -226,8 +226,11 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // u0 = t0 + 32k).  Band tiles cover chunk-relative key positions
   // t0 - W + 1 .. t0 + 63; sink tiles cover absolute positions 0 ..
   // n_sink-1 for queries whose window no longer contains them.
+  // Without caches (k_cache NULL) no position before the chunk exists: sa,
+  // the number of positions before the chunk that can be read, is s0 with a
+  // cache and 0 without, and keys below s0 - sa are outside every key set.
   struct Item {
-    int b, kvh, t0, s0, n_stile, kmin, n_tiles;
+    int b, kvh, t0, s0, sa, n_stile, kmin, n_tiles;
     int row0, len;   // varlen: the sequence's first packed row, its length
   };
   // The start positions are read through the constant address space, so
@@ -263,10 +266,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       it.len = C;
     }
     it.s0 = start_c[it.b];
+    it.sa = a.kc ? it.s0 : 0;
     const int tq_last = min(it.t0 + BM, it.len) - 1;
-    it.n_stile = (nsink > 0 && (it.s0 + tq_last - W) >= 0) ? (nsink + BN - 1) / BN : 0;
+    // sink tiles: some readable sink lies outside the window of some query
+    it.n_stile = (nsink > it.s0 - it.sa && tq_last - W + it.sa >= 0) ? (nsink + BN - 1) / BN : 0;
     const int k_lo = -((W - 1 + BN - 1) / BN);
-    const int k_clip = -((it.s0 + it.t0 + BN - 1) / BN);
+    const int k_clip = -((it.sa + it.t0 + BN - 1) / BN);
     it.kmin = max(k_lo, k_clip);
     it.n_tiles = it.n_stile + (2 - it.kmin);
     return it;
@@ -298,11 +303,33 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   int lr_round = 0, lt = 0;
   unsigned lslot = 0;           // LDS offset of the ring slot the next load fills
   int l_nt, l_ns, l_u0, l_s0;   // tiles, sink tiles, u0 of the first band tile, start
+  int l_nrec;                   // bytes of the item's rows of the chunk
   long long l_ec, l_es;         // element offset of the rows in the chunk, the cache
-  __amdgpu_buffer_rsrc_t rkc, rvc;   // the item's rows of the chunk's K and V
   auto rsrc = [&](const uint16_t* base, long long e, int nrec) __attribute__((always_inline)) {
     return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base + e), (short)0, nrec, 0x00020000);
   };
+  // Descriptors of the rows the next straight-path tile reads: the item's
+  // rows of the chunk's K and V (region 0) or of the caches (region 1; a
+  // chunk without a cache has none: nrec_s = 0 reads zeros).  They are made
+  // again only when the region changes, about twice per item, so that a
+  // cache tile issues like a chunk tile.
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int l_reg = -1;               // region rk / rv cover, -1 none
+  auto use_region = [&](int reg) __attribute__((always_inline)) {
+    if (reg != l_reg) {
+      if (reg == 0) {
+        rk = rsrc(a.kr, l_ec, l_nrec);
+        rv = rsrc(a.v, l_ec, l_nrec);
+      } else {
+        const long long e = a.kc ? l_es : 0;
+        rk = rsrc(a.kc ? a.kc : a.kr, e, nrec_s);
+        rv = rsrc(a.vc ? a.vc : a.v, e, nrec_s);
+      }
+      l_reg = reg;
+    }
+  };
+  int l_cm = -1;         // cache band tiles: see prepare()
+  int l_cmn = -1;        // l_cm of the item's next tile when it is a cache band tile, or -1
   auto set_cursor = [&](int L) __attribute__((always_inline)) {
     const Item it = item_params(L);
     l_nt = it.n_tiles;
@@ -311,18 +338,18 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     l_s0 = it.s0;
     l_ec = VAR ? ((long long)it.row0 * sh.Hkv + it.kvh) * HD : ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
     l_es = ((long long)it.b * S * sh.Hkv + it.kvh) * HD;
-    const int nrec = VAR ? (it.len - 1) * (int)rowbytes + HD * 2 : nrec_c;
-    rkc = rsrc(a.kr, l_ec, nrec);
-    rvc = rsrc(a.v, l_ec, nrec);
+    l_nrec = VAR ? (it.len - 1) * (int)rowbytes + HD * 2 : nrec_c;
+    l_reg = -1;
+    l_cmn = -1;
   };
   set_cursor(item_at(0));
   // The next load is prepared one step ahead (prepare(), run while the
   // previous loads are awaited) and issued by issue(): band tiles of the
-  // chunk, the common case, take the straight path with the uniform part of
-  // their offsets (l_srow) ready.
-  int l_slow = -1;       // >= 0 iff the next tile is a band tile of the chunk
+  // chunk and cache band tiles whose rows are consecutive slots, the common
+  // cases, take the straight path with the uniform part of their offsets
+  // (l_srow) and their region's descriptors ready.
+  int l_slow = -1;       // >= 0 iff the next tile takes the straight path
   int l_srow = 0;        // its uniform byte offset
-  int l_cm = -1;         // cache band tiles: see prepare()
   auto prepare = [&]() __attribute__((always_inline)) {
     if (lt >= l_nt) {
       const int L = item_at(lr_round + 1);
@@ -333,29 +360,39 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       }
     }
     const int u0 = l_u0 + BN * lt;
-    l_slow = __builtin_amdgcn_readfirstlane((lt - l_ns) | u0);
-    l_srow = __builtin_amdgcn_readfirstlane(u0 * (int)rowbytes);
-    asm volatile("" : "+s"(l_slow), "+s"(l_srow));   // (computed here, in the wait's shadow)
-    if (l_slow < 0 && lt >= l_ns) {
-      // cache band tile: the rolling-buffer slot of the wave's first row,
-      // less n_sink, when all its rows lie past the sinks
-      const int P0 = l_s0 + u0 + 4 * w;
-      l_cm = P0 >= nsink ? (int)((unsigned)(P0 - nsink) % (unsigned)W) : -1;
+    int reg = -1, srow = 0;
+    if (lt >= l_ns) {
+      if (u0 >= 0) {
+        reg = 0;                                   // band tile of the chunk
+        srow = u0 * (int)rowbytes;
+      } else {
+        // cache band tile: the rolling-buffer slot of the wave's first row,
+        // less n_sink, when all its rows lie past the sinks; consecutive
+        // cache tiles of an item are 32 slots apart
+        const int P0 = l_s0 + u0 + 4 * w;
+        if (P0 >= nsink) {
+          l_cm = l_cmn >= 0 ? l_cmn : (int)((unsigned)(P0 - nsink) % (unsigned)W);
+          const int nx = l_cm + BN >= W ? l_cm + BN - W : l_cm + BN;
+          l_cmn = nx < W ? nx : -1;
+          if (l_cm + 3 < W) {
+            reg = 1;                               // its 4 rows per wave are consecutive slots
+            srow = (nsink + l_cm - 4 * w) * (int)rowbytes;
+          }
+        } else {
+          l_cm = -1;
+        }
+      }
     }
+    l_slow = __builtin_amdgcn_readfirstlane(reg);
+    l_srow = __builtin_amdgcn_readfirstlane(srow);
+    asm volatile("" : "+s"(l_slow), "+s"(l_srow));   // (computed here, in the wait's shadow)
+    if (l_slow >= 0) use_region(l_slow);
   };
   // load the prepared tile into its ring slot
   auto issue = [&]() __attribute__((always_inline)) {
     const unsigned lk = lds_ring + lslot;
     if (__builtin_expect(l_slow >= 0, 1)) {
-      dma16x2(rkc, l_srow + vrk, lk, rvc, l_srow + vrv, lk + KTILEB);
-    } else if (lt >= l_ns && l_cm >= 0 && l_cm + 3 < W) {
-      // cache band tile whose 4 rows per wave are consecutive slots: the
-      // lane offsets of a chunk tile, the uniform part from the slot
-      // (a chunk without a cache has no cache rows: nrec_s = 0 reads zeros)
-      const int srow = (nsink + l_cm - 4 * w) * (int)rowbytes;
-      const long long e = a.kc ? l_es : 0;
-      dma16x2(rsrc(a.kc ? a.kc : a.kr, e, nrec_s), srow + vrk, lk,
-              rsrc(a.vc ? a.vc : a.v, e, nrec_s), srow + vrv, lk + KTILEB);
+      dma16x2(rk, l_srow + vrk, lk, rv, l_srow + vrv, lk + KTILEB);
     } else {
       // (lane offsets recomputed here rather than held in registers)
       int ln_ = lane;
@@ -372,8 +409,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
           dma16(rsrc(a.vc, l_es, nrec_s), P * (int)rowbytes + dv_, lk + KTILEB);
         } else {
           const int rr = min(max(P - l_s0, 0), C - 1) * (int)rowbytes;
-          dma16(rkc, rr + dk_, lk);
-          dma16(rvc, rr + dv_, lk + KTILEB);
+          dma16(rsrc(a.kr, l_ec, l_nrec), rr + dk_, lk);
+          dma16(rsrc(a.v, l_ec, l_nrec), rr + dv_, lk + KTILEB);
         }
       } else {
         // cache rows (a chunk without a cache has none: nrec_s = 0 reads zeros)
@@ -482,7 +519,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   Item it = item_params(L);
   load_qf(it);
   for (int round = 0;; ++round) {
-    const int b = it.b, kvh = it.kvh, t0 = it.t0, s0 = it.s0;
+    const int b = it.b, kvh = it.kvh, t0 = it.t0, s0 = it.s0, sa = it.sa;
     const int n_stile = it.n_stile, kmin = it.kmin, n_tiles = it.n_tiles;
     const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
     const int tq = q0w + i;                 // this lane's query
@@ -590,23 +627,27 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // range jlo <= j <= jhi (>> 5 is the floor division by 32).
     const int mfull = kmin - n_stile, dq = q0w - t0;
     const int jhi = ((dq - (BN - 1)) >> 5) - mfull;
-    const int jlo = max(max(n_stile, ((dq + 15 - W) >> 5) + 1 - mfull), -((s0 + t0) >> 5) - mfull);
+    const int jlo = max(max(n_stile, ((dq + 15 - W) >> 5) + 1 - mfull), -((sa + t0) >> 5) - mfull);
     auto mask_kind = [&](int j) __attribute__((always_inline)) {
       if (j < n_stile) return 2;
       return (j >= jlo && j <= jhi) ? 0 : 1;
     };
     // Each kind is one interval test per key: sink key P (absolute) is kept
-    // iff P <= min(n_sink - 1, I - W); band key u (chunk-relative) iff
-    // max(tq - W + 1, -s0) <= u <= tq (a non-empty interval: tq >= 0 >= -s0).
+    // iff s0 - sa <= P <= min(n_sink - 1, I - W); band key u (chunk-relative)
+    // iff max(tq - W + 1, -sa) <= u <= tq (a non-empty interval: tq >= 0 >= -sa).
     auto apply_mask = [&](int j, int mk, floatx4 (&s)[2][QB]) __attribute__((always_inline)) {
       int k0, lo, span;   // key index of row 0 of this lane, interval [lo, lo + span]
       if (mk == 2) {
         k0 = BN * j + 4 * g;
-        lo = INT_MIN / 2;
+        lo = a.kc ? INT_MIN / 2 : s0;
         span = min(nsink - 1, I - W) - lo;
+        if (span < 0) {   // (no readable sink for this query: a one-key interval no key is in)
+          lo = INT_MIN / 2 + 1;
+          span = 0;
+        }
       } else {
         k0 = band_u0(j) + 4 * g;
-        lo = max(tq - W + 1, -s0);
+        lo = max(tq - W + 1, -sa);
         span = tq - lo;
       }
 #pragma unroll

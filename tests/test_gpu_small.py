@@ -150,6 +150,30 @@ def test_prefill_chunks(case):
         t += C
 
 
+@pytest.mark.parametrize("D,S", [(128, 0), (128, 3), (64, 3)])
+def test_prefill_without_cache_at_nonzero_start(D, S):
+    """No caches (k_cache = v_cache = NULL) with chunks that start past 0:
+    no position before the chunk exists, so the queries attend only the
+    chunk's own keys (and the sinks that lie inside the chunk).  The oracle
+    sees the same with an empty rolling cache.  D = 128 runs the fast kernel,
+    D = 64 the generic one."""
+    print(f"prefill without cache, nonzero start, D={D} n_sink={S}", flush=True)
+    B, Hq, Hkv, W, theta = 3, 8, 2, 100, 10000.0
+    C = 150
+    starts = [50, 1000, 2]
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, theta)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta)
+    q = rnd((B, C, Hq, D), "q", 41)
+    k = rnd((B, C, Hkv, D), "k", 41)
+    v = rnd((B, C, Hkv, D), "v", 41)
+    out, lse = gpu.prefill(q, k, v, starts, use_cache=False)
+    ref = orc.prefill(q, k, v, starts)
+    atol, rrms, latol = tol(torch.bfloat16)
+    for b in range(B):
+        assert_close(out[b], ref[b][0], atol, rrms, f"seq {b} out")
+        assert_lse(lse[b], ref[b][1], latol, f"seq {b} lse")
+
+
 def test_prefill_key_counts_exact():
     """A (near) zero softmax scale makes every weight exactly 1, so exp(lse)
     counts the keys each query attended: an end-to-end integer check of the
