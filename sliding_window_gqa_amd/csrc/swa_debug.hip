@@ -1,6 +1,14 @@
-// swa_debug.hip — test hooks that run the device index functions the kernels
-// use (slot map of the rolling buffer, key-set predicate) over caller arrays,
-// so that integer conventions can be compared bit-exactly with the oracle.
+// swa_debug.hip — test hooks that run the device index functions of
+// swa_device.hpp over caller arrays, so that the integer conventions can be
+// compared bit-exactly with the oracle:
+//  * slot_of is the slot map itself: the cache-write kernel, the decode
+//    kernel's store of the new entry and the generic prefill kernel call it;
+//  * key_in_set is the key set A(i) written as one predicate; only this hook
+//    calls it.  The fast prefill kernel applies the same set as interval
+//    bounds (a closed-form tile range and one interval test per key), the
+//    fast decode kernel as the range of live slots, and the generic kernels
+//    as loop bounds; the key-count tests (scale ~ 0, exp(lse) = |A(i)|)
+//    check those end to end against the closed form.
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
 

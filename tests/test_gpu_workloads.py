@@ -15,10 +15,15 @@ from tests.gpu_harness import DEV, GpuSide, OracleSide, np64
 pytestmark = pytest.mark.gpu
 
 
-def sample_rows(C, n_random, seed, fixed):
+def sample_rows(C, n_random, seed, fixed, per_tile=True):
+    """Query rows the oracle evaluates: the fixed ones (tile and window edges),
+    n_random more, and one random row of every 64-query tile (every work item
+    of the persistent prefill grid is then compared somewhere)."""
     g = np.random.default_rng(seed)
     rows = set(int(r) for r in fixed if 0 <= r < C)
     rows |= set(int(x) for x in g.choice(C, size=min(n_random, C), replace=False))
+    if per_tile:
+        rows |= set(int(t0 + g.integers(min(64, C - t0))) for t0 in range(0, C, 64))
     return np.array(sorted(rows))
 
 
@@ -160,11 +165,13 @@ def test_workload5_sink_streaming():
             kc = synth.normal((B, C, Hkv, D), 5, "chunk_k")
             vc = synth.normal((B, C, Hkv, D), 5, "chunk_v")
             out, lse = gpu.prefill(qc, kc, vc, p)
-            rows = sample_rows(C, 6, 55, [0, 1, 4095])
-            ref = orc.prefill(qc, kc, vc, p, rows=rows)
             o, l = out.cpu(), lse.cpu()
-            for b, r in ref.items():
-                check_rows(o[b], l[b], r, rows, torch.bfloat16, f"chunk seq {b}")
+            for i, b in enumerate(orc.seqs):
+                # every 64-query tile on half the followed sequences
+                rows = sample_rows(C, 6, 55 + b, [0, 1, 4095], per_tile=i % 2 == 0)
+                ref = so.prefill_chunk(orc.caches[b], np64(qc[b]), np64(kc[b]), np64(vc[b]), int(p[b]),
+                                       orc.theta, orc.scale, rows=rows)
+                check_rows(o[b], l[b], ref, rows, torch.bfloat16, f"chunk seq {b}")
             p = p + C
 
 
