@@ -47,11 +47,30 @@ def profiled_traffic(name, sources):
     t = re.search(r"traffic_bytes: (\d+)", text)
     if not h or not t:
         return None
+    return int(t.group(1)) if source_hash(sources) == h.group(1) else None
+
+
+def profiled_avg_us(name, sources):
+    """rocprofv3's average duration (us) of the profile's kernel from the
+    committed summary profiles/<name>.txt, or None when it was taken on other
+    sources than the ones built now."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", name + ".txt")).read()
+    except OSError:
+        return None
+    h = re.search(r"source_sha256_16: (\w+)", text)
+    a = re.search(r"kernel_avg_us: ([0-9.]+)", text)
+    if not h or not a or h.group(1) != source_hash(sources):
+        return None
+    return float(a.group(1))
+
+
+def source_hash(sources):
     sha = hashlib.sha256()
     for f in sources:
         with open(os.path.join(ROOT, "sliding_window_gqa_amd", "csrc", f), "rb") as fh:
             sha.update(fh.read())
-    return int(t.group(1)) if sha.hexdigest()[:16] == h.group(1) else None
+    return sha.hexdigest()[:16]
 
 
 def prewarm(fn, seconds, torch):
@@ -87,7 +106,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the chunked / full-causal / sink timings")
-    ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all",
+    ap.add_argument("--only", choices=["prefill", "decode", "chunked", "sink", "all"], default="all",
                     help="restrict the GPU work (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (scales HBM byte counters)")
@@ -140,6 +159,9 @@ def main():
     flops2 = attn_flops(pairs2)
 
     def prefill_step(ev=None):
+        # ev: events around the key rotation, the attention and the cache write
+        if ev is not None:
+            ev[2].record()
         swa.swa_rope_keys(p, k, start, k_rot)
         if ev is not None:
             ev[0].record()
@@ -147,13 +169,15 @@ def main():
         if ev is not None:
             ev[1].record()
         swa.swa_cache_write(p, k, v, start, kc, vc)
+        if ev is not None:
+            ev[3].record()
 
     if args.only in ("prefill", "all"):
         prewarm(prefill_step, args.prewarm_s, torch)
         for _ in range(args.warmup):
             prefill_step()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -165,9 +189,19 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         ms_step = t0.elapsed_time(t1) / args.steps
-        attn_times = sorted(a.elapsed_time(b) for a, b in evs)
+        attn_times = sorted(e[0].elapsed_time(e[1]) for e in evs)
         attn_ms = sum(attn_times) / args.steps
         achieved = flops2 / (attn_ms * 1e-3) / 1e12
+        rope_ms = sum(e[2].elapsed_time(e[0]) for e in evs) / args.steps
+        write_ms = sum(e[1].elapsed_time(e[3]) for e in evs) / args.steps
+        # key rotation: every key read and its rotation written; cache write:
+        # the surviving last W tokens' k and v read and stored (digest
+        # "쓰기(write) 단계": one writer per slot)
+        row = Hkv * D * 2
+        rope_bytes = 2 * N * row
+        write_bytes = 2 * 2 * min(N, W) * row
+        prof_us = profiled_avg_us("prefill_bf16_d128_g4_kernel.prefill_n8192_w4096",
+                                  ["swa_prefill.hip", "swa_device.hpp"])
         result.update({
             "value": round(flops2 / (ms_step * 1e-3) / 1e12, 2),
             "unit": "TFLOP/s",
@@ -188,7 +222,19 @@ def main():
                          "avg_kernel_ms": round(attn_ms, 4),
                          "median_kernel_ms": round(attn_times[len(attn_times) // 2], 4),
                          "min_kernel_ms": round(attn_times[0], 4),
-                         "timing": "HIP events around each attention launch in the timed region"},
+                         "timing": "HIP events around each attention launch in the timed region",
+                         "rocprof_avg_us": prof_us,
+                         "frac_from_rocprof_avg": (round(flops2 / (prof_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                                                   if prof_us else None)},
+            "small_kernels": {
+                "key_rotation": {"kernel": "cache_write_kernel (dense mode)", "avg_us": round(rope_ms * 1e3, 2),
+                                 "bytes": rope_bytes, "gbps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
+                                 "frac_hbm_peak": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+                "cache_write": {"kernel": "cache_write_kernel", "avg_us": round(write_ms * 1e3, 2),
+                                "bytes": write_bytes, "gbps": round(write_bytes / (write_ms * 1e-3) / 1e9, 1),
+                                "frac_hbm_peak": round(write_bytes / (write_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                "bound": "hbm"},
+                "timing": "HIP events around each launch in the timed region (launch included)"},
             "wall_s_timed_region": round(wall, 4),
         })
 
@@ -229,6 +275,7 @@ def main():
         for s in range(min(8, T)):
             dstep(s)
         torch.cuda.synchronize()
+        kc4_0, vc4_0 = kc4.clone(), vc4.clone()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -241,6 +288,20 @@ def main():
         dec_times = sorted(a.elapsed_time(b) for a, b in evs)
         dec_ms = sum(dec_times)
         dec_achieved = (dec_bytes + write_bytes) / (dec_ms * 1e-3) / 1e9
+        # the same 256 steps again, from the same cache state, with the
+        # Infinity Cache (MALL, 256 MB) flushed before each step by a 512 MiB fill
+        kc4.copy_(kc4_0)
+        vc4.copy_(vc4_0)
+        del kc4_0, vc4_0
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
+        for s in range(T):
+            flush.fill_(s & 255)
+            dstep(s, evf[s])
+        torch.cuda.synchronize()
+        del flush
+        fl_ms = sum(a.elapsed_time(b) for a, b in evf)
+        fl_gbps = (dec_bytes + write_bytes) / (fl_ms * 1e-3) / 1e9
         result["decode"] = {
             "workload": wl4.name, "batch": B4, "steps": T, "window": wl4.window,
             "value": round((dec_bytes + write_bytes) / (total_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
@@ -256,12 +317,17 @@ def main():
                          "avg_call_ms": round(dec_ms / T, 4),
                          "median_call_ms": round(dec_times[len(dec_times) // 2], 4),
                          "bytes": "valid K/V slots read once + Q + O + new k/v read and stored"},
+            "mall_flushed": {"avg_call_ms": round(fl_ms / T, 4), "gbps": round(fl_gbps, 1),
+                             "frac": round(fl_gbps / PEAK_HBM_GBPS, 4),
+                             "note": "same steps from the same cache state, a 512 MiB fill before each call"},
         }
         del kc4, vc4, qs, ks, vs
 
     # ------------------------------------------------------------------
     # context: chunked SWA vs full causal at 16K, sink streaming decode
     # ------------------------------------------------------------------
+    if not args.no_context and args.only in ("chunked", "sink"):
+        result["context"] = context_timings(swa, synth, torch, dev, args.only)
     if not args.no_context and args.only == "all":
         result["context"] = context_timings(swa, synth, torch, dev)
         result["context"]["decode_32_layers"] = decode_layers(swa, synth, torch, dev)
@@ -269,6 +335,7 @@ def main():
         result["context"]["vanilla_vs_swa_16k"] = vanilla_vs_swa_decode(swa, synth, torch, dev,
                                                                         result["context"])
         result["context"]["decode_small_batches"] = decode_small_batches(swa, synth, torch, dev)
+        result["context"]["tiny_fp32_prefill"] = tiny_fp32(swa, synth, torch, dev)
 
     # ------------------------------------------------------------------
     # CPU baseline: the oracle on a bounded sample of the prefill workload
@@ -467,6 +534,31 @@ def vanilla_vs_swa_decode(swa, synth, torch, dev, ctx16, B=64, steps=64, n_gen=2
     }
 
 
+def tiny_fp32(swa, synth, torch, dev, reps=50):
+    """The tiny float32 prefill (batch 1, N = 256, 4 query / 1 KV head,
+    head_dim 64, scale 1/8, no RoPE) at W = 64 and W = 256 (full causal):
+    absolute time of one swa_prefill_chunk call (parity workload; launch-bound)."""
+    wl = synth.workload(1)
+    N, Hq, Hkv, D = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    f32 = torch.float32
+    q = synth.normal((1, N, Hq, D), 1, "q", dtype=f32).to(dev)
+    k = synth.normal((1, N, Hkv, D), 1, "k", dtype=f32).to(dev)
+    v = synth.normal((1, N, Hkv, D), 1, "v", dtype=f32).to(dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {"workload": wl.name}
+    for W in (wl.window, wl.extra["full_window"]):
+        p = swa.make_params(1, Hq, Hkv, D, W, 0, wl.scale, 0.0, f32)
+        out = torch.empty((1, N, Hq, D), dtype=f32, device=dev)
+        lse = torch.empty((1, Hq, N), dtype=f32, device=dev)
+        ws = torch.empty(swa.swa_prefill_workspace_bytes(p, N), dtype=torch.uint8, device=dev)
+        ms = timeit(lambda: swa.swa_prefill_chunk(p, q, k, v, None, None, st, out, lse, ws), torch, reps)
+        pairs = band_pairs(N, W)
+        res[f"w{W}"] = {"us_per_call": round(ms * 1e3, 2), "key_pairs": pairs,
+                        "gflops": round(4 * D * Hq * pairs / (ms * 1e-3) / 1e9, 2)}
+    res["step"] = "prefill_chunk (key copy + float32 attention, generic kernel)"
+    return res
+
+
 def decode_small_batches(swa, synth, torch, dev, batches=(1, 8), steps=64):
     """Per-token latency of one decode step (swa_decode_step: cache write +
     split-K attention + combine) at small batches, full windows of 4096."""
@@ -525,9 +617,33 @@ def decode_small_batches(swa, synth, torch, dev, batches=(1, 8), steps=64):
     return res
 
 
-def context_timings(swa, synth, torch, dev):
+def context_timings(swa, synth, torch, dev, only="all"):
     """Chunked SWA prefill (4 x 4096 into a 4096-slot buffer) vs one full
-    causal pass at N = 16384, and the sink-streaming decode rate."""
+    causal pass at N = 16384 ("chunked"), and the sink-streaming workload's
+    decode rate and prefill chunk ("sink")."""
+    ctx = {}
+    if only in ("all", "chunked"):
+        ctx.update(chunked_vs_full(swa, synth, torch, dev))
+    if only in ("all", "sink"):
+        ctx.update(sink_workload(swa, synth, torch, dev))
+    return ctx
+
+
+def timeit(fn, torch, reps=5):
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def chunked_vs_full(swa, synth, torch, dev):
     bf = torch.bfloat16
     wl = synth.workload(3)
     N, Hq, Hkv, D, W, C = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.chunk
@@ -562,21 +678,8 @@ def context_timings(swa, synth, torch, dev):
     def full():
         swa.swa_prefill_chunk(pf, q, k, v, None, None, z, outf, lsef, wsf)
 
-    def timeit(fn, reps=5):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    swa_ms = timeit(chunked2)
-    full_ms = timeit(full)
+    swa_ms = timeit(chunked2, torch)
+    full_ms = timeit(full, torch)
     swa_flops = attn_flops(band_pairs(N, W))
     full_flops = attn_flops(band_pairs(N, N))
     ctx = {
@@ -589,9 +692,18 @@ def context_timings(swa, synth, torch, dev):
         "pages_claim": "about 2x faster than vanilla attention at 16K tokens, W=4096 (no hardware stated)",
     }
     del q, k, v, outf, wsf
+    return ctx
 
+
+def sink_workload(swa, synth, torch, dev):
+    """Sink streaming (B=16, 4 sinks + 4092 window): 256 decode steps with and
+    without a MALL flush, and the 4096-token prefill chunk per sequence."""
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(3005)
+    ctx = {}
     # sink streaming decode (B=16, 4 sinks + 4092 window): 256 steps
     wl5 = synth.workload(5)
+    Hq, Hkv, D = wl5.n_q_heads, wl5.n_kv_heads, wl5.head_dim
     B, S = wl5.batch, wl5.n_slots
     p5 = swa.make_params(B, Hq, Hkv, D, wl5.window, wl5.n_sink, 0.0, wl5.rope_theta, bf)
     kc5 = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(bf)
@@ -640,7 +752,7 @@ def context_timings(swa, synth, torch, dev):
     def chunk5():
         swa.swa_prefill_chunk(p5, q5c, k5c, v5c, kc5, vc5, st5, o5c, l5c, ws5c)
 
-    chunk_ms = timeit(chunk5)
+    chunk_ms = timeit(chunk5, torch)
     chunk_pairs = sum(band_pairs(C5, wl5.window, int(x), wl5.n_sink) for x in st5.cpu().tolist())
     ctx["sink_chunk_prefill"] = {
         "workload": wl5.name, "batch": B, "chunk": C5, "ms": round(chunk_ms, 4),
