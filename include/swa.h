@@ -81,7 +81,9 @@ typedef enum swa_status {
   SWA_ERR_DTYPE = -3,       /* unknown dtype                                     */
   SWA_ERR_UNSUPPORTED = -4, /* valid request the library does not implement      */
   SWA_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required   */
-  SWA_ERR_LAUNCH = -6       /* a kernel launch failed (hipGetLastError)          */
+  SWA_ERR_LAUNCH = -6,      /* a kernel launch failed (hipGetLastError)          */
+  SWA_ERR_SCRATCH = -7      /* the call needs more than the library's fixed
+                               scratch array (swa_decode_step_noalloc)           */
 } swa_status;
 
 typedef enum swa_dtype { SWA_BF16 = 0, SWA_F32 = 1 } swa_dtype;
@@ -260,6 +262,23 @@ int swa_decode(const swa_params* params, const void* q, const void* k_cache, con
 int swa_decode_step(const swa_params* params, const void* q, const void* k, const void* v,
                     void* k_cache, void* v_cache, const int32_t* pos, void* out, float* lse,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * swa_decode_step_noalloc — swa_decode_step without a workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, layouts,
+ * result and cache contents as swa_decode_step; the split-K partial results
+ * go to a fixed array of the library (swa_noalloc_scratch_bytes() bytes, one
+ * copy per device, held until the process ends).  Nothing is allocated.
+ * Calls that overlap in time on one GPU share that array and race: issue
+ * them one after the other (one stream, or synchronised streams).
+ * Errors as swa_decode_step, and SWA_ERR_SCRATCH (nothing launched) when
+ * swa_decode_workspace_bytes(params) exceeds the array.
+ */
+size_t swa_noalloc_scratch_bytes(void);
+int swa_decode_step_noalloc(const swa_params* params, const void* q, const void* k, const void* v,
+                            void* k_cache, void* v_cache, const int32_t* pos, void* out, float* lse,
+                            hipStream_t stream);
 
 /* Human-readable name of a swa_status value. */
 const char* swa_status_string(int status);

@@ -19,15 +19,15 @@ __all__ = [
     "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen", "swa_prefill_attention_varlen",
     "swa_prefill_chunk_varlen", "swa_cache_write_varlen", "swa_step_varlen",
     "swa_step_varlen_workspace_bytes",
-    "swa_debug_slots", "swa_debug_mask",
+    "swa_debug_slots", "swa_debug_mask", "swa_decode_step_noalloc", "swa_noalloc_scratch_bytes",
     "SWA_OK", "SWA_ERR_NULL", "SWA_ERR_SHAPE", "SWA_ERR_DTYPE", "SWA_ERR_UNSUPPORTED",
-    "SWA_ERR_WORKSPACE", "SWA_ERR_LAUNCH", "SWA_BF16", "SWA_F32",
+    "SWA_ERR_WORKSPACE", "SWA_ERR_LAUNCH", "SWA_ERR_SCRATCH", "SWA_BF16", "SWA_F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 
 SWA_OK, SWA_ERR_NULL, SWA_ERR_SHAPE, SWA_ERR_DTYPE = 0, -1, -2, -3
-SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_LAUNCH = -4, -5, -6
+SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_LAUNCH, SWA_ERR_SCRATCH = -4, -5, -6, -7
 SWA_BF16, SWA_F32 = 0, 1
 
 
@@ -72,6 +72,8 @@ _SIGNATURES = {
     "swa_cache_write_varlen": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "swa_step_varlen_workspace_bytes": (_sz, [_P, _vp]),
     "swa_step_varlen": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "swa_decode_step_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "swa_noalloc_scratch_bytes": (_sz, []),
     "swa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "swa_debug_slots": (ctypes.c_int, [_P, _vp, _i32, _vp, _vp]),
     "swa_debug_mask": (ctypes.c_int, [_P, _i32, _vp, _i32, _vp, _vp]),
@@ -289,6 +291,28 @@ def swa_decode_step(params, q, k, v, k_cache, v_cache, pos, out=None, lse=None, 
         _ptr(out, "out", dt, qshp), _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads)),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "swa_decode_step")
+    return out, lse
+
+
+def swa_noalloc_scratch_bytes() -> int:
+    return int(library().swa_noalloc_scratch_bytes())
+
+
+def swa_decode_step_noalloc(params, q, k, v, k_cache, v_cache, pos, out, lse=None, stream=None):
+    """swa_decode_step with the library's fixed scratch array instead of a
+    workspace: allocates nothing (out, and lse if wanted, are the caller's)."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    qshp = (params.batch, params.n_q_heads, params.head_dim)
+    kshp = (params.batch, params.n_kv_heads, params.head_dim)
+    cshp = (params.batch, params.n_sink + params.window, params.n_kv_heads, params.head_dim)
+    st = library().swa_decode_step_noalloc(
+        ctypes.byref(params), _ptr(q, "q", dt, qshp), _ptr(k, "k", dt, kshp), _ptr(v, "v", dt, kshp),
+        _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp),
+        _ptr(pos, "pos", torch.int32, (params.batch,)),
+        _ptr(out, "out", dt, qshp), _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads)),
+        _stream(stream))
+    _check(st, "swa_decode_step_noalloc")
     return out, lse
 
 

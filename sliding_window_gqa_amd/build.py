@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libswa.so")
 
-SOURCES = ["swa_api.cpp", "swa_write.hip", "swa_prefill.hip", "swa_decode.hip", "swa_debug.hip"]
+SOURCES = ["swa_api.cpp", "swa_write.hip", "swa_prefill.hip", "swa_decode.hip", "swa_debug.hip",
+           "swa_noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

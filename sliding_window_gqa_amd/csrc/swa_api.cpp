@@ -472,6 +472,7 @@ const char* swa_status_string(int status) {
     case SWA_ERR_UNSUPPORTED: return "SWA_ERR_UNSUPPORTED: not implemented for these arguments";
     case SWA_ERR_WORKSPACE: return "SWA_ERR_WORKSPACE: workspace missing or too small";
     case SWA_ERR_LAUNCH: return "SWA_ERR_LAUNCH: kernel launch failed";
+    case SWA_ERR_SCRATCH: return "SWA_ERR_SCRATCH: needs more than the fixed scratch array";
     default: return "unknown swa_status";
   }
 }

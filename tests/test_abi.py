@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported():
             "swa_debug_mask", "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen",
             "swa_prefill_attention_varlen", "swa_prefill_chunk_varlen",
             "swa_cache_write_varlen", "swa_step_varlen",
-            "swa_step_varlen_workspace_bytes"} <= set(names)
+            "swa_step_varlen_workspace_bytes", "swa_decode_step_noalloc",
+            "swa_noalloc_scratch_bytes"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -69,6 +70,7 @@ def test_bad_params_rejected_everywhere(bad, code):
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
+    assert lib.swa_decode_step_noalloc(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
     assert lib.swa_debug_slots(bp, FAKE, 4, FAKE, None) == code
     assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, FAKE, None) == code
     assert lib.swa_prefill_attention(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None) == code
@@ -132,7 +134,7 @@ def test_workspace_sizes():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = swa.swa_status_string(code)
         assert s.startswith("SWA_")
     assert "unknown" in swa.swa_status_string(42)
@@ -215,3 +217,22 @@ def test_step_varlen_workspace_over_several_decode_launches():
     # float32: keys at 4 bytes per element
     p32 = P(batch=3, dtype=swa.SWA_F32)
     assert lib.swa_prefill_varlen_workspace_bytes(ctypes.byref(p32), _lens(5, 0, 7)) == 12 * 8 * 128 * 4
+
+
+def test_noalloc_decode_rejects_on_the_host():
+    """The no-allocation decode step: null pointers, and shapes whose split-K
+    partials need more than the fixed scratch array, are rejected before any
+    HIP call."""
+    lib = swa.library()
+    assert lib.swa_noalloc_scratch_bytes() == 4 << 20
+    p = P(batch=4)
+    bp = ctypes.byref(p)
+    assert lib.swa_decode_step_noalloc(bp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == swa.SWA_ERR_NULL
+    assert lib.swa_decode_step_noalloc(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == swa.SWA_ERR_NULL
+    # 4096 sequences on the generic path (float32): one split each, but 4096 x 32
+    # partials of 130 floats = 68 MB > 4 MiB
+    big = P(batch=4096, dtype=swa.SWA_F32)
+    assert lib.swa_decode_workspace_bytes(ctypes.byref(big)) > lib.swa_noalloc_scratch_bytes()
+    assert lib.swa_decode_step_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                       None) == swa.SWA_ERR_SCRATCH
+    assert "scratch" in swa.swa_status_string(swa.SWA_ERR_SCRATCH)
