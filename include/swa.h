@@ -13,7 +13,11 @@
  * at absolute position j iff
  *       0 <= j <= i   and   ( i - window < j   or   j < n_sink )
  * i.e. `window` keys including itself, plus the first n_sink positions
- * (attention sinks).  Digest "핵심 구성요소" / explainer How It Works 2 give
+ * (attention sinks).  With dilation d > 1 the window part keeps only the keys
+ * with (i - j) divisible by d: i, i-d, i-2d, ... inside the same span, so the
+ * rolling buffer is unchanged (the dilated sliding window the digest lists
+ * for Longformer, "Longformer vs Mistral SWA — 구조적 비교"; the pages define
+ * none: this is the reading taken).  Digest "핵심 구성요소" / explainer How It Works 2 give
  * the SWA mask; this is its reading that matches a window-slot buffer that is
  * written before it is read (digest "Rolling Buffer KV Cache 동작 설명":
  * the query at p reads p-W+1 .. p).  The sink prefix follows the sinks page,
@@ -98,6 +102,8 @@ typedef struct swa_params {
   float scale;         /* softmax scale; 0 means 1/sqrt(head_dim)               */
   float rope_theta;    /* RoPE base; 0 disables RoPE                            */
   int32_t dtype;       /* swa_dtype of q, k, v, out and the caches              */
+  int32_t dilation;    /* d >= 1 (0 means 1): the window part keeps only the
+                          keys at distances 0, d, 2d, ... (below)              */
 } swa_params;
 
 /*

@@ -48,6 +48,7 @@ class swa_params(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("rope_theta", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("dilation", ctypes.c_int32),
     ]
 
 
@@ -104,12 +105,12 @@ def swa_status_string(status: int) -> str:
 
 
 def make_params(batch, n_q_heads, n_kv_heads, head_dim, window, n_sink=0, scale=0.0,
-                rope_theta=10000.0, dtype=SWA_BF16) -> swa_params:
+                rope_theta=10000.0, dtype=SWA_BF16, dilation=1) -> swa_params:
     if not isinstance(dtype, int):
         import torch
         dtype = SWA_F32 if dtype == torch.float32 else SWA_BF16
     return swa_params(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(window),
-                      int(n_sink), float(scale), float(rope_theta), int(dtype))
+                      int(n_sink), float(scale), float(rope_theta), int(dtype), int(dilation))
 
 
 # ---------------------------------------------------------------------------

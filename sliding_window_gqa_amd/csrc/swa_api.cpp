@@ -29,6 +29,7 @@ int check_params(const swa_params* p, Shape* sh) {
   if ((long long)p->n_sink + p->window > (1LL << 30)) return SWA_ERR_SHAPE;
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return SWA_ERR_SHAPE;
   if (!(p->rope_theta >= 0.f) || !isfinite(p->rope_theta)) return SWA_ERR_SHAPE;
+  if (p->dilation < 0 || p->dilation > (1 << 20)) return SWA_ERR_SHAPE;
   if (sh) {
     sh->B = p->batch;
     sh->Hq = p->n_q_heads;
@@ -40,6 +41,7 @@ int check_params(const swa_params* p, Shape* sh) {
     sh->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->head_dim));
     sh->scale_log2 = (float)((double)sh->scale * 1.4426950408889634);
     sh->rope = p->rope_theta > 0.f ? 1 : 0;
+    sh->dil = p->dilation > 1 ? p->dilation : 1;
   }
   return SWA_OK;
 }
@@ -58,7 +60,7 @@ bool fast_path(const swa_params* p) {
   const long long seq_cache_bytes =
       (long long)(p->n_sink + p->window) * p->n_kv_heads * p->head_dim * 2;
   return p->dtype == SWA_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads &&
-         seq_cache_bytes < (1LL << 31);
+         seq_cache_bytes < (1LL << 31) && p->dilation <= 1;
 }
 
 // The fast prefill kernel also addresses one sequence's chunk (Q, K, V, and

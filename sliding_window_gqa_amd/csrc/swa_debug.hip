@@ -22,7 +22,7 @@ __global__ void debug_slots_kernel(Shape sh, const int32_t* pos, int n, int32_t*
 
 __global__ void debug_mask_kernel(Shape sh, int q_pos, const int32_t* k_pos, int n, uint8_t* mask) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < n) mask[t] = key_in_set(q_pos, k_pos[t], sh.W, sh.n_sink) ? 1 : 0;
+  if (t < n) mask[t] = key_in_set(q_pos, k_pos[t], sh.W, sh.n_sink, sh.dil) ? 1 : 0;
 }
 
 }  // namespace

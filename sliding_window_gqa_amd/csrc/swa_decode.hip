@@ -435,6 +435,9 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(Shape sh, RopeTab rt
     const int slot = c0 + lane;
     int P = -1;
     if (slot < sp1) P = slot_position(slot, p, sh.W, sh.n_sink);
+    // a rolling slot's position is inside the window; with dilation it is a
+    // key only at a distance that is a multiple of dil
+    if (P >= sh.n_sink && (p - P) % sh.dil != 0) P = -1;
     float sc = -INFINITY;
     const long long roff = (((long long)b * sh.S + slot) * sh.Hkv + kvh) * D;
     if (P >= 0) {

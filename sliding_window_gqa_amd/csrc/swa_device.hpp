@@ -18,6 +18,7 @@ constexpr int kMaxPairs = 64;  // head_dim <= 128
 // Shape and constants of one call, passed by value to every kernel.
 struct Shape {
   int B, Hq, Hkv, D, W, n_sink, S;
+  int dil;          // dilation of the window part (1: plain SWA)
   float scale;      // softmax scale (already defaulted to 1/sqrt(D))
   float scale_log2; // scale * log2(e)
   int rope;         // 0: no RoPE
@@ -37,9 +38,10 @@ __host__ __device__ inline int slot_of(int p, int W, int n_sink) {
   return p < n_sink ? p : n_sink + (p - n_sink) % W;
 }
 
-// Key set A(i): 0 <= j <= i and (i - W < j or j < n_sink).
-__host__ __device__ inline bool key_in_set(int i, int j, int W, int n_sink) {
-  return j >= 0 && j <= i && (j > i - W || j < n_sink);
+// Key set A(i): 0 <= j <= i and ((i - W < j and (i - j) mod dil == 0) or
+// j < n_sink).
+__host__ __device__ inline bool key_in_set(int i, int j, int W, int n_sink, int dil) {
+  return j >= 0 && j <= i && ((j > i - W && (i - j) % dil == 0) || j < n_sink);
 }
 
 // Position held by slot `s` of a cache whose newest position is p (p has

@@ -107,7 +107,9 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, int off, unsigned lds)
 }
 
 // The K and the V row of one tile: as dma16, twice, with one save and
-// restore of M0.
+// restore of M0.  (The whole offset stays in the per-lane operand: the range
+// check of a raw buffer does not cover the scalar offset, and rows past the
+// end must read as zeros.)
 __device__ inline void dma16x2(__amdgpu_buffer_rsrc_t rk, int ok, unsigned lk,
                                __amdgpu_buffer_rsrc_t rv, int ov, unsigned lv) {
   unsigned saved;
@@ -954,9 +956,12 @@ __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab r
     for (int d = 0; d < D; ++d) o[d] = fmaf(o[d], al, pp * ld<F32>(vb, off + d));
     m = mn;
   };
+  // the window part I, I - dil, ... down to lo, and the sinks it does not hold
   const int lo = max(0, I - sh.W + 1);
-  for (int j = 0; j < min(sh.n_sink, lo); ++j) visit(j);
-  for (int j = lo; j <= I; ++j) visit(j);
+  const int dil = sh.dil;
+  for (int j = 0; j < min(sh.n_sink, I + 1); ++j)
+    if (j < lo || (I - j) % dil != 0) visit(j);
+  for (int j = I; j >= lo; j -= dil) visit(j);
   const float inv = 1.f / l;
   const long long ooff = ((r0 + t) * sh.Hq + h) * D;
 #pragma unroll

@@ -22,10 +22,10 @@ def np64(t: torch.Tensor) -> np.ndarray:
 
 class GpuSide:
     def __init__(self, B, Hq, Hkv, D, W, n_sink=0, theta=10000.0, dtype=torch.bfloat16, scale=0.0,
-                 fill=float("nan")):
+                 fill=float("nan"), dilation=1):
         self.dtype = dtype
-        self.p = swa.make_params(B, Hq, Hkv, D, W, n_sink, scale, theta, dtype)
-        self.p_norope = swa.make_params(B, Hq, Hkv, D, W, n_sink, scale, 0.0, dtype)
+        self.p = swa.make_params(B, Hq, Hkv, D, W, n_sink, scale, theta, dtype, dilation)
+        self.p_norope = swa.make_params(B, Hq, Hkv, D, W, n_sink, scale, 0.0, dtype, dilation)
         S = n_sink + W
         self.kc = torch.full((B, S, Hkv, D), fill, dtype=dtype, device=DEV)
         self.vc = torch.full((B, S, Hkv, D), fill, dtype=dtype, device=DEV)
@@ -59,11 +59,11 @@ class GpuSide:
 class OracleSide:
     """One oracle RollingCache per sequence (or per sampled sequence)."""
 
-    def __init__(self, seqs, Hkv, D, W, n_sink=0, theta=10000.0, scale=None):
+    def __init__(self, seqs, Hkv, D, W, n_sink=0, theta=10000.0, scale=None, dilation=1):
         self.seqs = list(seqs)
         self.theta = theta
         self.scale = scale
-        self.caches = {b: so.RollingCache(Hkv, D, W, n_sink) for b in self.seqs}
+        self.caches = {b: so.RollingCache(Hkv, D, W, n_sink, dilation) for b in self.seqs}
 
     def write(self, k, v, start, rope=True):
         """k, v: [B][n][Hkv][D] tensors (all sequences); start [B]."""

@@ -199,6 +199,125 @@ def test_prefill_key_counts_exact():
 
 
 # ---------------------------------------------------------------------------
+# dilated windows (the window part keeps keys i, i-d, i-2d, ...)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W,S,d", [(100, 0, 3), (64, 4, 2), (4096, 0, 2), (300, 100, 5)])
+def test_debug_mask_dilated_bit_exact(W, S, d):
+    print(f"debug mask W={W} n_sink={S} dilation={d}", flush=True)
+    p = swa.make_params(1, 4, 1, 128, W, S, dilation=d)
+    for qp in [0, 1, 2, 3, d, W - 1, W, W + 1, S + W + 5, 70001]:
+        kp = torch.arange(max(0, qp - W - 70), qp + 70, dtype=torch.int32)
+        kp = torch.cat([torch.arange(0, S + 3, dtype=torch.int32), kp])
+        m = swa.swa_debug_mask(p, qp, kp.to(DEV)).cpu().numpy().astype(bool)
+        np.testing.assert_array_equal(m, so.key_mask([qp], kp.numpy(), W, S, d)[0])
+
+
+DILATED_PREFILL = [
+    # (B, Hq, Hkv, D, W, n_sink, dilation, dtype, chunks)
+    (2, 8, 2, 128, 100, 0, 3, torch.bfloat16, [130, 1, 64, 65, 7]),
+    (2, 8, 2, 128, 100, 4, 2, torch.bfloat16, [130, 3, 100]),
+    (1, 8, 2, 128, 64, 100, 4, torch.bfloat16, [300, 77]),
+    (2, 4, 2, 64, 90, 2, 5, torch.bfloat16, [140, 9]),
+    (1, 6, 2, 128, 50, 3, 2, torch.float32, [90, 7, 40]),
+]
+
+
+@pytest.mark.parametrize("case", DILATED_PREFILL,
+                         ids=[f"B{c[0]}H{c[1]}/{c[2]}D{c[3]}W{c[4]}S{c[5]}d{c[6]}{str(c[7])[6:]}" for c in DILATED_PREFILL])
+def test_prefill_dilated(case):
+    B, Hq, Hkv, D, W, S, dil, dtype, chunks = case
+    print(f"dilated prefill {case}", flush=True)
+    theta = 10000.0
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype, dilation=dil)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta, dilation=dil)
+    atol, rrms, latol = tol(dtype)
+    offs = [0, 37][:B]
+    if B > 1:   # sequence 1 starts after 37 tokens already in its cache
+        kp = rnd((1, 37, Hkv, D), "hist_k", 1, dtype)
+        vp = rnd((1, 37, Hkv, D), "hist_v", 1, dtype)
+        sub = GpuSide(1, Hq, Hkv, D, W, S, theta, dtype, dilation=dil)
+        sub.write(kp, vp, [0])
+        gpu.kc[1] = sub.kc[0]
+        gpu.vc[1] = sub.vc[0]
+        gpu.has_cache = True
+        orc.caches[1].write(so.rope(np64(kp[0]), np.arange(37), theta), np64(vp[0]), np.arange(37))
+    t = 0
+    for ci, C in enumerate(chunks):
+        q = rnd((B, C, Hq, D), "q", 60 + ci, dtype)
+        k = rnd((B, C, Hkv, D), "k", 60 + ci, dtype)
+        v = rnd((B, C, Hkv, D), "v", 60 + ci, dtype)
+        start = [offs[b] + t for b in range(B)]
+        out, lse = gpu.prefill(q, k, v, start)
+        ref = orc.prefill(q, k, v, start)
+        for b in range(B):
+            assert_close(out[b], ref[b][0], atol, rrms, f"chunk {ci} seq {b} out")
+            assert_lse(lse[b], ref[b][1], latol, f"chunk {ci} seq {b} lse")
+        t += C
+
+
+@pytest.mark.parametrize("case", [(3, 8, 2, 128, 100, 0, 3, torch.bfloat16), (2, 8, 2, 128, 64, 4, 2, torch.bfloat16),
+                                  (2, 4, 1, 64, 100, 2, 4, torch.float32)])
+def test_decode_dilated(case):
+    """Decode steps through the fill point and wraps, both as cache write +
+    decode and as one decode step, against the oracle."""
+    B, Hq, Hkv, D, W, S, dil, dtype = case
+    print(f"dilated decode {case}", flush=True)
+    theta = 10000.0
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype, dilation=dil)
+    orc = OracleSide(range(B), Hkv, D, W, S, theta, dilation=dil)
+    atol, rrms, latol = tol(dtype)
+    p0 = [0, 57, 250][:B]
+    for b in range(B):
+        if p0[b] == 0:
+            continue
+        kh = rnd((1, p0[b], Hkv, D), "hist_k", 70 + b, dtype)
+        vh = rnd((1, p0[b], Hkv, D), "hist_v", 70 + b, dtype)
+        sub = GpuSide(1, Hq, Hkv, D, W, S, theta, dtype, dilation=dil)
+        sub.write(kh, vh, [0])
+        gpu.kc[b] = sub.kc[0]
+        gpu.vc[b] = sub.vc[0]
+        orc.caches[b].write(so.rope(np64(kh[0]), np.arange(p0[b]), theta), np64(vh[0]), np.arange(p0[b]))
+    for st in range(140):
+        q = rnd((B, Hq, D), "step_q", 80 + st, dtype)
+        k = rnd((B, Hkv, D), "step_k", 80 + st, dtype)
+        v = rnd((B, Hkv, D), "step_v", 80 + st, dtype)
+        pos = [p0[b] + st for b in range(B)]
+        out, lse = gpu.decode(q, k, v, pos, fused=st % 2 == 1)
+        ref = orc.decode(q, k, v, pos)
+        for b in range(B):
+            assert_close(out[b], ref[b][0], atol, rrms, f"step {st} seq {b} out")
+            assert_lse(lse[b], ref[b][1], latol, f"step {st} seq {b} lse")
+
+
+def test_dilated_key_counts_exact():
+    """Scale ~ 0: exp(lse) counts the keys; the dilated window holds
+    min(ceil(W/d), floor(i/d) + 1) of them, the sinks add those below it."""
+    print("dilated key counts", flush=True)
+    B, Hq, Hkv, D, W, S, dil = 2, 8, 2, 128, 100, 3, 3
+    gpu = GpuSide(B, Hq, Hkv, D, W, S, 10000.0, torch.bfloat16, scale=1e-30, dilation=dil)
+    t = 0
+    for ci, C in enumerate([150, 70, 1, 130]):
+        q = rnd((B, C, Hq, D), "q", 90 + ci)
+        k = rnd((B, C, Hkv, D), "k", 90 + ci)
+        v = rnd((B, C, Hkv, D), "v", 90 + ci)
+        _, lse = gpu.prefill(q, k, v, [t, t])
+        lse = lse.cpu().numpy()
+        for tt in range(C):
+            I = t + tt
+            count = int(so.key_mask([I], np.arange(I + 1), W, S, dil)[0].sum())
+            got = np.rint(np.exp(lse[:, :, tt].astype(np.float64)))
+            assert (got == count).all(), (ci, tt, got.ravel()[:4], count)
+        t += C
+    for st in range(0, 40):
+        pos = [t + st] * B
+        _, lse = gpu.decode(rnd((B, Hq, D), "step_q", st), rnd((B, Hkv, D), "step_k", st),
+                            rnd((B, Hkv, D), "step_v", st), pos)
+        count = int(so.key_mask([t + st], np.arange(t + st + 1), W, S, dil)[0].sum())
+        got = np.rint(np.exp(lse.cpu().numpy().astype(np.float64)))
+        assert (got == count).all(), (st, got.ravel()[:4], count)
+
+
+# ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
 DECODE_CASES = [
