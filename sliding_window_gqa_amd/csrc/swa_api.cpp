@@ -60,14 +60,16 @@ bool fast_path(const swa_params* p) {
   const long long seq_cache_bytes =
       (long long)(p->n_sink + p->window) * p->n_kv_heads * p->head_dim * 2;
   return p->dtype == SWA_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads &&
-         seq_cache_bytes < (1LL << 31) && p->dilation <= 1;
+         seq_cache_bytes < (1LL << 31);
 }
 
 // The fast prefill kernel also addresses one sequence's chunk (Q, K, V, and
-// a few tiles past its end) with 32-bit byte offsets.
-bool fast_prefill(const swa_params* p, int32_t chunk_len) {
+// a few tiles past its end) with 32-bit byte offsets.  A dilated window takes
+// it without sinks and in fixed-length batches (varlen: dilated = false).
+bool fast_prefill(const swa_params* p, int32_t chunk_len, bool varlen = false) {
   const long long seq_q_bytes = (long long)(chunk_len + 256) * p->n_q_heads * p->head_dim * 2;
-  return fast_path(p) && seq_q_bytes < (1LL << 31);
+  return fast_path(p) && seq_q_bytes < (1LL << 31) &&
+         (p->dilation <= 1 || (!varlen && p->n_sink == 0));
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
@@ -125,12 +127,13 @@ T* rows_at(T* p, long long rows, long long row_elems, size_t es) {
 int decode_launch(const swa_params* params, const Shape& sh, const void* q, const void* k_cache,
                   const void* v_cache, const int32_t* pos, void* out, float* lse,
                   void* workspace, const swa::FusedWrite* fw, hipStream_t stream) {
-  const int n = swa::decode_splits(sh);
+  const bool fast = fast_path(params);
+  const int n = fast ? swa::decode_splits_fast(sh) : swa::decode_splits(sh);
   const RopeTab rt = rope_table(params);
   const bool f32 = params->dtype == SWA_F32;
   float* part = static_cast<float*>(workspace);
   hipError_t e;
-  if (fast_path(params)) {
+  if (fast) {
     e = swa::launch_decode_bf16_d128_g4(sh, rt, q, k_cache, v_cache, pos, part, n, out, lse, fw,
                                         nullptr, stream);
     if (n == 1) return launched(e);   // the kernel wrote out and lse
@@ -356,7 +359,7 @@ int swa_prefill_attention_varlen(const swa_params* params, const void* q, const 
   if (st != SWA_OK) return st;
   const RopeTab rt = rope_table(params);
   const bool f32 = params->dtype == SWA_F32;
-  const bool fast = fast_prefill(params, longest);
+  const bool fast = fast_prefill(params, longest, true);
   const size_t es = elem_size(params->dtype);
   const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
   return for_var_groups(sh, chunk_lens, total, [&](int g0, const swa::VarTab& vt, long long row, int mx,
@@ -426,7 +429,7 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
   if (st != SWA_OK) return st;
   if (!workspace || workspace_bytes < swa_step_varlen_workspace_bytes(params, chunk_lens))
     return SWA_ERR_WORKSPACE;
-  if (!fast_prefill(params, longest)) {
+  if (!fast_prefill(params, longest, true)) {
     // one path for every sequence: the prefill chunk, then the cache write
     st = swa_prefill_chunk_varlen(params, q, k, v, k_cache, v_cache, start_pos, chunk_lens, out, lse,
                                   workspace, workspace_bytes, stream);
@@ -457,7 +460,7 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
   //    their entries in the caches
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + step_keys_bytes(params, total));
   return for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap& m, const Shape& gs) {
-    const int n = swa::decode_splits(gs);
+    const int n = swa::decode_splits_fast(gs);
     hipError_t e = swa::launch_decode_bf16_d128_g4(gs, rt, q, k_cache, v_cache, start_pos, part, n, out,
                                                    lse, nullptr, &m, stream);
     if (e == hipSuccess && n > 1) e = swa::launch_decode_combine(gs, false, part, n, out, lse, &m, stream);

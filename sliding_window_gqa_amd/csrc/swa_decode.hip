@@ -111,6 +111,10 @@ __device__ inline void ddma2(__amdgpu_buffer_rsrc_t r0, int o0, unsigned l0,
       : "memory");
 }
 
+// DIL: dilated window.  The work-groups then cut the sequence's keys, not
+// its slots, into ranges: key v < n_sink is sink slot v, key n_sink + k the
+// position p - k*dil (slot n_sink + (p - k*dil - n_sink) mod W).
+template <bool DIL>
 __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kvs[4 * 2 * DTILE];   // [wave][buffer] K
   __shared__ float sm_m[4][4], sm_l[4][4];
@@ -127,10 +131,26 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   const int lane = tid & 63, i = lane & 15, g = lane >> 4;
   const int p = __builtin_amdgcn_readfirstlane(a.pos[b]);   // uniform: one sequence per work-group
   const int S = sh.S;
-  // slots [0, min(S, p+1)) hold live positions; the others are never read
-  const int n_live = min(S, p + 1);
+  // slots [0, min(S, p+1)) hold live positions; the others are never read.
+  // DIL: the keys are the live sinks, then the window's positions p, p-dil,
+  // ... (those past the sinks)
+  const int dil = sh.dil, W = sh.W, nsink = sh.n_sink;
+  const int n_live = DIL ? min(nsink, p + 1) +
+                               (p >= nsink ? min((W + dil - 1) / dil, (p - nsink) / dil + 1) : 0)
+                         : min(S, p + 1);
   const int sp0 = split * a.split_len;
   const int vend = min(min(S, sp0 + a.split_len), n_live);
+  const int sp_w = p >= nsink ? (p - nsink) % W : 0;   // DIL: slot of p, less n_sink
+  // DIL: the slot of key v (keys past vend read key vend-1's row, whose
+  // values are finite; their scores are masked)
+  auto key_slot = [&](int v) __attribute__((always_inline)) {
+    v = min(v, vend - 1);
+    if (v < nsink) return v;
+    int t = (v - nsink) * dil;
+    t = t >= W ? t - W : t;
+    const int x = sp_w - t;
+    return nsink + (x < 0 ? x + W : x);
+  };
   const int h0 = kvh * 4;
 
   const long long row_stride = (long long)sh.Hkv * HD;       // elements between slots
@@ -148,7 +168,8 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   // the barrier, so every load of the work-group issued after it sees them.
   if (a.knew != nullptr) {
     const int slot = slot_of(p, sh.W, sh.n_sink);
-    if (slot >= sp0 && slot < sp0 + a.split_len) {
+    const int vp = DIL ? (p < nsink ? p : nsink) : slot;   // the range that holds p
+    if (vp >= sp0 && vp < sp0 + a.split_len) {
       if (tid < 32) {
         const int c = tid & 15;   // 16-byte chunk: head-dim elements 8c .. 8c+7
         const long long src = ((long long)r * sh.Hkv + kvh) * HD + 8 * c;
@@ -211,7 +232,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   // slots [0, vend), so rows past vend read as zeros (and are masked out of
   // the softmax).  Each K/V byte is read once per call.
   const unsigned rowb = (unsigned)row_stride * 2u;
-  const int nrec = __builtin_amdgcn_readfirstlane((vend - 1) * (int)rowb + HD * 2);
+  const int nrec = __builtin_amdgcn_readfirstlane(((DIL ? S : vend) - 1) * (int)rowb + HD * 2);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbase), (short)0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbase), (short)0, nrec, 0x00020000);
   // Load instruction e (0..7) of a chunk fills rows 4e .. 4e+3 (row 4e + g'
@@ -225,10 +246,19 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   auto dma_chunk = [&](int c0, int buf) __attribute__((always_inline)) {
     const int cb = c0 * (int)rowb;
     const unsigned lb = lds_w + (unsigned)buf * DTILE;
+    if (DIL) {
+      // lane (i, g) of load e fetches key c0 + 4e + g
 #pragma unroll
-    for (int e = 0; e < 8; e += 2)
-      ddma2(rk, cb + 4 * e * (int)rowb + ko[e & 3], lb + 1024u * e,
-            rk, cb + 4 * (e + 1) * (int)rowb + ko[(e + 1) & 3], lb + 1024u * (e + 1));
+      for (int e = 0; e < 8; e += 2)
+        ddma2(rk, key_slot(c0 + 4 * e + g) * (int)rowb + 16 * (i ^ dkswz(4 * e + g)), lb + 1024u * e,
+              rk, key_slot(c0 + 4 * (e + 1) + g) * (int)rowb + 16 * (i ^ dkswz(4 * (e + 1) + g)),
+              lb + 1024u * (e + 1));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        ddma2(rk, cb + 4 * e * (int)rowb + ko[e & 3], lb + 1024u * e,
+              rk, cb + 4 * (e + 1) * (int)rowb + ko[(e + 1) & 3], lb + 1024u * (e + 1));
+    }
   };
   // V: lane (i, g) loads slots kappa(g, e) = {4g+e, 16+4g+e-4}, d = 8i .. 8i+7
   unsigned voff[8];
@@ -238,8 +268,11 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   auto load_v = [&](int c0, u32x4 (&vr)[8]) __attribute__((always_inline)) {
     const unsigned cb = (unsigned)c0 * rowb;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vr[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(cb + voff[e]), 0, kNT));
+    for (int e = 0; e < 8; ++e) {
+      const int off = DIL ? key_slot(c0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4))) * (int)rowb + 16 * i
+                          : (int)(cb + voff[e]);
+      vr[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kNT));
+    }
   };
   // operand reads (as the chunk layout above): K rows 16kb + i, d-chunk 4kk+g
   int kofs[4];
@@ -532,6 +565,16 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(Shape sh, const flo
 // ranges per work-group beat more, shorter ones: the per-work-group prologue,
 // merge and the combine pass cost more than the load imbalance), each range a
 // multiple of the 128 slots one work-group step covers.
+// Keys a fast decode streams per (sequence, KV head): the slots, or with a
+// dilated window the sinks and ceil(W/dil) window keys.
+static Shape key_shape(const Shape& sh) {
+  Shape k = sh;
+  if (sh.dil > 1) k.S = sh.n_sink + (sh.W + sh.dil - 1) / sh.dil;
+  return k;
+}
+
+int decode_splits_fast(const Shape& sh) { return decode_splits(key_shape(sh)); }
+
 int decode_splits(const Shape& sh) {
   const int units = sh.B * sh.Hkv;
   int n = (512 + units - 1) / units;
@@ -561,7 +604,7 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
   a.pos = pos;
   a.part = partial;
   a.n_splits = n_splits;
-  a.split_len = split_len_of(sh, n_splits);
+  a.split_len = split_len_of(key_shape(sh), n_splits);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.knew = fw ? static_cast<const uint16_t*>(fw->k) : nullptr;
@@ -572,7 +615,10 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
     a.map = *map;
   else
     a.map = DecodeMap{};
-  decode_bf16_d128_g4_kernel<<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
+  if (sh.dil > 1)
+    decode_bf16_d128_g4_kernel<true><<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
+  else
+    decode_bf16_d128_g4_kernel<false><<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 

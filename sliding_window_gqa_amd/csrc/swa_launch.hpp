@@ -67,6 +67,9 @@ struct FusedWrite {
   void* v_cache;
 };
 int decode_splits(const Shape& sh);
+// Splits of the fast decode kernel (a dilated window cuts its keys, fewer
+// than the slots); never more than decode_splits(sh).
+int decode_splits_fast(const Shape& sh);
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
                                       float* partial, int n_splits, void* out, float* lse,

@@ -178,7 +178,14 @@ struct PrefillArgs {
 // first tiles of the next one into the ring, and the next item's query rows
 // go to an LDS stage while the current item runs, so that an item starts
 // without waiting for memory.
-template <bool VAR>
+//
+// DIL (dilated window, no sinks): a query at i attends only keys j = i - k*dil,
+// all of i's residue mod dil, so each residue class of a sequence's positions
+// is plain sliding-window attention over its own rows (every dil-th row) with
+// a window of ceil(W/dil) of them.  An item is then (sequence, KV head,
+// residue, query tile); the band logic runs on a residue's decimated indices,
+// RoPE and the cache slots on absolute positions.
+template <bool VAR, bool DIL>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
@@ -197,6 +204,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   const int nsink = sh.n_sink;
   const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;   // bytes between tokens of K/V
   const unsigned qrowbytes = (unsigned)sh.Hq * 2u * HD;   // bytes between tokens of Q
+  // DIL: the dilation, the window in a residue's rows, and the bytes between
+  // a residue's consecutive rows of K/V and of Q
+  const int dil = DIL ? sh.dil : 1;
+  const int Wb = DIL ? (W + dil - 1) / dil : W;
+  const unsigned rbd = DIL ? rowbytes * (unsigned)dil : rowbytes;
+  const unsigned qrbd = DIL ? qrowbytes * (unsigned)dil : qrowbytes;
 
   // ---- work mapping ----
   // Items (sequence, KV head, query tile) are numbered sequence-major, KV
@@ -234,6 +247,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   struct Item {
     int b, kvh, t0, s0, sa, n_stile, kmin, n_tiles;
     int row0, len;   // varlen: the sequence's first packed row, its length
+    int abs0;        // absolute position of row 0 (DIL: of the residue's first row)
   };
   // The start positions are read through the constant address space, so
   // that they come in with scalar loads, which the wait for the tile loads
@@ -258,6 +272,22 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       const int rem = L - a.vt.item_off[it.b];
       it.kvh = rem / nqt;
       it.t0 = (nqt - 1 - (rem - it.kvh * nqt)) * BM;
+    } else if (DIL) {
+      // residue rho of sequence b: chunk rows r0, r0 + dil, ... (positions
+      // = rho mod dil), decimated indices from s0 = (s0_abs + r0 - rho) / dil
+      const int per_b = sh.Hkv * dil * a.n_qtiles;
+      it.b = L / per_b;
+      int rem = L - it.b * per_b;
+      it.kvh = rem / (dil * a.n_qtiles);
+      rem -= it.kvh * dil * a.n_qtiles;
+      const int rho = rem / a.n_qtiles;
+      it.t0 = (a.n_qtiles - 1 - (rem - rho * a.n_qtiles)) * BM;
+      const int sabs = start_c[it.b];
+      const int r0 = ((rho - sabs) % dil + dil) % dil;
+      it.row0 = it.b * C + r0;
+      it.len = r0 < C ? (C - r0 + dil - 1) / dil : 0;
+      it.abs0 = sabs + r0;
+      it.s0 = (sabs + r0 - rho) / dil;
     } else {
       const int per_b = sh.Hkv * a.n_qtiles;
       it.b = L / per_b;
@@ -267,12 +297,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       it.row0 = it.b * C;
       it.len = C;
     }
-    it.s0 = start_c[it.b];
+    if (!DIL) it.s0 = start_c[it.b];
     it.sa = a.kc ? it.s0 : 0;
     const int tq_last = min(it.t0 + BM, it.len) - 1;
     // sink tiles: some readable sink lies outside the window of some query
-    it.n_stile = (nsink > it.s0 - it.sa && tq_last - W + it.sa >= 0) ? (nsink + BN - 1) / BN : 0;
-    const int k_lo = -((W - 1 + BN - 1) / BN);
+    it.n_stile = (!DIL && nsink > it.s0 - it.sa && tq_last - W + it.sa >= 0) ? (nsink + BN - 1) / BN : 0;
+    const int k_lo = -((Wb - 1 + BN - 1) / BN);
     const int k_clip = -((it.sa + it.t0 + BN - 1) / BN);
     it.kmin = max(k_lo, k_clip);
     it.n_tiles = it.n_stile + (2 - it.kmin);
@@ -287,8 +317,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // cache rows take the slot map, and rows before position 0 read slot 0
   // (they are masked).
   const int rdma = 4 * w + (lane >> 4);               // row of the tile this lane loads
-  const int vrk = rdma * (int)rowbytes + 16 * ((lane & 15) ^ kswz(rdma));   // lane offsets
-  const int vrv = rdma * (int)rowbytes + 16 * ((lane & 15) ^ vswz(rdma));   // in a chunk tile
+  const int vrk = rdma * (int)rbd + 16 * ((lane & 15) ^ kswz(rdma));   // lane offsets
+  const int vrv = rdma * (int)rbd + 16 * ((lane & 15) ^ vswz(rdma));   // in a chunk tile
   const unsigned lds_ring = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)smem) + (unsigned)w * 1024u);
   const unsigned lds_q = __builtin_amdgcn_readfirstlane(
@@ -305,6 +335,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   int lr_round = 0, lt = 0;
   unsigned lslot = 0;           // LDS offset of the ring slot the next load fills
   int l_nt, l_ns, l_u0, l_s0;   // tiles, sink tiles, u0 of the first band tile, start
+  int l_a0 = 0;                 // DIL: absolute position of the item's row 0
   int l_nrec;                   // bytes of the item's rows of the chunk
   long long l_ec, l_es;         // element offset of the rows in the chunk, the cache
   auto rsrc = [&](const uint16_t* base, long long e, int nrec) __attribute__((always_inline)) {
@@ -338,9 +369,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     l_ns = it.n_stile;
     l_u0 = it.t0 + BN * (it.kmin - it.n_stile);
     l_s0 = it.s0;
-    l_ec = VAR ? ((long long)it.row0 * sh.Hkv + it.kvh) * HD : ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
+    if (DIL) l_a0 = it.abs0;
+    l_ec = (VAR || DIL) ? ((long long)it.row0 * sh.Hkv + it.kvh) * HD : ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
     l_es = ((long long)it.b * S * sh.Hkv + it.kvh) * HD;
-    l_nrec = VAR ? (it.len - 1) * (int)rowbytes + HD * 2 : nrec_c;
+    l_nrec = (VAR || DIL) ? (it.len - 1) * (int)rbd + HD * 2 : nrec_c;
     l_reg = -1;
     l_cmn = -1;
   };
@@ -366,19 +398,20 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     if (lt >= l_ns) {
       if (u0 >= 0) {
         reg = 0;                                   // band tile of the chunk
-        srow = u0 * (int)rowbytes;
+        srow = u0 * (int)rbd;
       } else {
         // cache band tile: the rolling-buffer slot of the wave's first row,
         // less n_sink, when all its rows lie past the sinks; consecutive
         // cache tiles of an item are 32 slots apart
-        const int P0 = l_s0 + u0 + 4 * w;
+        const int P0 = (DIL ? l_a0 : l_s0) + dil * (u0 + 4 * w);
         if (P0 >= nsink) {
           l_cm = l_cmn >= 0 ? l_cmn : (int)((unsigned)(P0 - nsink) % (unsigned)W);
-          const int nx = l_cm + BN >= W ? l_cm + BN - W : l_cm + BN;
+          const int nx = l_cm + BN * dil >= W ? l_cm + BN * dil - W : l_cm + BN * dil;
           l_cmn = nx < W ? nx : -1;
-          if (l_cm + 3 < W) {
-            reg = 1;                               // its 4 rows per wave are consecutive slots
-            srow = (nsink + l_cm - 4 * w) * (int)rowbytes;
+          if (l_cm + 3 * dil < W) {
+            // its 4 rows per wave are slots dil apart (consecutive without dilation)
+            reg = 1;
+            srow = DIL ? (nsink + l_cm) * (int)rowbytes - 4 * w * (int)rbd : (nsink + l_cm - 4 * w) * (int)rowbytes;
           }
         } else {
           l_cm = -1;
@@ -418,10 +451,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         // cache rows (a chunk without a cache has none: nrec_s = 0 reads zeros)
         int sl;
         if (l_cm >= 0) {
-          sl = l_cm + r;
-          sl = nsink + (sl >= W ? sl - W : sl);
+          sl = l_cm + dil * r;
+          sl = nsink + (DIL ? sl % W : (sl >= W ? sl - W : sl));
         } else {
-          const int P = max(l_s0 + l_u0 + BN * lt + rd, 0);
+          const int P = max((DIL ? l_a0 : l_s0) + dil * (l_u0 + BN * lt + rd), 0);
           sl = P < nsink ? P : nsink + (P - nsink) % W;
         }
         const int row = sl * (int)rowbytes;
@@ -440,16 +473,16 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // operand read touches fall in 16 different bank groups.  Rows past the
   // chunk read as zeros.
   auto load_q = [&](const Item& it) __attribute__((always_inline)) {
-    const long long qrow = VAR ? (long long)it.row0 : (long long)it.b * C;
+    const long long qrow = (VAR || DIL) ? (long long)it.row0 : (long long)it.b * C;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(a.q + (qrow * sh.Hq + 4 * it.kvh) * HD), (short)0,
-        VAR ? (it.len - 1) * (int)qrowbytes + QROWB : nrec_q, 0x00020000);
+        (VAR || DIL) ? (it.len - 1) * (int)qrbd + QROWB : nrec_q, 0x00020000);
     int ln_ = lane;   // (computed here, not held in registers across the loop)
     asm volatile("" : "+v"(ln_));
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int q = 8 * w + m;
-      dma16(rq, (it.t0 + q) * (int)qrowbytes + 16 * (ln_ ^ (q & 15)), lds_q + (unsigned)q * QROWB);
+      dma16(rq, (it.t0 + q) * (int)qrbd + 16 * (ln_ ^ (q & 15)), lds_q + (unsigned)q * QROWB);
     }
   };
 
@@ -489,7 +522,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // directly.
   bf16x8 qf[QB][4];
   auto load_qf = [&](const Item& it) __attribute__((always_inline)) {
-    const int I = it.s0 + it.t0 + 16 * (w & 3) + i;   // absolute position of the lane's query
+    const int I = (DIL ? it.abs0 : it.s0) + dil * (it.t0 + 16 * (w & 3) + i);   // the lane's query position
     // (the asm keeps the table addresses from being computed once for all
     // items and held in registers)
     int gi = g;
@@ -525,7 +558,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     const int n_stile = it.n_stile, kmin = it.kmin, n_tiles = it.n_tiles;
     const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
     const int tq = q0w + i;                 // this lane's query
-    const int I = s0 + tq;                  // its absolute position
+    const int I = (DIL ? it.abs0 : s0) + dil * tq;   // its absolute position
     const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
     // the next item, whose query rows go to the stage during this item
     const int Ln = item_at(round + 1);
@@ -629,7 +662,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     // range jlo <= j <= jhi (>> 5 is the floor division by 32).
     const int mfull = kmin - n_stile, dq = q0w - t0;
     const int jhi = ((dq - (BN - 1)) >> 5) - mfull;
-    const int jlo = max(max(n_stile, ((dq + 15 - W) >> 5) + 1 - mfull), -((sa + t0) >> 5) - mfull);
+    const int jlo = max(max(n_stile, ((dq + 15 - Wb) >> 5) + 1 - mfull), -((sa + t0) >> 5) - mfull);
     auto mask_kind = [&](int j) __attribute__((always_inline)) {
       if (j < n_stile) return 2;
       return (j >= jlo && j <= jhi) ? 0 : 1;
@@ -649,7 +682,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         }
       } else {
         k0 = band_u0(j) + 4 * g;
-        lo = max(tq - W + 1, -sa);
+        lo = max(tq - Wb + 1, -sa);
         span = tq - lo;
       }
 #pragma unroll
@@ -852,7 +885,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       }
       if (a.lse && g == 0 && tq < it.len) {
         const long long lo = VAR ? (long long)(h0 + qb) * a.vt.total + it.row0 + tq
-                                 : ((long long)b * sh.Hq + h0 + qb) * C + tq;
+                             : DIL ? ((long long)b * sh.Hq + h0 + qb) * C + (it.row0 - b * C) + dil * tq
+                                   : ((long long)b * sh.Hq + h0 + qb) * C + tq;
         a.lse[lo] = (ref[qb] + log2f(lsum[qb][0])) * 0.69314718055994531f;
       }
     }
@@ -860,13 +894,13 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     {
-      uint16_t* orow = a.out + ((VAR ? (long long)it.row0 : (long long)b * C) * sh.Hq + 4 * kvh) * HD;
+      uint16_t* orow = a.out + (((VAR || DIL) ? (long long)it.row0 : (long long)b * C) * sh.Hq + 4 * kvh) * HD;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int q = 8 * w + m;
         if (t0 + q < it.len) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(qstage + q * QROWB + 16 * li_);
-          *reinterpret_cast<u32x4*>(orow + (long long)(t0 + q) * sh.Hq * HD + 8 * (li_ ^ (q & 15))) = v;
+          *reinterpret_cast<u32x4*>(orow + (long long)(t0 + q) * dil * sh.Hq * HD + 8 * (li_ ^ (q & 15))) = v;
         }
       }
     }
@@ -999,10 +1033,12 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.vc = static_cast<const uint16_t*>(vc);
   a.start = start;
   a.C = C;
-  a.n_qtiles = (C + BM - 1) / BM;
+  const bool dil = sh.dil > 1 && !vt;   // (the API sends dilated varlen batches to the generic kernel)
+  const int rows = dil ? (C + sh.dil - 1) / sh.dil : C;   // the longest residue's rows
+  a.n_qtiles = (rows + BM - 1) / BM;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B;
+  long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B * (dil ? sh.dil : 1);
   if (vt) {
     // items of sequence j: Hkv x its own query tiles, numbered after those of 0 .. j-1
     a.vt = *vt;
@@ -1025,9 +1061,11 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   const long long ncu = (long long)(device_cu_count() & ~7);
   const long long nwg = (ncu >= 8 && n_items > ncu) ? ncu : n_items;
   if (vt)
-    prefill_bf16_d128_g4_kernel<true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+    prefill_bf16_d128_g4_kernel<true, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+  else if (dil)
+    prefill_bf16_d128_g4_kernel<false, true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   else
-    prefill_bf16_d128_g4_kernel<false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+    prefill_bf16_d128_g4_kernel<false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   return hipGetLastError();
 }
 

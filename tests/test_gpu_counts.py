@@ -128,3 +128,65 @@ def test_counts_decode_steps(index):
     want = count_closed_form(pos, W, S)[:, :, None]
     bad = np.argwhere(got != want)
     assert bad.size == 0, f"{len(bad)} wrong counts, first at (step, seq, head) {tuple(bad[0])}"
+
+
+def count_dilated(pos, W, d):
+    """|A(i)| of a dilated window without sinks: the progression i, i-d, ...
+    inside the span, min(ceil(W/d), floor(i/d) + 1) keys."""
+    pos = np.asarray(pos, dtype=np.int64)
+    return np.minimum(-(-W // d), pos // d + 1)
+
+
+@pytest.mark.parametrize("d", [2, 3])
+def test_counts_dilated_prefill_n8192(d):
+    """The 8192-token layer with a dilated window (the fast kernel's residue
+    classes), one pass from position 0 and a second 1000-token chunk against
+    the cache it left, every row and head."""
+    wl = synth.workload(2)
+    print(f"dilated key counts n8192 d={d}", flush=True)
+    N, Hq, Hkv, D, W = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    g = torch.Generator(device=DEV).manual_seed(8100 + d)
+    p = swa.make_params(1, Hq, Hkv, D, W, 0, TINY, wl.rope_theta, dilation=d)
+    q, k, v = rand((1, N, Hq, D), g), rand((1, N, Hkv, D), g), rand((1, N, Hkv, D), g)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _, lse = swa.swa_prefill_chunk(p, q, k, v, None, None, st)
+    got = counts_of(lse)
+    want = count_dilated(np.arange(N), W, d)[None, None, :]
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} wrong counts, first at (seq, head, row) {tuple(bad[0])}"
+    kc = torch.zeros((1, W, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    swa.swa_cache_write(p, k, v, st, kc, vc)
+    C2 = 1000
+    q2, k2, v2 = rand((1, C2, Hq, D), g), rand((1, C2, Hkv, D), g), rand((1, C2, Hkv, D), g)
+    _, lse2 = swa.swa_prefill_chunk(p, q2, k2, v2, kc, vc, torch.full((1,), N, dtype=torch.int32, device=DEV))
+    got = counts_of(lse2)
+    want = count_dilated(N + np.arange(C2), W, d)[None, None, :]
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"chunk 2: {len(bad)} wrong counts, first at (seq, head, row) {tuple(bad[0])}"
+
+
+def test_counts_dilated_decode_b64():
+    """The batched-decode workload's shape with dilation 2: 64 steps of the
+    64 sequences through swa_decode_step, every count."""
+    wl = synth.workload(4)
+    print("dilated key counts decode b64", flush=True)
+    B, Hq, Hkv, D, W = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    d = 2
+    g = torch.Generator(device=DEV).manual_seed(8104)
+    p = swa.make_params(B, Hq, Hkv, D, W, 0, TINY, wl.rope_theta, dilation=d)
+    p0 = synth.positions(4, B, wl.pos_lo, wl.pos_hi).numpy().astype(np.int64)
+    p0[:3] = [1, W - 40, 2 * W - 3]
+    kc, vc = rand((B, W, Hkv, D), g), rand((B, W, Hkv, D), g)
+    ws = torch.empty(swa.swa_decode_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    steps = 64
+    lses = torch.empty((steps, B, Hq), dtype=torch.float32, device=DEV)
+    for s in range(steps):
+        pos = torch.tensor(p0 + s, dtype=torch.int32, device=DEV)
+        swa.swa_decode_step(p, rand((B, Hq, D), g), rand((B, Hkv, D), g), rand((B, Hkv, D), g), kc, vc, pos,
+                            out, lses[s], ws)
+    got = counts_of(lses)
+    want = count_dilated(p0[None, :] + np.arange(steps)[:, None], W, d)[:, :, None]
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} wrong counts, first at (step, seq, head) {tuple(bad[0])}"

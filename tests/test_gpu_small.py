@@ -213,8 +213,14 @@ def test_debug_mask_dilated_bit_exact(W, S, d):
 
 
 DILATED_PREFILL = [
-    # (B, Hq, Hkv, D, W, n_sink, dilation, dtype, chunks)
+    # (B, Hq, Hkv, D, W, n_sink, dilation, dtype, chunks) -- without sinks, bf16,
+    # head_dim 128 and 4 query heads per KV head: the fast kernel, per residue
     (2, 8, 2, 128, 100, 0, 3, torch.bfloat16, [130, 1, 64, 65, 7]),
+    (2, 32, 8, 128, 300, 0, 2, torch.bfloat16, [1100, 1030]),     # several items per work-group
+    (1, 4, 1, 128, 4096, 0, 4, torch.bfloat16, [4100, 50]),
+    (3, 8, 2, 128, 64, 0, 5, torch.bfloat16, [200, 7, 64]),      # window < 32 * dilation
+    (1, 8, 2, 128, 4, 0, 5, torch.bfloat16, [70, 9]),            # dilation > window: only self
+    # with sinks, or other shapes: the generic kernel
     (2, 8, 2, 128, 100, 4, 2, torch.bfloat16, [130, 3, 100]),
     (1, 8, 2, 128, 64, 100, 4, torch.bfloat16, [300, 77]),
     (2, 4, 2, 64, 90, 2, 5, torch.bfloat16, [140, 9]),
@@ -231,7 +237,7 @@ def test_prefill_dilated(case):
     gpu = GpuSide(B, Hq, Hkv, D, W, S, theta, dtype, dilation=dil)
     orc = OracleSide(range(B), Hkv, D, W, S, theta, dilation=dil)
     atol, rrms, latol = tol(dtype)
-    offs = [0, 37][:B]
+    offs = [0, 37, 0][:B]
     if B > 1:   # sequence 1 starts after 37 tokens already in its cache
         kp = rnd((1, 37, Hkv, D), "hist_k", 1, dtype)
         vp = rnd((1, 37, Hkv, D), "hist_v", 1, dtype)
