@@ -106,7 +106,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the chunked / full-causal / sink timings")
-    ap.add_argument("--only", choices=["prefill", "decode", "chunked", "sink", "all"], default="all",
+    ap.add_argument("--only", choices=["prefill", "decode", "chunked", "sink", "dilated", "all"], default="all",
                     help="restrict the GPU work (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (scales HBM byte counters)")
@@ -328,6 +328,8 @@ def main():
     # ------------------------------------------------------------------
     if not args.no_context and args.only in ("chunked", "sink"):
         result["context"] = context_timings(swa, synth, torch, dev, args.only)
+    if not args.no_context and args.only == "dilated":
+        result["context"] = {"dilated_windows": dilated_windows(swa, synth, torch, dev)}
     if not args.no_context and args.only == "all":
         result["context"] = context_timings(swa, synth, torch, dev)
         result["context"]["decode_32_layers"] = decode_layers(swa, synth, torch, dev)
@@ -336,6 +338,7 @@ def main():
                                                                         result["context"])
         result["context"]["decode_small_batches"] = decode_small_batches(swa, synth, torch, dev)
         result["context"]["tiny_fp32_prefill"] = tiny_fp32(swa, synth, torch, dev)
+        result["context"]["dilated_windows"] = dilated_windows(swa, synth, torch, dev)
 
     # ------------------------------------------------------------------
     # CPU baseline: the oracle on a bounded sample of the prefill workload
@@ -534,6 +537,62 @@ def vanilla_vs_swa_decode(swa, synth, torch, dev, ctx16, B=64, steps=64, n_gen=2
     }
 
 
+def dilated_windows(swa, synth, torch, dev, dils=(2, 4), steps=64):
+    """The dilated sliding window (keys i, i-d, i-2d, ... inside the W span) at
+    the headline prefill shape (8192 tokens, W = 4096, no sinks: the fast
+    kernel per residue class) and at the batched-decode shape (64 sequences,
+    full windows: the fast decode over the window's keys)."""
+    bf = torch.bfloat16
+    wl = synth.workload(2)
+    N, Hq, Hkv, D, W = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    g = torch.Generator(device=dev).manual_seed(2202)
+    q = torch.randn((1, N, Hq, D), generator=g, device=dev).to(bf)
+    k = torch.randn((1, N, Hkv, D), generator=g, device=dev).to(bf)
+    v = torch.randn((1, N, Hkv, D), generator=g, device=dev).to(bf)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((1, N, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((1, Hq, N), dtype=torch.float32, device=dev)
+    res = {"prefill_workload": wl.name, "decode_workload": "decode_b64_w4096 (full windows)"}
+    wl4 = synth.workload(4)
+    B = wl4.batch
+    kc = torch.randn((B, W, Hkv, D), generator=g, device=dev).to(bf)
+    vc = torch.randn((B, W, Hkv, D), generator=g, device=dev).to(bf)
+    qd = torch.randn((B, Hq, D), generator=g, device=dev).to(bf)
+    kd = torch.randn((B, Hkv, D), generator=g, device=dev).to(bf)
+    vd = torch.randn((B, Hkv, D), generator=g, device=dev).to(bf)
+    od = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    ld = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    pos = [torch.full((B,), 20000 + s, dtype=torch.int32, device=dev) for s in range(steps)]
+    for d in dils:
+        p = swa.make_params(1, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf, d)
+        # (the key rotation is common to every window; the attention is timed)
+        kr = swa.swa_rope_keys(p, k, st)
+        ms = timeit(lambda: swa.swa_prefill_attention(p, q, kr, v, None, None, st, out, lse), torch, 10)
+        pairs = sum(min(-(-W // d), i // d + 1) for i in range(N))
+        pd = swa.make_params(B, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta, bf, d)
+        ws = torch.empty(swa.swa_decode_workspace_bytes(pd), dtype=torch.uint8, device=dev)
+        t = {"s": 0}
+
+        def dstep():
+            swa.swa_decode_step(pd, qd, kd, vd, kc, vc, pos[t["s"] % steps], od, ld, ws)
+            t["s"] += 1
+
+        dms = timeit(dstep, torch, steps)
+        dbytes = B * (-(-W // d)) * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2 + B * Hkv * D * 2 * 2 * 2
+        res[f"d{d}"] = {
+            "prefill_ms": round(ms, 4), "prefill_key_pairs": pairs,
+            "prefill_tflops": round(attn_flops(pairs) / (ms * 1e-3) / 1e12, 1),
+            "prefill_frac_bf16_peak": round(attn_flops(pairs) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "decode_ms_per_step": round(dms, 4), "decode_bytes": dbytes,
+            "decode_gbps": round(dbytes / (dms * 1e-3) / 1e9, 1),
+            "decode_frac_hbm_peak": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        }
+    res["step"] = ("prefill_attention (rotated keys given) and decode_step (cache write + attention) with "
+                   "a dilated window: keys at distances 0, d, 2d, ... inside the W span")
+    del kc, vc
+    return res
+
+
 def tiny_fp32(swa, synth, torch, dev, reps=50):
     """The tiny float32 prefill (batch 1, N = 256, 4 query / 1 KV head,
     head_dim 64, scale 1/8, no RoPE) at W = 64 and W = 256 (full causal):
@@ -629,7 +688,10 @@ def context_timings(swa, synth, torch, dev, only="all"):
     return ctx
 
 
-def timeit(fn, torch, reps=5):
+def timeit(fn, torch, reps=5, prewarm_s=0.1):
+    """Mean ms of fn over reps calls, timed with events after about prewarm_s
+    seconds of untimed calls (the clocks rise over the first ~50 ms of load)."""
+    prewarm(fn, prewarm_s, torch)
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
@@ -669,6 +731,31 @@ def chunked_vs_full(swa, synth, torch, dev):
                                   starts[c], outc, lsec, ws)
             swa.swa_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc)
 
+    def chunked_parts(reps=5):
+        # the same loop as two calls per part (key rotation, attention, cache
+        # write), events around each launch: where the loop's time goes
+        kr = torch.empty_like(ks_[0])
+        acc = {"key_rotation": 0.0, "attention": [0.0] * (N // C), "cache_write": 0.0}
+        for _ in range(reps):
+            evs = []
+            for c in range(N // C):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e[0].record()
+                swa.swa_rope_keys(p, ks_[c], starts[c], kr)
+                e[1].record()
+                swa.swa_prefill_attention(p, qs[c], kr, vs_[c], kc if c else None, vc if c else None,
+                                          starts[c], outc, lsec)
+                e[2].record()
+                swa.swa_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc)
+                e[3].record()
+                evs.append(e)
+            torch.cuda.synchronize()
+            for c, e in enumerate(evs):
+                acc["key_rotation"] += e[0].elapsed_time(e[1]) / reps
+                acc["attention"][c] += e[1].elapsed_time(e[2]) / reps
+                acc["cache_write"] += e[2].elapsed_time(e[3]) / reps
+        return acc
+
     pf = swa.make_params(1, Hq, Hkv, D, N, 0, 0.0, wl.rope_theta, bf)
     wsf = torch.empty(swa.swa_prefill_workspace_bytes(pf, N), dtype=torch.uint8, device=dev)
     outf = torch.empty((1, N, Hq, D), dtype=bf, device=dev)
@@ -679,13 +766,21 @@ def chunked_vs_full(swa, synth, torch, dev):
         swa.swa_prefill_chunk(pf, q, k, v, None, None, z, outf, lsef, wsf)
 
     swa_ms = timeit(chunked2, torch)
+    parts = chunked_parts()
     full_ms = timeit(full, torch)
     swa_flops = attn_flops(band_pairs(N, W))
     full_flops = attn_flops(band_pairs(N, N))
+    attn_ms = sum(parts["attention"])
     ctx = {
         "chunked_swa_prefill": {"workload": wl.name, "ms": round(swa_ms, 4),
                                 "tflops": round(swa_flops / (swa_ms * 1e-3) / 1e12, 1),
-                                "step": "4 x (prefill_chunk + cache_write)"},
+                                "step": "4 x (prefill_chunk + cache_write)",
+                                "attention_ms_per_chunk": [round(x, 4) for x in parts["attention"]],
+                                "attention_tflops": round(swa_flops / (attn_ms * 1e-3) / 1e12, 1),
+                                "key_rotation_ms_total": round(parts["key_rotation"], 4),
+                                "cache_write_ms_total": round(parts["cache_write"], 4),
+                                "breakdown_note": "events around each launch of the same loop run as separate "
+                                                  "calls (launch included)"},
         "full_causal_prefill": {"seq_len": N, "ms": round(full_ms, 4),
                                 "tflops": round(full_flops / (full_ms * 1e-3) / 1e12, 1)},
         "full_over_swa_time": round(full_ms / swa_ms, 3),
