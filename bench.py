@@ -461,9 +461,6 @@ def varlen_mixed(swa, synth, torch, dev, n_prefill=4, chunk=1024, reps=10):
         swa.swa_decode_step(pd, qd, kd, vd, kc[n_prefill:], vc[n_prefill:], st[n_prefill:], outd, lsed, wsd)
 
     def timeit(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -473,9 +470,15 @@ def varlen_mixed(swa, synth, torch, dev, n_prefill=4, chunk=1024, reps=10):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    ms_one = timeit(one_call)
-    ms_step = timeit(step)
-    ms_sep = timeit(separate)
+    # the three paths in turn, five rounds after a prewarm of all three: the
+    # median of each (the clock drifts over a run; turns keep it fair)
+    prewarm(lambda: (one_call(), step(), separate()), 0.2, torch)
+    times = {"one": [], "step": [], "sep": []}
+    for _ in range(5):
+        times["one"].append(timeit(one_call))
+        times["step"].append(timeit(step))
+        times["sep"].append(timeit(separate))
+    ms_one, ms_step, ms_sep = (sorted(times[x])[2] for x in ("one", "step", "sep"))
     pairs = n_prefill * chunk * W + nd * W
     res = {
         "workload": f"mixed_b{B}_{n_prefill}x{chunk}_prefill_{nd}_decode_w{W}",
@@ -484,8 +487,10 @@ def varlen_mixed(swa, synth, torch, dev, n_prefill=4, chunk=1024, reps=10):
         "ms_prefill_chunk_varlen_and_cache_write_varlen": round(ms_one, 4),
         "ms_fixed_length_calls": round(ms_sep, 4),
         "tflops_step_varlen": round(attn_flops(pairs) / (ms_step * 1e-3) / 1e12, 1),
-        "step": "step_varlen (chunks on the prefill kernel, one-token sequences on the decode kernel) vs "
-                "prefill_chunk_varlen + cache_write_varlen vs prefill_chunk + cache_write + decode_step",
+        "step": "step_varlen (one call: equal-length chunks on the fixed-length prefill kernel, one-token "
+                "sequences on the decode kernel with its fused cache write) vs prefill_chunk_varlen + "
+                "cache_write_varlen vs prefill_chunk + cache_write + decode_step",
+        "timing": "median of 5 turns of the three paths, 10 calls each, HIP events",
     }
     del kc, vc
     return res

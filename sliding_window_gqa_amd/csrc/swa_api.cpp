@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "../../include/swa.h"
@@ -167,6 +168,26 @@ int for_decode_groups(const Shape& sh, const int32_t* lens, long long total, F&&
     }
   }
   return SWA_OK;
+}
+
+// Whether the sequences of more than one token among g0 .. g0+n-1 are one
+// contiguous run [*j0, *j1) of a single length *len (*j0 == *j1: none).
+bool equal_run(const int32_t* lens, int g0, int n, int* j0, int* j1, int* len) {
+  *j0 = *j1 = -1;
+  *len = 0;
+  for (int j = 0; j < n; ++j) {
+    const int l = lens[g0 + j];
+    if (l <= 1) continue;
+    if (*j0 < 0) {
+      *j0 = j;
+      *len = l;
+    } else if (*j1 != j || l != *len) {
+      return false;
+    }
+    *j1 = j + 1;
+  }
+  if (*j0 < 0) *j0 = *j1 = 0;
+  return true;
 }
 
 // Bytes of the rotated keys of a varlen step, rounded up to 256.
@@ -436,13 +457,64 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
     if (st != SWA_OK) return st;
     return swa_cache_write_varlen(params, k, v, start_pos, chunk_lens, k_cache, v_cache, stream);
   }
+  const RopeTab rt = rope_table(params);
+  const size_t es = elem_size(params->dtype);
+  const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + step_keys_bytes(params, total));
+  // Chunks of one size (chunked prefill with a fixed chunk length): when in
+  // every group of kVarMax sequences those of more than one token form one
+  // contiguous run of a single length, each run takes the fixed-length
+  // kernels (key rotation, attention, cache write) and the one-token
+  // sequences the decode kernel that stores their new entries itself: the
+  // launches of the separate fixed-length calls, in one call.
+  bool runs = true;
+  for (int g0 = 0; g0 < sh.B && runs; g0 += swa::kVarMax) {
+    int j0, j1, len;
+    runs = equal_run(chunk_lens, g0, std::min(swa::kVarMax, sh.B - g0), &j0, &j1, &len);
+  }
+  if (runs) {
+    long long row = 0;   // packed row of sequence g0
+    for (int g0 = 0; g0 < sh.B; g0 += swa::kVarMax) {
+      const int n = std::min(swa::kVarMax, sh.B - g0);
+      int j0, j1, len;
+      equal_run(chunk_lens, g0, n, &j0, &j1, &len);
+      long long r0 = row;
+      for (int j = 0; j < j0; ++j) r0 += chunk_lens[g0 + j];
+      if (j1 > j0) {
+        Shape rs = sh;
+        rs.B = j1 - j0;
+        const int32_t* sp = start_pos + g0 + j0;
+        const long long c0 = (long long)(g0 + j0) * sh.S;
+        void* kr = rows_at(workspace, r0, kv_row, es);
+        hipError_t e = swa::launch_cache_write(rs, rt, false, rows_at(k, r0, kv_row, es), nullptr, sp, len,
+                                               kr, nullptr, swa::kToDense, nullptr, stream);
+        if (e == hipSuccess)
+          e = swa::launch_prefill_bf16_d128_g4(rs, rt, rows_at(q, r0, q_row, es), kr, rows_at(v, r0, kv_row, es),
+                                               rows_at((const void*)k_cache, c0, kv_row, es),
+                                               rows_at((const void*)v_cache, c0, kv_row, es), sp, len,
+                                               rows_at(out, r0, q_row, es), lse ? lse + r0 : nullptr, nullptr,
+                                               stream, total);
+        if (e == hipSuccess)
+          e = swa::launch_cache_write(rs, rt, false, rows_at(k, r0, kv_row, es), rows_at(v, r0, kv_row, es), sp,
+                                      len, rows_at(k_cache, c0, kv_row, es), rows_at(v_cache, c0, kv_row, es),
+                                      swa::kToCache, nullptr, stream);
+        if (e != hipSuccess) return SWA_ERR_LAUNCH;
+      }
+      for (int j = 0; j < n; ++j) row += chunk_lens[g0 + j];
+    }
+    const swa::FusedWrite fw{k, v, k_cache, v_cache};
+    return for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap& m, const Shape& gs) {
+      const int n = swa::decode_splits_fast(gs);
+      hipError_t e = swa::launch_decode_bf16_d128_g4(gs, rt, q, k_cache, v_cache, start_pos, part, n, out,
+                                                     lse, &fw, &m, stream);
+      if (e == hipSuccess && n > 1) e = swa::launch_decode_combine(gs, false, part, n, out, lse, &m, stream);
+      return launched(e);
+    });
+  }
   // 1. every chunk's keys rotated into the workspace
   st = swa_rope_keys_varlen(params, k, start_pos, chunk_lens, workspace, stream);
   if (st != SWA_OK) return st;
   // 2. attention of the sequences of more than one token (they read the caches as they stand)
-  const RopeTab rt = rope_table(params);
-  const size_t es = elem_size(params->dtype);
-  const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
   st = for_var_groups(sh, chunk_lens, total, [&](int g0, swa::VarTab& vt, long long row, int mx,
                                                  const Shape& gs) {
     vt.skip_len1 = 1;
@@ -458,7 +530,6 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
   if (st != SWA_OK) return st;
   // 4. the one-token sequences through the decode kernel, which now finds
   //    their entries in the caches
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + step_keys_bytes(params, total));
   return for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap& m, const Shape& gs) {
     const int n = swa::decode_splits_fast(gs);
     hipError_t e = swa::launch_decode_bf16_d128_g4(gs, rt, q, k_cache, v_cache, start_pos, part, n, out,

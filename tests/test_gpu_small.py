@@ -482,6 +482,13 @@ VARLEN_CASES = [
     (4, 8, 2, 128, 4096, 0, torch.bfloat16, [300, 1, 65, 129], [0, 70, 3, 0]),
     (3, 4, 1, 64, 100, 0, torch.float32, [3, 0, 70], [10, 5, 0]),       # generic path
     (70, 8, 2, 128, 64, 0, torch.bfloat16) + _varlen_lens_starts(70, 7),  # two launches, mixed with decodes
+    # chunks of one length in one contiguous run per group of 64 sequences
+    # (the step takes the fixed-length kernels for the run): sinks, a wrap,
+    # empty and one-token sequences on both sides of the run
+    (6, 8, 2, 128, 100, 3, torch.bfloat16, [1, 96, 96, 96, 1, 0], [40, 250, 0, 130, 7, 9]),
+    (4, 8, 2, 128, 4096, 0, torch.bfloat16, [129, 129, 1, 1], [0, 5000, 70, 4095]),
+    (70, 8, 2, 128, 64, 0, torch.bfloat16, [1] * 10 + [70] * 5 + [1] * 49 + [33] * 3 + [1] * 3,
+     [int(x) for x in np.random.default_rng(8).integers(0, 200, 70)]),
 ]
 
 
