@@ -190,6 +190,21 @@ bool equal_run(const int32_t* lens, int g0, int n, int* j0, int* j1, int* len) {
   return true;
 }
 
+// Whether every group of kVarMax sequences has its multi-token sequences in
+// one equal-length run (the step's fixed-length path), and the largest run's
+// LSE bytes ([run][Hq][len] floats) then.
+bool equal_runs(const Shape& sh, const int32_t* lens, size_t* lse_bytes) {
+  size_t mx = 0;
+  for (int g0 = 0; g0 < sh.B; g0 += swa::kVarMax) {
+    int j0, j1, len;
+    if (!equal_run(lens, g0, std::min(swa::kVarMax, sh.B - g0), &j0, &j1, &len)) return false;
+    const size_t b = (size_t)(j1 - j0) * sh.Hq * (size_t)len * sizeof(float);
+    if (b > mx) mx = b;
+  }
+  *lse_bytes = mx;
+  return true;
+}
+
 // Bytes of the rotated keys of a varlen step, rounded up to 256.
 size_t step_keys_bytes(const swa_params* p, long long total) {
   const size_t kb = (size_t)total * p->n_kv_heads * p->head_dim * elem_size(p->dtype);
@@ -433,6 +448,9 @@ size_t swa_step_varlen_workspace_bytes(const swa_params* params, const int32_t* 
     if (need > part) part = need;
     return SWA_OK;
   });
+  // the fixed-length path packs each run's LSE through the same region
+  size_t run_lse = 0;
+  if (equal_runs(sh, chunk_lens, &run_lse) && run_lse > part) part = run_lse;
   return step_keys_bytes(params, total) + part;
 }
 
@@ -461,18 +479,15 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
   const size_t es = elem_size(params->dtype);
   const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + step_keys_bytes(params, total));
+  float* run_lse = part;   // (the decode partials come after the runs' LSE is packed)
   // Chunks of one size (chunked prefill with a fixed chunk length): when in
   // every group of kVarMax sequences those of more than one token form one
   // contiguous run of a single length, each run takes the fixed-length
   // kernels (key rotation, attention, cache write) and the one-token
   // sequences the decode kernel that stores their new entries itself: the
   // launches of the separate fixed-length calls, in one call.
-  bool runs = true;
-  for (int g0 = 0; g0 < sh.B && runs; g0 += swa::kVarMax) {
-    int j0, j1, len;
-    runs = equal_run(chunk_lens, g0, std::min(swa::kVarMax, sh.B - g0), &j0, &j1, &len);
-  }
-  if (runs) {
+  size_t run_lse_bytes = 0;
+  if (equal_runs(sh, chunk_lens, &run_lse_bytes)) {
     long long row = 0;   // packed row of sequence g0
     for (int g0 = 0; g0 < sh.B; g0 += swa::kVarMax) {
       const int n = std::min(swa::kVarMax, sh.B - g0);
@@ -488,12 +503,14 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
         void* kr = rows_at(workspace, r0, kv_row, es);
         hipError_t e = swa::launch_cache_write(rs, rt, false, rows_at(k, r0, kv_row, es), nullptr, sp, len,
                                                kr, nullptr, swa::kToDense, nullptr, stream);
+        // the run's LSE [B][Hq][C] goes through the workspace into its packed columns
+        float* lrun = lse ? run_lse : nullptr;
         if (e == hipSuccess)
           e = swa::launch_prefill_bf16_d128_g4(rs, rt, rows_at(q, r0, q_row, es), kr, rows_at(v, r0, kv_row, es),
                                                rows_at((const void*)k_cache, c0, kv_row, es),
                                                rows_at((const void*)v_cache, c0, kv_row, es), sp, len,
-                                               rows_at(out, r0, q_row, es), lse ? lse + r0 : nullptr, nullptr,
-                                               stream, total);
+                                               rows_at(out, r0, q_row, es), lrun, nullptr, stream);
+        if (e == hipSuccess && lse) e = swa::launch_lse_pack(run_lse, lse + r0, rs.B, sh.Hq, len, total, stream);
         if (e == hipSuccess)
           e = swa::launch_cache_write(rs, rt, false, rows_at(k, r0, kv_row, es), rows_at(v, r0, kv_row, es), sp,
                                       len, rows_at(k_cache, c0, kv_row, es), rows_at(v_cache, c0, kv_row, es),

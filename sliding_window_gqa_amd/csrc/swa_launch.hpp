@@ -34,14 +34,16 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
                               const void* v, const int32_t* start, int n_tok, void* kdst,
                               void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st);
 
-// Fast bf16 prefill: head_dim 128, group size 4.  Without a VarTab the LSE
-// is [B][Hq][C], or, with lse_total > 0, the columns of the B sequences in a
-// packed [Hq][lse_total] array whose first column lse points at.
+// LSE of a fixed-length batch [B][Hq][C] into its columns of a packed
+// [Hq][total] array (dst = the batch's first column).
+hipError_t launch_lse_pack(const float* src, float* dst, int B, int Hq, int C, long long total,
+                           hipStream_t st);
+
+// Fast bf16 prefill: head_dim 128, group size 4.
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
-                                       float* lse, const VarTab* vt, hipStream_t st,
-                                       long long lse_total = 0);
+                                       float* lse, const VarTab* vt, hipStream_t st);
 
 // Generic prefill (float32 or bf16, head_dim 64 or 128, any group size).
 hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,

@@ -163,7 +163,6 @@ struct PrefillArgs {
   int n_items;          // n_qtiles * Hkv * B, or the VarTab's item count
   uint16_t* out;
   float* lse;
-  long long lse_bs, lse_hs;   // fixed-length LSE: element strides of a sequence and of a head
   VarTab vt;            // packed sequences of their own lengths (varlen kernel)
 };
 
@@ -886,8 +885,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       }
       if (a.lse && g == 0 && tq < it.len) {
         const long long lo = VAR ? (long long)(h0 + qb) * a.vt.total + it.row0 + tq
-                             : DIL ? b * a.lse_bs + (h0 + qb) * a.lse_hs + (it.row0 - b * C) + dil * tq
-                                   : b * a.lse_bs + (h0 + qb) * a.lse_hs + tq;
+                             : DIL ? ((long long)b * sh.Hq + h0 + qb) * C + (it.row0 - b * C) + dil * tq
+                                   : ((long long)b * sh.Hq + h0 + qb) * C + tq;
         a.lse[lo] = (ref[qb] + log2f(lsum[qb][0])) * 0.69314718055994531f;
       }
     }
@@ -1023,8 +1022,7 @@ static int device_cu_count() {
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
-                                       float* lse, const VarTab* vt, hipStream_t st,
-                                       long long lse_total) {
+                                       float* lse, const VarTab* vt, hipStream_t st) {
   PrefillArgs a;
   a.sh = sh;
   a.rt = rt;
@@ -1040,9 +1038,6 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.n_qtiles = (rows + BM - 1) / BM;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  // [B][Hq][C], or the packed [Hq][lse_total] columns of B sequences of C tokens
-  a.lse_bs = lse_total > 0 ? (long long)C : (long long)sh.Hq * C;
-  a.lse_hs = lse_total > 0 ? lse_total : (long long)C;
   long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B * (dil ? sh.dil : 1);
   if (vt) {
     // items of sequence j: Hkv x its own query tiles, numbered after those of 0 .. j-1

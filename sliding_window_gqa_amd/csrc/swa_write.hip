@@ -111,7 +111,27 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
   }
 }
 
+// LSE rows of a fixed-length batch [B][Hq][C] into the columns of a packed
+// [Hq][total] array: dst[h][b*C + t] = src[b][h][t] (dst points at the
+// batch's first column).  One thread per element, in source order.
+__global__ void __launch_bounds__(256) lse_pack_kernel(const float* src, float* dst, int Hq, int C,
+                                                       long long total, int n) {
+  const int e = blockIdx.x * 256 + (int)threadIdx.x;
+  if (e >= n) return;
+  const int row = e / C, t = e - row * C;   // row = b * Hq + h
+  const int b = row / Hq, h = row - b * Hq;
+  dst[(long long)h * total + (long long)b * C + t] = src[e];
+}
+
 }  // namespace
+
+hipError_t launch_lse_pack(const float* src, float* dst, int B, int Hq, int C, long long total,
+                           hipStream_t st) {
+  const long long n = (long long)B * Hq * C;
+  if (n > INT32_MAX - 256 || B < 1 || Hq < 1 || C < 1) return hipErrorInvalidValue;
+  lse_pack_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(src, dst, Hq, C, total, (int)n);
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
                               const void* v, const int32_t* start, int n_tok, void* kdst,

@@ -202,6 +202,19 @@ def test_step_varlen_workspace():
                                None) == swa.SWA_ERR_WORKSPACE
 
 
+def test_step_varlen_workspace_equal_runs():
+    """Chunks of one length in one contiguous run: the step's fixed-length
+    path packs the run's LSE ([run][Hq][len] floats) through the workspace;
+    chunks of different lengths take the varlen kernel and need no such room."""
+    lib = swa.library()
+    p = P(batch=4)
+    bp = ctypes.byref(p)
+    keys = 80 * 8 * 128 * 2
+    assert lib.swa_step_varlen_workspace_bytes(bp, _lens(0, 40, 40, 0)) == keys + 2 * 32 * 40 * 4
+    assert lib.swa_step_varlen_workspace_bytes(bp, _lens(40, 40, 3, 0)) == -(-(83 * 8 * 128 * 2) // 256) * 256
+    assert lib.swa_step_varlen_workspace_bytes(bp, _lens(40, 0, 40, 0)) == keys   # not contiguous
+
+
 def test_step_varlen_workspace_over_several_decode_launches():
     """70 one-token sequences decode in two launches (64 + 6); the smaller
     launch takes more splits, and the workspace holds the larger need."""
