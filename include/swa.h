@@ -161,6 +161,25 @@ int swa_rope_keys(const swa_params* params, const void* k, const int32_t* start_
                   int32_t n_tok, void* k_rot, hipStream_t stream);
 
 /*
+ * swa_rope_keys_cache_write — swa_rope_keys and swa_cache_write in one pass
+ * over the chunk: every key rotated into k_rot, and the entries that survive
+ * the chunk (digest "Rolling Buffer KV Cache 동작 설명", 쓰기(write) 단계)
+ * stored into the caches; k_rot, k_cache and v_cache afterwards are
+ * byte-identical to those two calls'.  It writes the caches BEFORE the
+ * chunk's attention, so it is for chunks whose attention reads no cache: a
+ * sequence's first chunk (start_pos 0, or swa_prefill_attention called with
+ * NULL caches).  A chunk that reads the cache keeps the order of essay §4.1
+ * (swa_rope_keys, swa_prefill_attention, then swa_cache_write).
+ *   k, v      : [batch][n_tok][n_kv_heads][head_dim] raw keys, values.
+ *   k_rot     : [batch][n_tok][n_kv_heads][head_dim] rotated keys (output).
+ *   k_cache, v_cache : [batch][n_sink + window][n_kv_heads][head_dim].
+ * Errors as swa_cache_write; nothing is launched on an error.
+ */
+int swa_rope_keys_cache_write(const swa_params* params, const void* k, const void* v,
+                              const int32_t* start_pos, int32_t n_tok, void* k_rot,
+                              void* k_cache, void* v_cache, hipStream_t stream);
+
+/*
  * swa_prefill_attention — the attention pass of swa_prefill_chunk on keys
  * that are already rotated (k_rot from swa_rope_keys); queries are rotated on
  * load.  Arguments and semantics otherwise as swa_prefill_chunk; it needs no

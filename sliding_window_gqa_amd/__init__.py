@@ -15,7 +15,7 @@ __all__ = [
     "SwaError", "swa_params", "make_params", "library", "LIB_PATH",
     "swa_cache_write", "swa_prefill_chunk", "swa_prefill_workspace_bytes",
     "swa_decode", "swa_decode_step", "swa_decode_workspace_bytes", "swa_status_string",
-    "swa_rope_keys", "swa_prefill_attention",
+    "swa_rope_keys", "swa_prefill_attention", "swa_rope_keys_cache_write",
     "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen", "swa_prefill_attention_varlen",
     "swa_prefill_chunk_varlen", "swa_cache_write_varlen", "swa_step_varlen",
     "swa_step_varlen_workspace_bytes",
@@ -62,6 +62,7 @@ _SIGNATURES = {
     "swa_prefill_workspace_bytes": (_sz, [_P, _i32]),
     "swa_prefill_chunk": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "swa_rope_keys": (ctypes.c_int, [_P, _vp, _vp, _i32, _vp, _vp]),
+    "swa_rope_keys_cache_write": (ctypes.c_int, [_P, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "swa_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "swa_decode_workspace_bytes": (_sz, [_P]),
     "swa_decode": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -221,6 +222,24 @@ def swa_rope_keys(params, k, start_pos, k_rot=None, stream=None):
                                  _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), k.shape[1],
                                  _ptr(k_rot, "k_rot", dt, shp), _stream(stream))
     _check(st, "swa_rope_keys")
+    return k_rot
+
+
+def swa_rope_keys_cache_write(params, k, v, start_pos, k_cache, v_cache, k_rot=None, stream=None):
+    """swa_rope_keys and swa_cache_write in one pass, for a chunk whose
+    attention reads no cache (a sequence's first chunk); returns k_rot."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    n_tok = k.shape[1]
+    shp = (params.batch, n_tok, params.n_kv_heads, params.head_dim)
+    cshp = (params.batch, params.n_sink + params.window, params.n_kv_heads, params.head_dim)
+    if k_rot is None:
+        k_rot = torch.empty(shp, dtype=dt, device=k.device)
+    st = library().swa_rope_keys_cache_write(
+        ctypes.byref(params), _ptr(k, "k", dt, shp), _ptr(v, "v", dt, shp),
+        _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), n_tok, _ptr(k_rot, "k_rot", dt, shp),
+        _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp), _stream(stream))
+    _check(st, "swa_rope_keys_cache_write")
     return k_rot
 
 

@@ -247,6 +247,20 @@ int swa_rope_keys(const swa_params* params, const void* k, const int32_t* start_
                                           swa::kToDense, nullptr, stream));
 }
 
+int swa_rope_keys_cache_write(const swa_params* params, const void* k, const void* v,
+                              const int32_t* start_pos, int32_t n_tok, void* k_rot, void* k_cache,
+                              void* v_cache, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k || !v || !start_pos || !k_rot || !k_cache || !v_cache) return SWA_ERR_NULL;
+  if (n_tok < 1 || n_tok > (1 << 24)) return SWA_ERR_SHAPE;
+  if ((long long)sh.B * n_tok * sh.Hkv * (sh.D / 8) >= (1LL << 40)) return SWA_ERR_SHAPE;
+  return launched(swa::launch_cache_write(sh, rope_table(params), params->dtype == SWA_F32, k, v,
+                                          start_pos, n_tok, k_rot, v_cache, swa::kToBoth, nullptr,
+                                          stream, k_cache));
+}
+
 int swa_prefill_attention(const swa_params* params, const void* q, const void* k_rot,
                           const void* v, const void* k_cache, const void* v_cache,
                           const int32_t* start_pos, int32_t chunk_len, void* out, float* lse,

@@ -13,6 +13,7 @@ namespace swa {
 enum WriteMode {
   kToCache = 0,  // rolling-buffer slots of k_cache / v_cache (survivors only)
   kToDense = 1,  // rotated K into a dense [B][n_tok][Hkv][D] buffer (V untouched)
+  kToBoth = 2,   // both at once: every rotated key dense, survivors (k, v) into the caches
 };
 
 // Sequences of different chunk lengths, packed one after the other (rows of
@@ -30,9 +31,12 @@ struct VarTab {
   int item_off[kVarMax + 1];   // prefill work items, filled by the launcher
 };
 
+// kToBoth: kdst is the dense rotated-key buffer, vdst the value cache and
+// kcache the key cache.
 hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
                               const void* v, const int32_t* start, int n_tok, void* kdst,
-                              void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st);
+                              void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st,
+                              void* kcache = nullptr);
 
 // LSE of a fixed-length batch [B][Hq][C] into its columns of a packed
 // [Hq][total] array (dst = the batch's first column).

@@ -6,6 +6,11 @@
 // is applied to keys here, at their absolute position, so the cache holds
 // rotated keys and values verbatim.
 //
+// The same pass serves the dense key rotation (every rotated key into a
+// [B][n_tok] buffer) and, for a chunk whose attention reads no cache, both
+// at once: the key is rotated once and stored densely and, if it survives,
+// into its slot.
+//
 // Varlen batches (a VarTab) take each sequence's rows from its packed run and
 // its own length, in one grid row of exactly the blocks the sequences need;
 // the rule for survivors is the same per sequence.
@@ -32,7 +37,8 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
                                                          const void* __restrict__ v,
                                                          const int32_t* __restrict__ start, int n_tok,
                                                          void* __restrict__ kdst, void* __restrict__ vdst,
-                                                         int mode, int tok_per_block, int t_lo, VarTab vt) {
+                                                         int mode, int tok_per_block, int t_lo, VarTab vt,
+                                                         void* __restrict__ kcache) {
   const int cpr = sh.D / 8;           // chunks per (token, head) row: 8 or 16
   const int cpt = sh.Hkv * cpr;       // chunks per token
   int b, blk;
@@ -58,13 +64,17 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
   const int s0 = start[b];
   const int last = s0 + len - 1;
   const int p = s0 + t;
-  if (mode == kToCache && p >= sh.n_sink && p + sh.W <= last) return;  // overwritten later in this call
-  const long long row0 = srow + t;                                      // source token row
-  const long long drow0 = mode == kToCache ? (long long)b * sh.S + slot_of(p, sh.W, sh.n_sink) : row0;
+  const bool survives = p < sh.n_sink || p + sh.W > last;   // not overwritten later in this call
+  if (mode == kToCache && !survives) return;
+  const long long row0 = srow + t;                                                  // source token row
+  const long long crow0 = (long long)b * sh.S + slot_of(p, sh.W, sh.n_sink);        // its cache slot
+  const long long drow0 = mode == kToCache ? crow0 : row0;
+  const bool to_cache = mode == kToCache || (mode == kToBoth && survives);
   for (int ct = (int)threadIdx.x - tb * cpt; ct < cpt; ct += (int)blockDim.x) {
     const int h = ct / cpr, c = ct - h * cpr;
     const long long src_off = (row0 * sh.Hkv + h) * sh.D + 8 * c;
     const long long dst_off = (drow0 * sh.Hkv + h) * sh.D + 8 * c;
+    const long long cst_off = (crow0 * sh.Hkv + h) * sh.D + 8 * c;   // the cache entry (v, and k in kToBoth)
 
     float x[8];
     if (F32) {
@@ -92,9 +102,14 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
       float4* dst = reinterpret_cast<float4*>(static_cast<float*>(kdst) + dst_off);
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);
-      if (mode == kToCache) {
+      if (mode == kToBoth && survives) {
+        float4* kd = reinterpret_cast<float4*>(static_cast<float*>(kcache) + cst_off);
+        kd[0] = make_float4(x[0], x[1], x[2], x[3]);
+        kd[1] = make_float4(x[4], x[5], x[6], x[7]);
+      }
+      if (to_cache) {
         const float4* vs = reinterpret_cast<const float4*>(static_cast<const float*>(v) + src_off);
-        float4* vd = reinterpret_cast<float4*>(static_cast<float*>(vdst) + dst_off);
+        float4* vd = reinterpret_cast<float4*>(static_cast<float*>(vdst) + cst_off);
         vd[0] = vs[0];
         vd[1] = vs[1];
       }
@@ -103,8 +118,9 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = pack_bf16(x[2 * j], x[2 * j + 1]);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + dst_off) = w;
-      if (mode == kToCache) {
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(vdst) + dst_off) =
+      if (mode == kToBoth && survives) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kcache) + cst_off) = w;
+      if (to_cache) {
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(vdst) + cst_off) =
             *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + src_off);
       }
     }
@@ -135,7 +151,8 @@ hipError_t launch_lse_pack(const float* src, float* dst, int B, int Hq, int C, l
 
 hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, const void* k,
                               const void* v, const int32_t* start, int n_tok, void* kdst,
-                              void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st) {
+                              void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st,
+                              void* kcache) {
   const int threads = 256;
   const int cpt = sh.Hkv * (sh.D / 8);
   const int tok_per_block = cpt <= threads ? threads / cpt : 1;
@@ -162,17 +179,17 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
   if (f32) {
     if (vt)
       cache_write_kernel<true, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                     (int)mode, tok_per_block, t_lo, t);
+                                                                     (int)mode, tok_per_block, t_lo, t, kcache);
     else
       cache_write_kernel<true, false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                      (int)mode, tok_per_block, t_lo, t);
+                                                                      (int)mode, tok_per_block, t_lo, t, kcache);
   } else {
     if (vt)
       cache_write_kernel<false, true><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                      (int)mode, tok_per_block, t_lo, t);
+                                                                      (int)mode, tok_per_block, t_lo, t, kcache);
     else
       cache_write_kernel<false, false><<<grid, dim3(threads), 0, st>>>(sh, rt, k, v, start, n_tok, kdst, vdst,
-                                                                       (int)mode, tok_per_block, t_lo, t);
+                                                                       (int)mode, tok_per_block, t_lo, t, kcache);
   }
   return hipGetLastError();
 }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
             "swa_prefill_attention_varlen", "swa_prefill_chunk_varlen",
             "swa_cache_write_varlen", "swa_step_varlen",
             "swa_step_varlen_workspace_bytes", "swa_decode_step_noalloc",
-            "swa_noalloc_scratch_bytes"} <= set(names)
+            "swa_noalloc_scratch_bytes", "swa_rope_keys_cache_write"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -73,6 +73,7 @@ def test_bad_params_rejected_everywhere(bad, code):
     assert lib.swa_decode_step_noalloc(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
     assert lib.swa_debug_slots(bp, FAKE, 4, FAKE, None) == code
     assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, FAKE, None) == code
+    assert lib.swa_rope_keys_cache_write(bp, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == code
     assert lib.swa_prefill_attention(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None) == code
     assert lib.swa_decode_workspace_bytes(bp) == 0
     assert lib.swa_prefill_workspace_bytes(bp, 16) == 0
@@ -95,6 +96,10 @@ def test_null_pointers_rejected():
         assert lib.swa_decode_step(bp, *args, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL, i
     assert lib.swa_debug_mask(bp, 5, None, 4, FAKE, None) == swa.SWA_ERR_NULL
     assert lib.swa_rope_keys(bp, FAKE, FAKE, 4, None, None) == swa.SWA_ERR_NULL
+    for i in range(6):   # k, v, start_pos, k_rot, k_cache, v_cache
+        args = [FAKE] * 6
+        args[i] = None
+        assert lib.swa_rope_keys_cache_write(bp, *args[:3], 4, *args[3:], None) == swa.SWA_ERR_NULL, i
     assert lib.swa_prefill_attention(bp, FAKE, None, FAKE, None, None, FAKE, 16, FAKE, None, None) == swa.SWA_ERR_NULL
     assert lib.swa_prefill_attention(bp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, None, None) == swa.SWA_ERR_NULL
 
@@ -104,6 +109,7 @@ def test_sizes_and_workspace_rejected():
     p = P()
     bp = ctypes.byref(p)
     assert lib.swa_cache_write(bp, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == swa.SWA_ERR_SHAPE
+    assert lib.swa_rope_keys_cache_write(bp, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None) == swa.SWA_ERR_SHAPE
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 0, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_SHAPE
     need = lib.swa_prefill_workspace_bytes(bp, 16)
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, need - 1, None) == swa.SWA_ERR_WORKSPACE

@@ -70,6 +70,31 @@ def test_cache_write_placement(dtype, theta, S):
             assert (err <= ulp * np.abs(c.k[held]) + 1e-6).all(), err.max()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("theta", [0.0, 10000.0])
+@pytest.mark.parametrize("S", [0, 3])
+def test_rope_keys_cache_write_equals_the_two_calls(dtype, theta, S):
+    """The one-pass rotation + cache write leaves k_rot and both caches
+    byte-identical to swa_rope_keys followed by swa_cache_write: chunks
+    shorter and longer than the window, at starts across fills and wraps,
+    on NaN-filled caches (a stray store shows)."""
+    print(f"rope_keys_cache_write dtype={dtype} theta={theta} n_sink={S}", flush=True)
+    B, Hkv, D, W = 3, 2, 128, 20
+    p = swa.make_params(B, 4 * Hkv, Hkv, D, W, S, 0.0, theta, dtype)
+    for n, start in [(7, [0, 5, 33]), (45, [7, 12, 40]), (1, [52, 57, 85]), (19, [0, 58, 86])]:
+        k = rnd((B, n, Hkv, D), "k", n, dtype).to(DEV)
+        v = rnd((B, n, Hkv, D), "v", n, dtype).to(DEV)
+        st = torch.tensor(start, dtype=torch.int32, device=DEV)
+        kc1 = torch.full((B, S + W, Hkv, D), float("nan"), dtype=dtype, device=DEV)
+        vc1 = kc1.clone()
+        kc2, vc2 = kc1.clone(), vc1.clone()
+        kr1 = swa.swa_rope_keys(p, k, st)
+        swa.swa_cache_write(p, k, v, st, kc1, vc1)
+        kr2 = swa.swa_rope_keys_cache_write(p, k, v, st, kc2, vc2)
+        for a, b_, what in ((kr1, kr2, "k_rot"), (kc1, kc2, "k_cache"), (vc1, vc2, "v_cache")):
+            assert torch.equal(a.view(torch.uint8), b_.view(torch.uint8)), (what, n, start)
+
+
 # ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------

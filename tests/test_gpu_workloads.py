@@ -227,3 +227,23 @@ def test_mixed_varlen_step_b64():
         np.testing.assert_array_equal(vc_b[held], c.v[held])
         err = np.abs(kc_b[held] - c.k[held])
         assert (err <= 2.0 ** -8 * np.abs(c.k[held]) + 1e-6).all(), (b, err.max())
+
+
+def test_rope_keys_cache_write_full_size():
+    """The headline layer (8192 tokens, window 4096): the one-pass rotation +
+    cache write against swa_rope_keys + swa_cache_write, byte for byte."""
+    wl = synth.workload(2)
+    print(f"rope_keys_cache_write {wl.name}", flush=True)
+    N, Hq, Hkv, D, W = wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    p = swa.make_params(1, Hq, Hkv, D, W, 0, 0.0, wl.rope_theta)
+    k = synth.normal((1, N, Hkv, D), 2, "k").to(DEV)
+    v = synth.normal((1, N, Hkv, D), 2, "v").to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kc1 = torch.full((1, W, Hkv, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc1 = kc1.clone()
+    kc2, vc2 = kc1.clone(), vc1.clone()
+    kr1 = swa.swa_rope_keys(p, k, st)
+    swa.swa_cache_write(p, k, v, st, kc1, vc1)
+    kr2 = swa.swa_rope_keys_cache_write(p, k, v, st, kc2, vc2)
+    for a, b, what in ((kr1, kr2, "k_rot"), (kc1, kc2, "k_cache"), (vc1, vc2, "v_cache")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), what
