@@ -205,6 +205,18 @@ bool equal_runs(const Shape& sh, const int32_t* lens, size_t* lse_bytes) {
   return true;
 }
 
+// Bytes of the decode partials of a varlen step's one-token sequences (the
+// largest launch), rounded up to 256.
+size_t step_part_bytes(const Shape& sh, const int32_t* lens, long long total) {
+  size_t part = 0;
+  for_decode_groups(sh, lens, total, [&](const swa::DecodeMap&, const Shape& gs) {
+    const size_t need = (size_t)gs.B * gs.Hq * swa::decode_splits(gs) * (gs.D + 2) * sizeof(float);
+    if (need > part) part = need;
+    return SWA_OK;
+  });
+  return (part + 255) / 256 * 256;
+}
+
 // Bytes of the rotated keys of a varlen step, rounded up to 256.
 size_t step_keys_bytes(const swa_params* p, long long total) {
   const size_t kb = (size_t)total * p->n_kv_heads * p->head_dim * elem_size(p->dtype);
@@ -456,16 +468,11 @@ size_t swa_step_varlen_workspace_bytes(const swa_params* params, const int32_t* 
   int longest;
   if (check_params(params, &sh) != SWA_OK) return 0;
   if (check_lens(params, chunk_lens, &total, &longest) != SWA_OK) return 0;
-  size_t part = 0;
-  for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap&, const Shape& gs) {
-    const size_t need = (size_t)gs.B * gs.Hq * swa::decode_splits(gs) * (gs.D + 2) * sizeof(float);
-    if (need > part) part = need;
-    return SWA_OK;
-  });
-  // the fixed-length path packs each run's LSE through the same region
+  // the fixed-length path keeps each run's LSE [run][Hq][len] in a region of
+  // its own after the decode partials, until the step's tail repacks it
   size_t run_lse = 0;
-  if (equal_runs(sh, chunk_lens, &run_lse) && run_lse > part) part = run_lse;
-  return step_keys_bytes(params, total) + part;
+  if (!equal_runs(sh, chunk_lens, &run_lse)) run_lse = 0;
+  return step_keys_bytes(params, total) + step_part_bytes(sh, chunk_lens, total) + run_lse;
 }
 
 int swa_step_varlen(const swa_params* params, const void* q, const void* k, const void* v,
@@ -493,7 +500,7 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
   const size_t es = elem_size(params->dtype);
   const long long kv_row = (long long)sh.Hkv * sh.D, q_row = (long long)sh.Hq * sh.D;
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + step_keys_bytes(params, total));
-  float* run_lse = part;   // (the decode partials come after the runs' LSE is packed)
+  float* run_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + step_part_bytes(sh, chunk_lens, total));
   // Chunks of one size (chunked prefill with a fixed chunk length): when in
   // every group of kVarMax sequences those of more than one token form one
   // contiguous run of a single length, each run takes the fixed-length
@@ -501,6 +508,67 @@ int swa_step_varlen(const swa_params* params, const void* q, const void* k, cons
   // sequences the decode kernel that stores their new entries itself: the
   // launches of the separate fixed-length calls, in one call.
   size_t run_lse_bytes = 0;
+  if (equal_runs(sh, chunk_lens, &run_lse_bytes) && sh.B <= swa::kVarMax) {
+    // One group: the run's key rotation and attention, the one-token
+    // sequences' decode (with its fused cache write), then one tail launch:
+    // their combine, the run's LSE repack and the run's cache write (after
+    // its attention; the decode touches other sequences' caches).
+    int j0, j1, len;
+    equal_run(chunk_lens, 0, sh.B, &j0, &j1, &len);
+    long long r0 = 0;
+    for (int j = 0; j < j0; ++j) r0 += chunk_lens[j];
+    swa::StepTail tail{};
+    if (j1 > j0) {
+      Shape rs = sh;
+      rs.B = j1 - j0;
+      const int32_t* sp = start_pos + j0;
+      const long long c0 = (long long)j0 * sh.S;
+      void* kr = rows_at(workspace, r0, kv_row, es);
+      hipError_t e = swa::launch_cache_write(rs, rt, false, rows_at(k, r0, kv_row, es), nullptr, sp, len,
+                                             kr, nullptr, swa::kToDense, nullptr, stream);
+      if (e == hipSuccess)
+        e = swa::launch_prefill_bf16_d128_g4(rs, rt, rows_at(q, r0, q_row, es), kr, rows_at(v, r0, kv_row, es),
+                                             rows_at((const void*)k_cache, c0, kv_row, es),
+                                             rows_at((const void*)v_cache, c0, kv_row, es), sp, len,
+                                             rows_at(out, r0, q_row, es), lse ? run_lse : nullptr, nullptr, stream);
+      if (e != hipSuccess) return SWA_ERR_LAUNCH;
+      if (lse) {
+        tail.psrc = run_lse;
+        tail.pdst = lse + r0;
+        tail.pHq = sh.Hq;
+        tail.pC = len;
+        tail.pn = rs.B * sh.Hq * len;
+        tail.ptotal = total;
+      }
+      tail.wsh = rs;
+      tail.rt = rt;
+      tail.k = rows_at(k, r0, kv_row, es);
+      tail.v = rows_at(v, r0, kv_row, es);
+      tail.start = sp;
+      tail.n_tok = len;
+      tail.kc = rows_at(k_cache, c0, kv_row, es);
+      tail.vc = rows_at(v_cache, c0, kv_row, es);
+    } else {
+      tail.wsh.B = 0;
+    }
+    const swa::FusedWrite fw{k, v, k_cache, v_cache};
+    st = for_decode_groups(sh, chunk_lens, total, [&](const swa::DecodeMap& m, const Shape& gs) {
+      const int n = swa::decode_splits_fast(gs);
+      hipError_t e = swa::launch_decode_bf16_d128_g4(gs, rt, q, k_cache, v_cache, start_pos, part, n, out,
+                                                     lse, &fw, &m, stream);
+      if (n > 1) {   // (one split writes out and lse itself)
+        tail.csh = gs;
+        tail.part = part;
+        tail.n_splits = n;
+        tail.out = out;
+        tail.lse = lse;
+        tail.map = m;
+      }
+      return launched(e);
+    });
+    if (st != SWA_OK) return st;
+    return launched(swa::launch_step_tail(tail, stream));
+  }
   if (equal_runs(sh, chunk_lens, &run_lse_bytes)) {
     long long row = 0;   // packed row of sequence g0
     for (int g0 = 0; g0 < sh.B; g0 += swa::kVarMax) {

@@ -32,6 +32,7 @@
 
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
+#include "swa_passes.hpp"
 
 namespace swa {
 namespace {
@@ -510,53 +511,14 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(Shape sh, RopeTab rt
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one work-group per (query head, sequence), one thread per head dim.
+// Combine: one work-group per (query head, sequence), one thread per head
+// dim (the body, combine_column, is shared with the mixed step's tail).
 // ---------------------------------------------------------------------------
-// Combine: one block of D threads per (sequence, query head); thread d owns
-// element d.  The splits' maxima and sums come in with one load per split,
-// spread over the block, and each split's weight 2^(m_s - m*) is formed
-// once; the partial outputs are then loaded eight splits at a time, so that
-// the block waits for memory a few times rather than once per split.  The
-// sums run over the splits in ascending order.
-constexpr int kMaxSplits = 512;   // decode_splits() never exceeds it
 template <bool F32>
 __global__ void __launch_bounds__(128) decode_combine_kernel(Shape sh, const float* part, int n_splits,
                                                              void* out, float* lse, DecodeMap map) {
   __shared__ float sm_m[kMaxSplits], sm_l[kMaxSplits], sm_f[kMaxSplits];
-  const int h = blockIdx.x, z = blockIdx.y, d = threadIdx.x;
-  const int r = map.n ? map.row[z] : z;   // the token's row in out
-  const int D = sh.D;
-  const float* src = part + ((long long)z * sh.Hq + h) * n_splits * (D + 2);
-  for (int s = d; s < n_splits; s += D) {
-    sm_m[s] = src[s * (D + 2) + D];
-    sm_l[s] = src[s * (D + 2) + D + 1];
-  }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, sm_m[s]);
-  for (int s = d; s < n_splits; s += D) sm_f[s] = (sm_m[s] == -INFINITY) ? 0.f : exp2f(sm_m[s] - M);
-  __syncthreads();
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < n_splits; ++s) L += sm_l[s] * sm_f[s];
-  int s = 0;
-  for (; s + 8 <= n_splits; s += 8) {
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = src[(s + u) * (D + 2) + d];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) O += x[u] * sm_f[s + u];
-  }
-  for (; s < n_splits; ++s) O += src[s * (D + 2) + d] * sm_f[s];
-  const float val = O / L;
-  const long long off = ((long long)r * sh.Hq + h) * D + d;
-  if (F32)
-    static_cast<float*>(out)[off] = val;
-  else
-    static_cast<uint16_t*>(out)[off] = to_bf16_bits(val);
-  if (lse && d == 0) {
-    const long long lo = map.n ? (long long)h * map.lse_hs + r : (long long)r * sh.Hq + h;
-    lse[lo] = (M + log2f(L)) * 0.69314718055994531f;
-  }
+  combine_column<F32>(sh, part, n_splits, out, lse, map, blockIdx.x, blockIdx.y, threadIdx.x, sm_m, sm_l, sm_f);
 }
 
 }  // namespace

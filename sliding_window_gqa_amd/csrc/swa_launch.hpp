@@ -75,6 +75,36 @@ struct FusedWrite {
   void* k_cache;
   void* v_cache;
 };
+
+// The tail of a mixed step in one launch: the decode combine of the
+// one-token sequences (map columns; csh.B = map.n), the run's LSE repack
+// (pn elements of psrc [B][pHq][pC] into pdst [pHq][ptotal]) and the run's
+// rolling-buffer write (wsh.B sequences of n_tok tokens at rows b * n_tok of
+// k / v); a part with nothing to do has 0 sequences / elements.  The
+// launcher fills the block counts.
+struct StepTail {
+  Shape csh;
+  const float* part;
+  int n_splits;
+  void* out;
+  float* lse;
+  DecodeMap map;
+  const float* psrc;
+  float* pdst;
+  int pHq, pC, pn;
+  long long ptotal;
+  Shape wsh;
+  RopeTab rt;
+  const void* k;
+  const void* v;
+  const int32_t* start;
+  int n_tok;
+  void* kc;
+  void* vc;
+  int nb_comb, nb_pack, nb_write, tpb, t_lo, bps;
+};
+hipError_t launch_step_tail(StepTail t, hipStream_t st);
+
 int decode_splits(const Shape& sh);
 // Splits of the fast decode kernel (a dilated window cuts its keys, fewer
 // than the slots); never more than decode_splits(sh).

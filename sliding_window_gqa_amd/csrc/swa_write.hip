@@ -28,6 +28,7 @@
 
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
+#include "swa_passes.hpp"
 
 namespace swa {
 namespace {
@@ -39,8 +40,7 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
                                                          void* __restrict__ kdst, void* __restrict__ vdst,
                                                          int mode, int tok_per_block, int t_lo, VarTab vt,
                                                          void* __restrict__ kcache) {
-  const int cpr = sh.D / 8;           // chunks per (token, head) row: 8 or 16
-  const int cpt = sh.Hkv * cpr;       // chunks per token
+  const int cpt = sh.Hkv * (sh.D / 8);   // 16-byte chunks per token
   int b, blk;
   if (VAR) {
     // one grid row: block L is block L - item_off[b] of sequence b, the
@@ -62,69 +62,8 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
   const int t = t_lo + blk * tok_per_block + tb;
   if (tb >= tok_per_block || t >= len) return;
   const int s0 = start[b];
-  const int last = s0 + len - 1;
-  const int p = s0 + t;
-  const bool survives = p < sh.n_sink || p + sh.W > last;   // not overwritten later in this call
-  if (mode == kToCache && !survives) return;
-  const long long row0 = srow + t;                                                  // source token row
-  const long long crow0 = (long long)b * sh.S + slot_of(p, sh.W, sh.n_sink);        // its cache slot
-  const long long drow0 = mode == kToCache ? crow0 : row0;
-  const bool to_cache = mode == kToCache || (mode == kToBoth && survives);
-  for (int ct = (int)threadIdx.x - tb * cpt; ct < cpt; ct += (int)blockDim.x) {
-    const int h = ct / cpr, c = ct - h * cpr;
-    const long long src_off = (row0 * sh.Hkv + h) * sh.D + 8 * c;
-    const long long dst_off = (drow0 * sh.Hkv + h) * sh.D + 8 * c;
-    const long long cst_off = (crow0 * sh.Hkv + h) * sh.D + 8 * c;   // the cache entry (v, and k in kToBoth)
-
-    float x[8];
-    if (F32) {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(k) + src_off);
-      const float4 a = src[0], bb = src[1];
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = bb.x; x[5] = bb.y; x[6] = bb.z; x[7] = bb.w;
-    } else {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(k) + src_off);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = bf16_lo(w[j]);
-        x[2 * j + 1] = bf16_hi(w[j]);
-      }
-    }
-    if (sh.rope) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float cs, sn;
-        rope_cs(p, rt.rev[4 * c + j], cs, sn);
-        rotate(x[2 * j], x[2 * j + 1], cs, sn);
-      }
-    }
-    if (F32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(kdst) + dst_off);
-      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
-      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
-      if (mode == kToBoth && survives) {
-        float4* kd = reinterpret_cast<float4*>(static_cast<float*>(kcache) + cst_off);
-        kd[0] = make_float4(x[0], x[1], x[2], x[3]);
-        kd[1] = make_float4(x[4], x[5], x[6], x[7]);
-      }
-      if (to_cache) {
-        const float4* vs = reinterpret_cast<const float4*>(static_cast<const float*>(v) + src_off);
-        float4* vd = reinterpret_cast<float4*>(static_cast<float*>(vdst) + cst_off);
-        vd[0] = vs[0];
-        vd[1] = vs[1];
-      }
-    } else {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = pack_bf16(x[2 * j], x[2 * j + 1]);
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + dst_off) = w;
-      if (mode == kToBoth && survives) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kcache) + cst_off) = w;
-      if (to_cache) {
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(vdst) + cst_off) =
-            *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + src_off);
-      }
-    }
-  }
+  rotate_store_token<F32>(sh, rt, k, v, b, srow, t, s0, s0 + len - 1, (int)threadIdx.x - tb * cpt,
+                          (int)blockDim.x, kdst, vdst, mode, kcache);
 }
 
 // LSE rows of a fixed-length batch [B][Hq][C] into the columns of a packed
@@ -139,7 +78,65 @@ __global__ void __launch_bounds__(256) lse_pack_kernel(const float* src, float* 
   dst[(long long)h * total + (long long)b * C + t] = src[e];
 }
 
+// The tail of a mixed step (swa_step_varlen with a run of equal chunks), in
+// one launch of 128-thread blocks: the decode combine of the one-token
+// sequences (blocks [0, nb_comb)), the run's LSE repack ([.., + nb_pack)) and
+// the run's rolling-buffer write ([.., + nb_write)).  The three touch
+// disjoint memory; each block does one job.
+__global__ void __launch_bounds__(128) step_tail_kernel(StepTail t) {
+  __shared__ float sm_m[kMaxSplits], sm_l[kMaxSplits], sm_f[kMaxSplits];
+  int blk = blockIdx.x;
+  if (blk < t.nb_comb) {
+    combine_column<false>(t.csh, t.part, t.n_splits, t.out, t.lse, t.map, blk % t.csh.Hq, blk / t.csh.Hq,
+                          (int)threadIdx.x, sm_m, sm_l, sm_f);
+    return;
+  }
+  blk -= t.nb_comb;
+  if (blk < t.nb_pack) {
+    const int e = blk * 128 + (int)threadIdx.x;
+    if (e < t.pn) {
+      const int row = e / t.pC, c = e - row * t.pC;   // row = b * Hq + h
+      const int b = row / t.pHq, h = row - b * t.pHq;
+      t.pdst[(long long)h * t.ptotal + (long long)b * t.pC + c] = t.psrc[e];
+    }
+    return;
+  }
+  blk -= t.nb_pack;
+  // the run's write: block blk covers tokens t_lo + tpb * (blk % bps) .. of sequence blk / bps
+  const int cpt = t.wsh.Hkv * (t.wsh.D / 8);
+  const int b = blk / t.bps, tb = (int)threadIdx.x / cpt;
+  const int tok = t.t_lo + (blk - b * t.bps) * t.tpb + tb;
+  if (b >= t.wsh.B || tb >= t.tpb || tok >= t.n_tok) return;
+  const int s0 = t.start[b];
+  rotate_store_token<false>(t.wsh, t.rt, t.k, t.v, b, (long long)b * t.n_tok, tok, s0, s0 + t.n_tok - 1,
+                            (int)threadIdx.x - tb * cpt, 128, t.kc, t.vc, kToCache, nullptr);
+}
+
 }  // namespace
+
+hipError_t launch_step_tail(StepTail t, hipStream_t st) {
+  // combine: one block of D = 128 threads per (one-token sequence, query head)
+  t.nb_comb = t.map.n > 0 ? t.map.n * t.csh.Hq : 0;
+  if (t.nb_comb > 0 && (t.csh.D != 128 || t.n_splits < 2 || t.n_splits > kMaxSplits)) return hipErrorInvalidValue;
+  t.nb_pack = t.pn > 0 ? (t.pn + 127) / 128 : 0;
+  t.nb_write = 0;
+  if (t.wsh.B > 0) {
+    const int cpt = t.wsh.Hkv * (t.wsh.D / 8);
+    if (cpt > 128) return hipErrorInvalidValue;
+    t.tpb = 128 / cpt;
+    // without sinks only the last W tokens of the run can survive it
+    t.t_lo = (t.wsh.n_sink == 0 && t.n_tok > t.wsh.W) ? t.n_tok - t.wsh.W : 0;
+    t.bps = (t.n_tok - t.t_lo + t.tpb - 1) / t.tpb;
+    const long long nb = (long long)t.bps * t.wsh.B;
+    if (nb > INT32_MAX / 2) return hipErrorInvalidValue;
+    t.nb_write = (int)nb;
+  }
+  const long long total = (long long)t.nb_comb + t.nb_pack + t.nb_write;
+  if (total == 0) return hipSuccess;
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  step_tail_kernel<<<dim3((unsigned)total), dim3(128), 0, st>>>(t);
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_pack(const float* src, float* dst, int B, int Hq, int C, long long total,
                            hipStream_t st) {
