@@ -309,11 +309,11 @@ def main():
         dec_ms = sum(dec_times)
         dec_achieved = (dec_bytes + write_bytes) / (dec_ms * 1e-3) / 1e9
         # the same 256 steps again, from the same cache state, with the
-        # Infinity Cache (MALL, 256 MB) flushed before each step by a 512 MiB fill
+        # Infinity Cache (MALL, 256 MB) flushed before each step by a 1 GiB fill
         kc4.copy_(kc4_0)
         vc4.copy_(vc4_0)
         del kc4_0, vc4_0
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
         for s in range(T):
             flush.fill_(s & 255)
@@ -339,7 +339,7 @@ def main():
                          "bytes": "valid K/V slots read once + Q + O + new k/v read and stored"},
             "mall_flushed": {"avg_call_ms": round(fl_ms / T, 4), "gbps": round(fl_gbps, 1),
                              "frac": round(fl_gbps / PEAK_HBM_GBPS, 4),
-                             "note": "same steps from the same cache state, a 512 MiB fill before each call"},
+                             "note": "same steps from the same cache state, a 1 GiB fill before each call"},
         }
         del kc4, vc4, qs, ks, vs
 
@@ -851,10 +851,10 @@ def sink_workload(swa, synth, torch, dev):
     o5 = torch.empty((B, Hq, D), dtype=bf, device=dev)
     l5 = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws5 = torch.empty(swa.swa_decode_workspace_bytes(p5), dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def run5(flush_each):
-        # flushed: a 512 MiB fill before each step; warm: the steps back to back
+        # flushed: a 1 GiB fill before each step; warm: the steps back to back
         evs = []
         for s in range(T):
             if flush_each:
@@ -901,7 +901,7 @@ def sink_workload(swa, synth, torch, dev):
         "gbps_mall_flushed": round(bytes5 / (ms_flushed * 1e-3) / 1e9, 1),
         "ms_per_decode_warm": round(ms_warm, 4),
         "gbps_warm_cache_resident": round(bytes5 / (ms_warm * 1e-3) / 1e9, 1),
-        "note": "working set 256 MiB fits the 256 MB Infinity Cache; the flushed figure writes 512 MiB before each step",
+        "note": "working set 256 MiB fits the 256 MB Infinity Cache; the flushed figure writes 1 GiB before each step",
     }
     return ctx
 
