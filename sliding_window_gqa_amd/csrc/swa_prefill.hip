@@ -914,7 +914,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Generic kernel: one thread per (query position, query head).
+// Generic kernel: 16 lanes per (query position, query head); a work-group of
+// 4 queries shares its key tiles in LDS.
 // ---------------------------------------------------------------------------
 template <bool F32>
 __device__ inline float ld(const void* base, long long off) {
@@ -929,78 +930,115 @@ __device__ inline void st(void* base, long long off, float x) {
     static_cast<uint16_t*>(base)[off] = to_bf16_bits(x);
 }
 
+// Sum over the 16 lanes of a DPP row, in every lane of the row: quad
+// butterflies (lane ^ 1, lane ^ 2), then the half-row and the row mirrors.
+template <int CTRL>
+__device__ inline float dpp_f(float y) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), CTRL, 0xF, 0xF, true));
+}
+__device__ inline float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);   // row_half_mirror
+  x += dpp_f<0x140>(x);   // row_mirror
+  return x;
+}
+
 template <bool F32, int D>
 __global__ void __launch_bounds__(64) prefill_generic_kernel(Shape sh, RopeTab rt, const void* q,
                                                              const void* kr, const void* v,
                                                              const void* kc, const void* vc,
                                                              const int32_t* start, int C, void* out,
                                                              float* lse, VarTab vt) {
-  const int t = blockIdx.x * 64 + threadIdx.x;
+  // One work-group (one wave) per GQ = 4 consecutive queries of one head;
+  // 16 lanes per query, each owning DP = D/16 elements of q and o, so that a
+  // score is 16 short partial dots and a 4-step reduction.  The candidate
+  // keys of the 4 queries (the sinks below the first query's window, then
+  // the union of the windows) stream through LDS in tiles of TK keys loaded
+  // by the whole wave.
+  constexpr int GQ = 4, TK = 32, DP = D / 16;
+  __shared__ float ks[TK][D], vs[TK][D];
+  const int tid = threadIdx.x, qi = tid >> 4, part = tid & 15;
+  const int t_first = blockIdx.x * GQ, t = t_first + qi;
   const int h = blockIdx.y, b = blockIdx.z;
   // the sequence's rows: b * C .. + C, or its packed run (vt.n > 0)
   const long long r0 = vt.n ? (long long)vt.row_off[b] : (long long)b * C;
   const int len = vt.n ? vt.row_off[b + 1] - vt.row_off[b] : C;
-  if (t >= len) return;
+  if (t_first >= len) return;   // (uniform: the whole work-group)
+  const bool active = t < len;
   const int kvh = h / (sh.Hq / sh.Hkv);
   const int s0 = start[b];
-  const int I = s0 + t;
-  float qv[D];
-  const long long qoff = ((r0 + t) * sh.Hq + h) * D;
+  const int tq = active ? t : t_first;
+  const int I = s0 + tq;
+  float qv[DP];
+  const long long qoff = ((r0 + tq) * sh.Hq + h) * D + part * DP;
 #pragma unroll
-  for (int d = 0; d < D; ++d) qv[d] = ld<F32>(q, qoff + d);
+  for (int d = 0; d < DP; ++d) qv[d] = ld<F32>(q, qoff + d);
   if (sh.rope) {
 #pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) {
+    for (int kk = 0; kk < DP / 2; ++kk) {
       float cs, sn;
-      rope_cs(I, rt.rev[kk], cs, sn);
+      rope_cs(I, rt.rev[part * DP / 2 + kk], cs, sn);
       rotate(qv[2 * kk], qv[2 * kk + 1], cs, sn);
     }
   }
   if (!F32) {
     // the matrix path multiplies bf16 operands: round the rotated query alike
 #pragma unroll
-    for (int d = 0; d < D; ++d) qv[d] = __uint_as_float(((uint32_t)to_bf16_bits(qv[d])) << 16);
+    for (int d = 0; d < DP; ++d) qv[d] = __uint_as_float(((uint32_t)to_bf16_bits(qv[d])) << 16);
   }
-  float o[D];
+  float o[DP];
 #pragma unroll
-  for (int d = 0; d < D; ++d) o[d] = 0.f;
+  for (int d = 0; d < DP; ++d) o[d] = 0.f;
   float m = -INFINITY, l = 0.f;
-  auto visit = [&](int j) {
-    const void *kb, *vb;
-    long long off;
-    if (j >= s0) {
-      kb = kr;
-      vb = v;
-      off = ((r0 + (j - s0)) * sh.Hkv + kvh) * D;
-    } else {
-      if (!kc) return;
-      kb = kc;
-      vb = vc;
-      off = (((long long)b * sh.S + slot_of(j, sh.W, sh.n_sink)) * sh.Hkv + kvh) * D;
+  // candidate keys: [0, min(n_sink, wlo)) and [wlo, I_last]
+  const int I_last = s0 + min(t_first + GQ - 1, len - 1);
+  const int wlo = max(0, s0 + t_first - sh.W + 1);
+  auto run = [&](int lo, int hi) {   // keys lo .. hi (inclusive)
+    for (int j0 = lo; j0 <= hi; j0 += TK) {
+      __syncthreads();   // the previous tile is consumed
+      for (int e = tid; e < TK * D; e += 64) {
+        const int kk = e / D, d = e - kk * D, j = j0 + kk;
+        float kx = 0.f, vx = 0.f;
+        if (j <= hi && (j >= s0 || kc)) {
+          // a key of the chunk, or of the cache as it stood before the chunk
+          const bool ch = j >= s0;
+          const long long off = ch ? ((r0 + (j - s0)) * sh.Hkv + kvh) * D
+                                   : (((long long)b * sh.S + slot_of(j, sh.W, sh.n_sink)) * sh.Hkv + kvh) * D;
+          kx = ld<F32>(ch ? kr : kc, off + d);
+          vx = ld<F32>(ch ? v : vc, off + d);
+        }
+        ks[kk][d] = kx;
+        vs[kk][d] = vx;
+      }
+      __syncthreads();
+      const int nk = min(TK, hi - j0 + 1);
+      for (int kk = 0; kk < nk; ++kk) {
+        const int j = j0 + kk;
+        float sc = 0.f;
+#pragma unroll
+        for (int d = 0; d < DP; ++d) sc = fmaf(qv[d], ks[kk][part * DP + d], sc);
+        sc = row16_sum(sc);   // the 16 lanes of the query add their partial dots
+        if (!active || !key_in_set(I, j, sh.W, sh.n_sink, sh.dil) || (j < s0 && !kc)) continue;
+        sc *= sh.scale_log2;
+        const float mn = fmaxf(m, sc);
+        const float al = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+        const float pp = exp2f(sc - mn);
+        l = l * al + pp;
+#pragma unroll
+        for (int d = 0; d < DP; ++d) o[d] = fmaf(o[d], al, pp * vs[kk][part * DP + d]);
+        m = mn;
+      }
     }
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; ++d) s = fmaf(qv[d], ld<F32>(kb, off + d), s);
-    s *= sh.scale_log2;
-    const float mn = fmaxf(m, s);
-    const float al = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-    const float pp = exp2f(s - mn);
-    l = l * al + pp;
-#pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = fmaf(o[d], al, pp * ld<F32>(vb, off + d));
-    m = mn;
   };
-  // the window part I, I - dil, ... down to lo, and the sinks it does not hold
-  const int lo = max(0, I - sh.W + 1);
-  const int dil = sh.dil;
-  for (int j = 0; j < min(sh.n_sink, I + 1); ++j)
-    if (j < lo || (I - j) % dil != 0) visit(j);
-  for (int j = I; j >= lo; j -= dil) visit(j);
+  run(0, min(sh.n_sink, wlo) - 1);
+  run(wlo, I_last);
+  if (!active) return;
   const float inv = 1.f / l;
-  const long long ooff = ((r0 + t) * sh.Hq + h) * D;
+  const long long ooff = ((r0 + t) * sh.Hq + h) * D + part * DP;
 #pragma unroll
-  for (int d = 0; d < D; ++d) st<F32>(out, ooff + d, o[d] * inv);
-  if (lse) {
+  for (int d = 0; d < DP; ++d) st<F32>(out, ooff + d, o[d] * inv);
+  if (lse && part == 0) {
     const long long lo = vt.n ? (long long)h * vt.total + r0 + t : ((long long)b * sh.Hq + h) * C + t;
     lse[lo] = (m + log2f(l)) * 0.69314718055994531f;
   }
@@ -1073,7 +1111,7 @@ hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, 
                                   const void* k_rot, const void* v, const void* kc,
                                   const void* vc, const int32_t* start, int C, void* out,
                                   float* lse, const VarTab* vt, hipStream_t st) {
-  dim3 grid((C + 63) / 64, sh.Hq, sh.B);
+  dim3 grid((C + 3) / 4, sh.Hq, sh.B);   // 4 queries per work-group
   const VarTab none{};
   const VarTab& t = vt ? *vt : none;
   if (f32) {
