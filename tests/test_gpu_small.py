@@ -670,6 +670,66 @@ def test_decode_step_graph_replay():
         _ = (gpu.kc.float().sum() + 1).item()   # eager work between replays
 
 
+def test_first_chunk_and_mixed_step_graph_replay():
+    """A first chunk (one-pass rotation + cache write, then attention
+    without the cache) and a mixed step whose chunks form one equal-length run
+    (fixed-length kernels, decode with its fused write, the tail launch),
+    captured in one HIP graph: every replay, from restored caches, reproduces
+    the eager outputs, LSE and caches bit for bit."""
+    print("first chunk + mixed step graph replay", flush=True)
+    B, Hq, Hkv, D, W, S = 4, 8, 2, 128, 100, 2
+    gpu = GpuSide(B, Hq, Hkv, D, W, S)
+    C = 70
+    q0 = rnd((B, C, Hq, D), "q", 0, index=96).to(DEV)
+    k0 = rnd((B, C, Hkv, D), "k", 0, index=96).to(DEV)
+    v0 = rnd((B, C, Hkv, D), "v", 0, index=96).to(DEV)
+    st0 = torch.zeros(B, dtype=torch.int32, device=DEV)
+    lens = [1, 40, 40, 1]
+    T = sum(lens)
+    q1 = rnd((T, Hq, D), "chunk_q", 1, index=96).to(DEV)
+    k1 = rnd((T, Hkv, D), "chunk_k", 1, index=96).to(DEV)
+    v1 = rnd((T, Hkv, D), "chunk_v", 1, index=96).to(DEV)
+    st1 = torch.full((B,), C, dtype=torch.int32, device=DEV)
+    kr = torch.empty_like(k0)
+    o0 = torch.empty((B, C, Hq, D), dtype=torch.bfloat16, device=DEV)
+    l0 = torch.empty((B, Hq, C), dtype=torch.float32, device=DEV)
+    o1 = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=DEV)
+    l1 = torch.empty((Hq, T), dtype=torch.float32, device=DEV)
+    ws = torch.empty(swa.swa_step_varlen_workspace_bytes(gpu.p, lens), dtype=torch.uint8, device=DEV)
+    kc0, vc0 = gpu.kc.clone(), gpu.vc.clone()
+
+    def run():
+        swa.swa_rope_keys_cache_write(gpu.p, k0, v0, st0, gpu.kc, gpu.vc, kr)
+        swa.swa_prefill_attention(gpu.p, q0, kr, v0, None, None, st0, o0, l0)
+        swa.swa_step_varlen(gpu.p, q1, k1, v1, gpu.kc, gpu.vc, st1, lens, o1, l1, ws)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (o0, l0, o1, l1, gpu.kc, gpu.vc)]
+    gpu.kc.copy_(kc0)
+    gpu.vc.copy_(vc0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    names = ("out0", "lse0", "out1", "lse1", "k_cache", "v_cache")
+    for rep in range(3):
+        gpu.kc.copy_(kc0)
+        gpu.vc.copy_(vc0)
+        for t in (o0, l0, o1, l1):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((o0, l0, o1, l1, gpu.kc, gpu.vc), eager, names):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}: {name}"
+        _ = (gpu.kc.float().sum() + 1).item()   # eager work between replays
+
+
 def test_decode_long_window_wrap():
     """A 16384-slot buffer (the window of the 16K full-cache comparison)
     filled to its last slot and wrapping to slot 0, through both decode forms,
