@@ -602,9 +602,15 @@ def test_step_varlen(case):
     ref_o, ref_l = swa.swa_prefill_chunk_varlen(gpu.p, qd, kd, vd, gpu.kc, gpu.vc, st, lens)
     ref_k, ref_v = gpu.kc.clone(), gpu.vc.clone()
     swa.swa_cache_write_varlen(gpu.p, kd, vd, st, lens, ref_k, ref_v)
+    kc0, vc0 = gpu.kc.clone(), gpu.vc.clone()
     out, lse = swa.swa_step_varlen(gpu.p, qd, kd, vd, gpu.kc, gpu.vc, st, lens)
     assert torch.equal(gpu.kc.view(torch.uint8), ref_k.view(torch.uint8))
     assert torch.equal(gpu.vc.view(torch.uint8), ref_v.view(torch.uint8))
+    # without an LSE the step writes the same outputs and caches
+    out2, lse2 = swa.swa_step_varlen(gpu.p, qd, kd, vd, kc0, vc0, st, lens, want_lse=False)
+    assert lse2 is None and torch.equal(out2, out)
+    assert torch.equal(kc0.view(torch.uint8), ref_k.view(torch.uint8))
+    assert torch.equal(vc0.view(torch.uint8), ref_v.view(torch.uint8))
     atol, rrms, latol = tol(dtype)
     r = 0
     for b in range(B):
