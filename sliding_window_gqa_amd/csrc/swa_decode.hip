@@ -523,9 +523,11 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(Shape sh, const flo
 
 }  // namespace
 
-// Splits: about one round of work-groups (two per CU on 256 CUs; longer
-// ranges per work-group beat more, shorter ones: the per-work-group prologue,
-// merge and the combine pass cost more than the load imbalance), each range a
+// Splits: about one work-group per CU (256 CUs).  Longer ranges per
+// work-group beat more, shorter ones: the per-work-group prologue, the merge
+// and the combine pass cost more than the load imbalance (16 sequences with
+// 4096 slots stream at 5.17 TB/s with 2 splits against 5.05 with 4, 8
+// sequences take 31.9 us with 4 splits against 32.3 with 8).  Each range is a
 // multiple of the 128 slots one work-group step covers.
 // Keys a fast decode streams per (sequence, KV head): the slots, or with a
 // dilated window the sinks and ceil(W/dil) window keys.
@@ -539,10 +541,10 @@ int decode_splits_fast(const Shape& sh) { return decode_splits(key_shape(sh)); }
 
 int decode_splits(const Shape& sh) {
   const int units = sh.B * sh.Hkv;
-  int n = (512 + units - 1) / units;
+  int n = (256 + units - 1) / units;
   const int max_n = (sh.S + 4 * kChunk - 1) / (4 * kChunk);
   if (n > max_n) n = max_n;
-  if (n > kMaxSplits) n = kMaxSplits;   // (the combine's LDS; 512 / units never exceeds it)
+  if (n > kMaxSplits) n = kMaxSplits;   // (the combine's LDS; 256 / units never exceeds it)
   if (n < 1) n = 1;
   return n;
 }
