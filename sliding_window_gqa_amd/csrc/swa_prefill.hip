@@ -185,7 +185,13 @@ struct PrefillArgs {
 // a window of ceil(W/dil) of them.  An item is then (sequence, KV head,
 // residue, query tile); the band logic runs on a residue's decimated indices,
 // RoPE and the cache slots on absolute positions.
-template <bool VAR, bool DIL>
+//
+// NC (fixed length, no cache, no sinks: a first chunk, a whole prompt): every
+// tile is a band tile of the chunk, and the sink and slot logic drops out.
+// The instantiation exists for its register allocation: with the scalar
+// registers over-subscribed, the code without that logic places fewer of
+// its spills in the tile loop (1-1.5% on the 8192-token layer).
+template <bool VAR, bool DIL, bool NC>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
@@ -201,7 +207,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   const int C = a.C;
   const int W = sh.W;
   const int S = sh.S;
-  const int nsink = sh.n_sink;
+  const int nsink = NC ? 0 : sh.n_sink;
   const unsigned rowbytes = (unsigned)sh.Hkv * 2u * HD;   // bytes between tokens of K/V
   const unsigned qrowbytes = (unsigned)sh.Hq * 2u * HD;   // bytes between tokens of Q
   // DIL: the dilation, the window in a residue's rows, and the bytes between
@@ -404,7 +410,12 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         // less n_sink, when all its rows lie past the sinks; consecutive
         // cache tiles of an item are 32 slots apart
         const int P0 = (DIL ? l_a0 : l_s0) + dil * (u0 + 4 * w);
-        if (P0 >= nsink) {
+        if (NC) {
+          // (no row precedes the chunk without a cache: a tile before it would
+          // take the straight path on a descriptor with no records, zeros)
+          reg = 1;
+          srow = (u0 + W) * (int)rowbytes;
+        } else if (P0 >= nsink) {
           l_cm = l_cmn >= 0 ? l_cmn : (int)((unsigned)(P0 - nsink) % (unsigned)W);
           const int nx = l_cm + BN * dil >= W ? l_cm + BN * dil - W : l_cm + BN * dil;
           l_cmn = nx < W ? nx : -1;
@@ -1099,11 +1110,13 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   const long long ncu = (long long)(device_cu_count() & ~7);
   const long long nwg = (ncu >= 8 && n_items > ncu) ? ncu : n_items;
   if (vt)
-    prefill_bf16_d128_g4_kernel<true, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+    prefill_bf16_d128_g4_kernel<true, false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   else if (dil)
-    prefill_bf16_d128_g4_kernel<false, true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+    prefill_bf16_d128_g4_kernel<false, true, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+  else if (a.kc == nullptr && sh.n_sink == 0)
+    prefill_bf16_d128_g4_kernel<false, false, true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   else
-    prefill_bf16_d128_g4_kernel<false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+    prefill_bf16_d128_g4_kernel<false, false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   return hipGetLastError();
 }
 
