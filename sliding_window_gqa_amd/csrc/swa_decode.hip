@@ -26,9 +26,11 @@
 //  * Each lane loads 8 V rows (16 bytes at one head-dim offset; whole rows
 //    per instruction) and transposes them in registers into the A operand of
 //    O^T += V^T P^T.  The score accumulator is the B operand.
-//  * The 4 waves of a work-group interleave over the range and merge through
+//  * The NW (4 or 8) waves of a work-group interleave over the range and merge through
 //    LDS, so one partial per (sequence, query head, range) reaches memory.
 #include <math.h>
+
+#include <atomic>
 
 #include "swa_device.hpp"
 #include "swa_launch.hpp"
@@ -115,11 +117,13 @@ __device__ inline void ddma2(__amdgpu_buffer_rsrc_t r0, int o0, unsigned l0,
 // DIL: dilated window.  The work-groups then cut the sequence's keys, not
 // its slots, into ranges: key v < n_sink is sink slot v, key n_sink + k the
 // position p - k*dil (slot n_sink + (p - k*dil - n_sink) mod W).
-template <bool DIL>
-__global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[4 * 2 * DTILE];   // [wave][buffer] K
-  __shared__ float sm_m[4][4], sm_l[4][4];
-  __shared__ float sm_o[4][4][HD];
+//
+// NW: waves per work-group (4 or 8), two waves per SIMD either way.
+template <bool DIL, int NW>
+__global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[NW * 2 * DTILE];   // [wave][buffer] K
+  __shared__ float sm_m[NW][4], sm_l[NW][4];
+  __shared__ float sm_o[NW][4][HD];
   __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
@@ -348,7 +352,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
   // younger loads (V(m+1), K(m+1)) are outstanding; the compiler's own wait
   // for V(m) (8 younger register loads in its count) leaves K(m+1) in flight.
   {
-    const int cstep = 4 * kChunk;
+    const int cstep = NW * kChunk;
     int c0 = sp0 + kChunk * w;
     u32x4 vA[8], vB[8];
     if (c0 < vend) {
@@ -377,7 +381,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  // ---- merge the 4 waves through LDS ----
+  // ---- merge the NW waves through LDS ----
   const float lt = xg_sum(l_run);
   if (i < 4) {
     if (g == 0) {
@@ -391,14 +395,14 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_d128_g4_kernel(DecodeArgs 
       for (int r = 0; r < 4; ++r) sm_o[w][i][8 * (4 * g + r) + db] = o[db][r];
   }
   __syncthreads();
-  for (int idx = tid; idx < 4 * HD; idx += 256) {
+  for (int idx = tid; idx < 4 * HD; idx += 64 * NW) {
     const int hh = idx / HD, d = idx - hh * HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][hh]);
     float Lsum = 0.f, O = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float mw = sm_m[ww][hh];
       const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
       Lsum += sm_l[ww][hh] * f;
@@ -555,6 +559,29 @@ static int split_len_of(const Shape& sh, int n_splits) {
   return len;
 }
 
+// Waves per work-group of the fast kernel (no dilation): 8 when the grid
+// holds at most one work-group per CU and each range gives all 8 waves
+// slots, else 4.  With one work-group per CU the 8-wave form keeps twice the
+// loads in flight per CU: 16 sequences x 8 KV heads x 2 ranges stream at
+// 5.19 against 5.14 TB/s, 8 sequences x 4 ranges take 31.2 against 31.8 us;
+// with two or more work-groups per CU (64 sequences) 4 waves are faster.
+static int cu_count() {   // of the current device, 0 if unknown; cached per device
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static int decode_waves(const Shape& sh, int n_splits) {
+  if (sh.dil > 1) return 4;
+  const long long wgs = (long long)sh.B * sh.Hkv * n_splits;
+  const int cus = cu_count();
+  return (cus > 0 && wgs <= cus && split_len_of(key_shape(sh), n_splits) >= 8 * kChunk) ? 8 : 4;
+}
+
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                       const void* kc, const void* vc, const int32_t* pos,
                                       float* partial, int n_splits, void* out, float* lse,
@@ -579,10 +606,14 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
     a.map = *map;
   else
     a.map = DecodeMap{};
+  const int nw = decode_waves(sh, n_splits);
+  const dim3 grid(n_splits, sh.Hkv, sh.B);
   if (sh.dil > 1)
-    decode_bf16_d128_g4_kernel<true><<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
+    decode_bf16_d128_g4_kernel<true, 4><<<grid, dim3(256), 0, st>>>(a);
+  else if (nw == 8)
+    decode_bf16_d128_g4_kernel<false, 8><<<grid, dim3(512), 0, st>>>(a);
   else
-    decode_bf16_d128_g4_kernel<false><<<dim3(n_splits, sh.Hkv, sh.B), dim3(256), 0, st>>>(a);
+    decode_bf16_d128_g4_kernel<false, 4><<<grid, dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
