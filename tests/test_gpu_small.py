@@ -358,6 +358,9 @@ DECODE_CASES = [
     (3, 4, 2, 64, 100, 0, torch.bfloat16),   # generic path
     (2, 4, 1, 64, 100, 2, torch.float32),    # generic path
     (2, 8, 2, 128, 64, 100, torch.bfloat16),  # a global prefix longer than the window
+    # 16 (sequence, KV head) units x 16 ranges of 384 slots: at most one
+    # work-group per CU, so the fast kernel runs 8 waves per work-group
+    (2, 32, 8, 128, 4096, 2, torch.bfloat16),
 ]
 
 
