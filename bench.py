@@ -760,40 +760,49 @@ def chunked_vs_full(swa, synth, torch, dev):
 
     def chunked2():
         # the first chunk reads no cache: its rotation and cache write are one
-        # pass before its attention; the others read the cache before writing it
+        # pass before its attention; the others read the cache before writing
+        # it.  The chunks are W tokens long from position 0, so every start is
+        # a multiple of W and the aligned entry reads the cache in slot order.
         swa.swa_rope_keys_cache_write(p, ks_[0], vs_[0], starts[0], kc, vc, kr0)
         swa.swa_prefill_attention(p, qs[0], kr0, vs_[0], None, None, starts[0], outc, lsec)
         for c in range(1, N // C):
-            swa.swa_prefill_chunk(p, qs[c], ks_[c], vs_[c], kc, vc, starts[c], outc, lsec, ws)
+            swa.swa_prefill_chunk_aligned(p, qs[c], ks_[c], vs_[c], kc, vc, starts[c], outc, lsec, ws)
             swa.swa_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc)
 
     def chunked_parts(reps=5):
-        # the same loop as two calls per part (key rotation, attention, cache
-        # write), events around each launch: where the loop's time goes
+        # the same loop with events around each call: where the loop's time
+        # goes.  Chunks 1.. run the aligned entry (rotation + attention in one
+        # call); their attention is that call less the rotation pass, timed
+        # on its own (swa_rope_keys) in the same turn.
         kr = torch.empty_like(ks_[0])
         acc = {"key_rotation": 0.0, "attention": [0.0] * (N // C), "cache_write": 0.0}
         for _ in range(reps):
             evs = []
             for c in range(N // C):
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
                 e[0].record()
                 if c == 0:
                     swa.swa_rope_keys_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc, kr)
                 else:
                     swa.swa_rope_keys(p, ks_[c], starts[c], kr)
                 e[1].record()
-                swa.swa_prefill_attention(p, qs[c], kr, vs_[c], kc if c else None, vc if c else None,
-                                          starts[c], outc, lsec)
+                if c == 0:
+                    swa.swa_prefill_attention(p, qs[c], kr, vs_[c], None, None, starts[c], outc, lsec)
                 e[2].record()
                 if c > 0:
-                    swa.swa_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc)
+                    swa.swa_prefill_chunk_aligned(p, qs[c], ks_[c], vs_[c], kc, vc, starts[c], outc, lsec, ws)
                 e[3].record()
+                if c > 0:
+                    swa.swa_cache_write(p, ks_[c], vs_[c], starts[c], kc, vc)
+                e[4].record()
                 evs.append(e)
             torch.cuda.synchronize()
             for c, e in enumerate(evs):
-                acc["key_rotation"] += e[0].elapsed_time(e[1]) / reps
-                acc["attention"][c] += e[1].elapsed_time(e[2]) / reps
-                acc["cache_write"] += e[2].elapsed_time(e[3]) / reps
+                rot = e[0].elapsed_time(e[1])
+                acc["key_rotation"] += rot / reps
+                att = e[1].elapsed_time(e[2]) if c == 0 else e[2].elapsed_time(e[3]) - rot
+                acc["attention"][c] += att / reps
+                acc["cache_write"] += e[3].elapsed_time(e[4]) / reps
         return acc
 
     pf = swa.make_params(1, Hq, Hkv, D, N, 0, 0.0, wl.rope_theta, bf)
@@ -815,14 +824,16 @@ def chunked_vs_full(swa, synth, torch, dev):
         "chunked_swa_prefill": {"workload": wl.name, "ms": round(swa_ms, 4),
                                 "tflops": round(swa_flops / (swa_ms * 1e-3) / 1e12, 1),
                                 "step": "rope_keys_cache_write + prefill_attention (chunk 0), then 3 x "
-                                        "(prefill_chunk + cache_write)",
+                                        "(prefill_chunk_aligned + cache_write): chunks of W tokens from "
+                                        "position 0, every start a multiple of W",
                                 "attention_ms_per_chunk": [round(x, 4) for x in parts["attention"]],
                                 "attention_tflops": round(swa_flops / (attn_ms * 1e-3) / 1e12, 1),
                                 "key_rotation_ms_total": round(parts["key_rotation"], 4),
                                 "key_rotation_note": "chunk 0's entry is its fused rotation + cache write",
                                 "cache_write_ms_total": round(parts["cache_write"], 4),
-                                "breakdown_note": "events around each launch of the same loop run as separate "
-                                                  "calls (launch included)"},
+                                "breakdown_note": "events around each call of the same loop (launch included); "
+                                                  "chunks 1..3: attention = prefill_chunk_aligned less the "
+                                                  "rotation pass timed alone"},
         "full_causal_prefill": {"seq_len": N, "ms": round(full_ms, 4),
                                 "tflops": round(full_flops / (full_ms * 1e-3) / 1e12, 1)},
         "full_over_swa_time": round(full_ms / swa_ms, 3),

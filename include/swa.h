@@ -152,6 +152,27 @@ int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, co
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * swa_prefill_chunk_aligned — swa_prefill_chunk for chunks that start at
+ * multiples of the window, the pages' own chunking: digest summary
+ * "Pre-fill + Chunking" and explainer How It Works 4 cut a prompt into
+ * chunks of W tokens, so from position 0 chunk c starts at c*W (essay §4.1:
+ * the window size as the chunk size).  The rolling buffer then holds
+ * positions start - W .. start - 1 in slot order and the attention reads it
+ * as one run of rows.  Arguments, layouts, workspace and results as
+ * swa_prefill_chunk, and byte-identical to it.
+ *   start_pos : device int32[batch]; every start_pos[b] must be a multiple of
+ *               window.  The host cannot see the positions, so the device
+ *               checks: a sequence whose start is not a multiple gets NaN in
+ *               every out row and lse entry.
+ * With sinks, dilation, or a shape off the fast kernel (bf16, head_dim 128,
+ * 4 query heads per KV head) it runs swa_prefill_chunk (any start).
+ */
+int swa_prefill_chunk_aligned(const swa_params* params, const void* q, const void* k, const void* v,
+                              const void* k_cache, const void* v_cache, const int32_t* start_pos,
+                              int32_t chunk_len, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * swa_rope_keys — the key-rotation pass of swa_prefill_chunk on its own:
  * k_rot[b][t] = RoPE(k[b][t], start_pos[b] + t) (digest "Methods": RoPE,
  * theta from the architecture table), same layout as k.  With rope_theta == 0

@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "SwaError", "swa_params", "make_params", "library", "LIB_PATH",
-    "swa_cache_write", "swa_prefill_chunk", "swa_prefill_workspace_bytes",
+    "swa_cache_write", "swa_prefill_chunk", "swa_prefill_chunk_aligned", "swa_prefill_workspace_bytes",
     "swa_decode", "swa_decode_step", "swa_decode_workspace_bytes", "swa_status_string",
     "swa_rope_keys", "swa_prefill_attention", "swa_rope_keys_cache_write",
     "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen", "swa_prefill_attention_varlen",
@@ -61,6 +61,7 @@ _SIGNATURES = {
     "swa_cache_write": (ctypes.c_int, [_P, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "swa_prefill_workspace_bytes": (_sz, [_P, _i32]),
     "swa_prefill_chunk": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "swa_prefill_chunk_aligned": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "swa_rope_keys": (ctypes.c_int, [_P, _vp, _vp, _i32, _vp, _vp]),
     "swa_rope_keys_cache_write": (ctypes.c_int, [_P, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "swa_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
@@ -185,7 +186,7 @@ def _workspace(nbytes, device, workspace):
 
 
 def swa_prefill_chunk(params, q, k, v, k_cache, v_cache, start_pos, out=None, lse=None,
-                      workspace=None, want_lse=True, stream=None):
+                      workspace=None, want_lse=True, stream=None, _entry="swa_prefill_chunk"):
     """Attention of one prefill chunk; returns (out, lse).  Does not write the
     cache (call swa_cache_write afterwards)."""
     torch = _torch()
@@ -200,15 +201,24 @@ def swa_prefill_chunk(params, q, k, v, k_cache, v_cache, start_pos, out=None, ls
         lse = torch.empty((params.batch, params.n_q_heads, C), dtype=torch.float32, device=q.device)
     need = swa_prefill_workspace_bytes(params, C)
     workspace = _workspace(need, q.device, workspace)
-    st = library().swa_prefill_chunk(
+    st = getattr(library(), _entry)(
         ctypes.byref(params), _ptr(q, "q", dt, qshp), _ptr(k, "k", dt, kshp), _ptr(v, "v", dt, kshp),
         _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp),
         _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), C,
         _ptr(out, "out", dt, qshp),
         _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads, C)),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "swa_prefill_chunk")
+    _check(st, _entry)
     return out, lse
+
+
+def swa_prefill_chunk_aligned(params, q, k, v, k_cache, v_cache, start_pos, out=None, lse=None,
+                              workspace=None, want_lse=True, stream=None):
+    """swa_prefill_chunk for chunks whose starts are all multiples of the
+    window (a prompt cut into chunks of W tokens); a sequence whose start is
+    not gets NaN outputs.  Same arguments and results as swa_prefill_chunk."""
+    return swa_prefill_chunk(params, q, k, v, k_cache, v_cache, start_pos, out, lse, workspace,
+                             want_lse, stream, _entry="swa_prefill_chunk_aligned")
 
 
 def swa_rope_keys(params, k, start_pos, k_rot=None, stream=None):

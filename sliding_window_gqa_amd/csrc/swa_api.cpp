@@ -313,6 +313,31 @@ int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, co
                                out, lse, stream);
 }
 
+int swa_prefill_chunk_aligned(const swa_params* params, const void* q, const void* k, const void* v,
+                              const void* k_cache, const void* v_cache, const int32_t* start_pos,
+                              int32_t chunk_len, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  // sinks, dilation or a shape off the fast kernel: the general path serves any start
+  if (!fast_prefill(params, chunk_len) || sh.n_sink != 0 || sh.dil > 1)
+    return swa_prefill_chunk(params, q, k, v, k_cache, v_cache, start_pos, chunk_len, out, lse,
+                             workspace, workspace_bytes, stream);
+  if (!q || !k || !v || !start_pos || !out) return SWA_ERR_NULL;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return SWA_ERR_NULL;
+  if (chunk_len < 1 || chunk_len > (1 << 24)) return SWA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < swa_prefill_workspace_bytes(params, chunk_len))
+    return SWA_ERR_WORKSPACE;
+  const RopeTab rt = rope_table(params);
+  hipError_t e = swa::launch_cache_write(sh, rt, false, k, nullptr, start_pos, chunk_len, workspace,
+                                         nullptr, swa::kToDenseAligned, nullptr, stream);
+  if (e == hipSuccess)
+    e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, workspace, v, k_cache, v_cache, start_pos, chunk_len,
+                                         out, lse, nullptr, stream, true);
+  return launched(e);
+}
+
 size_t swa_decode_workspace_bytes(const swa_params* params) {
   Shape sh;
   if (check_params(params, &sh) != SWA_OK) return 0;

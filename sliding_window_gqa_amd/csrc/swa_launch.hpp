@@ -14,6 +14,8 @@ enum WriteMode {
   kToCache = 0,  // rolling-buffer slots of k_cache / v_cache (survivors only)
   kToDense = 1,  // rotated K into a dense [B][n_tok][Hkv][D] buffer (V untouched)
   kToBoth = 2,   // both at once: every rotated key dense, survivors (k, v) into the caches
+  kToDenseAligned = 3,   // kToDense for a chunk whose starts must be multiples of W: a
+                         // sequence whose start is not gets NaN keys (see swa_prefill_chunk_aligned)
 };
 
 // Sequences of different chunk lengths, packed one after the other (rows of
@@ -47,7 +49,10 @@ hipError_t launch_lse_pack(const float* src, float* dst, int B, int Hq, int C, l
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
-                                       float* lse, const VarTab* vt, hipStream_t st);
+                                       float* lse, const VarTab* vt, hipStream_t st,
+                                       bool aligned = false);
+// aligned: every start is a multiple of W (fixed length, no sinks), so the
+// rolling buffer holds positions start - W .. start - 1 in slot order.
 
 // Generic prefill (float32 or bf16, head_dim 64 or 128, any group size).
 hipError_t launch_prefill_generic(const Shape& sh, const RopeTab& rt, bool f32, const void* q,

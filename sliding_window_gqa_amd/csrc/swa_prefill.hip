@@ -186,11 +186,14 @@ struct PrefillArgs {
 // residue, query tile); the band logic runs on a residue's decimated indices,
 // RoPE and the cache slots on absolute positions.
 //
-// NC (fixed length, no cache, no sinks: a first chunk, a whole prompt): every
-// tile is a band tile of the chunk, and the sink and slot logic drops out.
-// The instantiation exists for its register allocation: with the scalar
-// registers over-subscribed, the code without that logic places fewer of
-// its spills in the tile loop (1-1.5% on the 8192-token layer).
+// NC (fixed length, no sinks, and either no cache -- a first chunk, a whole
+// prompt -- or a cache in slot order: every start a multiple of W, as when a
+// prompt is prefilled from position 0 in chunks of W tokens).  A tile before
+// the chunk then covers positions s0 + u0 .. s0 + u0 + 31 with u0 >= -W,
+// which sit in slots u0 + W .. u0 + W + 31, so the sink and slot logic drops
+// out.  With the scalar registers over-subscribed, the code without that
+// logic places fewer of its spills in the tile loop: 1-1.5% on the
+// 8192-token layer, 3-3.5% on a chunk that reads the cache.
 template <bool VAR, bool DIL, bool NC>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
@@ -411,8 +414,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
         // cache tiles of an item are 32 slots apart
         const int P0 = (DIL ? l_a0 : l_s0) + dil * (u0 + 4 * w);
         if (NC) {
-          // (no row precedes the chunk without a cache: a tile before it would
-          // take the straight path on a descriptor with no records, zeros)
+          // slot order: row u0 + W of the cache (without a cache no tile
+          // precedes the chunk)
           reg = 1;
           srow = (u0 + W) * (int)rowbytes;
         } else if (P0 >= nsink) {
@@ -1071,7 +1074,7 @@ static int device_cu_count() {
 hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,
                                        const void* k_rot, const void* v, const void* kc,
                                        const void* vc, const int32_t* start, int C, void* out,
-                                       float* lse, const VarTab* vt, hipStream_t st) {
+                                       float* lse, const VarTab* vt, hipStream_t st, bool aligned) {
   PrefillArgs a;
   a.sh = sh;
   a.rt = rt;
@@ -1113,7 +1116,7 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
     prefill_bf16_d128_g4_kernel<true, false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   else if (dil)
     prefill_bf16_d128_g4_kernel<false, true, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
-  else if (a.kc == nullptr && sh.n_sink == 0)
+  else if ((a.kc == nullptr || aligned) && sh.n_sink == 0)
     prefill_bf16_d128_g4_kernel<false, false, true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
   else
     prefill_bf16_d128_g4_kernel<false, false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);

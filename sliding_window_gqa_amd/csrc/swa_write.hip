@@ -62,6 +62,25 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
   const int t = t_lo + blk * tok_per_block + tb;
   if (tb >= tok_per_block || t >= len) return;
   const int s0 = start[b];
+  if (mode == kToDenseAligned) {
+    if (s0 % sh.W != 0) {
+      // the start breaks the caller's promise: NaN keys, so that every output
+      // of the sequence is NaN rather than silently wrong
+      const long long e0 = (srow + t) * cpt * 8;
+      for (int ct = (int)threadIdx.x - tb * cpt; ct < cpt; ct += (int)blockDim.x) {
+        if (F32) {
+          float4* d = reinterpret_cast<float4*>(static_cast<float*>(kdst) + e0 + 8 * ct);
+          const float qn = __builtin_nanf("");
+          d[0] = d[1] = make_float4(qn, qn, qn, qn);
+        } else {
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + e0 + 8 * ct) =
+              u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+        }
+      }
+      return;
+    }
+    mode = kToDense;
+  }
   rotate_store_token<F32>(sh, rt, k, v, b, srow, t, s0, s0 + len - 1, (int)threadIdx.x - tb * cpt,
                           (int)blockDim.x, kdst, vdst, mode, kcache);
 }

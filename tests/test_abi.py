@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported():
             "swa_prefill_attention_varlen", "swa_prefill_chunk_varlen",
             "swa_cache_write_varlen", "swa_step_varlen",
             "swa_step_varlen_workspace_bytes", "swa_decode_step_noalloc",
-            "swa_noalloc_scratch_bytes", "swa_rope_keys_cache_write"} <= set(names)
+            "swa_noalloc_scratch_bytes", "swa_rope_keys_cache_write",
+            "swa_prefill_chunk_aligned"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -68,6 +69,8 @@ def test_bad_params_rejected_everywhere(bad, code):
     bp = ctypes.byref(p)
     assert lib.swa_cache_write(bp, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == code
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == code
+    assert lib.swa_prefill_chunk_aligned(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30,
+                                         None) == code
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode_step_noalloc(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
@@ -89,6 +92,12 @@ def test_null_pointers_rejected():
     assert lib.swa_prefill_chunk(bp, None, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     # exactly one cache pointer given
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
+    for i in range(5):   # q, k, v, start_pos, out
+        args = [FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE]
+        args[[0, 1, 2, 5, 7][i]] = None
+        assert lib.swa_prefill_chunk_aligned(bp, *args, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL, i
+    assert lib.swa_prefill_chunk_aligned(bp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, None, FAKE, 1 << 30,
+                                         None) == swa.SWA_ERR_NULL
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     for i in range(7):   # q, k, v, k_cache, v_cache, pos, out
         args = [FAKE] * 7
@@ -114,6 +123,14 @@ def test_sizes_and_workspace_rejected():
     need = lib.swa_prefill_workspace_bytes(bp, 16)
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, need - 1, None) == swa.SWA_ERR_WORKSPACE
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None, need, None) == swa.SWA_ERR_WORKSPACE
+    for ap in (P(), P(n_sink=4)):   # the aligned path, and its fallback to swa_prefill_chunk (sinks)
+        b2 = ctypes.byref(ap)
+        assert lib.swa_prefill_chunk_aligned(b2, FAKE, FAKE, FAKE, None, None, FAKE, 0, FAKE, None, FAKE, 1 << 30,
+                                             None) == swa.SWA_ERR_SHAPE
+        assert lib.swa_prefill_chunk_aligned(b2, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, need - 1,
+                                             None) == swa.SWA_ERR_WORKSPACE
+        assert lib.swa_prefill_chunk_aligned(b2, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None, need,
+                                             None) == swa.SWA_ERR_WORKSPACE
     dneed = lib.swa_decode_workspace_bytes(bp)
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE
     assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE

@@ -69,13 +69,18 @@ def test_counts_chunked_n16384_and_full_causal():
     q, k, v = rand((1, N, Hq, D), g), rand((1, N, Hkv, D), g), rand((1, N, Hkv, D), g)
     kc = torch.zeros((1, W, Hkv, D), dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros_like(kc)
-    for c in range(N // C):
-        s = c * C
-        st = torch.tensor([s], dtype=torch.int32, device=DEV)
-        qc, kk, vv = (x[:, s:s + C].contiguous() for x in (q, k, v))
-        _, lse = swa.swa_prefill_chunk(p, qc, kk, vv, kc if c else None, vc if c else None, st)
-        swa.swa_cache_write(p, kk, vv, st, kc, vc)
-        check(lse, np.arange(s, s + C)[None], W, 0, f"chunk {c}")
+    # the chunks through swa_prefill_chunk, then again (fresh caches) through
+    # swa_prefill_chunk_aligned: chunks of W tokens from 0, starts multiples of W
+    for entry in (swa.swa_prefill_chunk, swa.swa_prefill_chunk_aligned):
+        kc.zero_()
+        vc.zero_()
+        for c in range(N // C):
+            s = c * C
+            st = torch.tensor([s], dtype=torch.int32, device=DEV)
+            qc, kk, vv = (x[:, s:s + C].contiguous() for x in (q, k, v))
+            _, lse = entry(p, qc, kk, vv, kc if c else None, vc if c else None, st)
+            swa.swa_cache_write(p, kk, vv, st, kc, vc)
+            check(lse, np.arange(s, s + C)[None], W, 0, f"{entry.__name__} chunk {c}")
     Wf = wl.extra["full_window"]
     pf = swa.make_params(1, Hq, Hkv, D, Wf, 0, TINY, wl.rope_theta)
     _, lse = swa.swa_prefill_chunk(pf, q, k, v, None, None, torch.zeros(1, dtype=torch.int32, device=DEV))

@@ -175,6 +175,73 @@ def test_prefill_chunks(case):
         t += C
 
 
+# (B, Hq, Hkv, D, W, chunk lengths): chunks of W (or 2W) tokens from position
+# 0, so every start is a multiple of W; a ragged last chunk
+ALIGNED_CASES = [
+    (2, 8, 2, 128, 256, [256, 256, 256, 100]),
+    (2, 8, 2, 128, 128, [256, 256, 77]),
+    (1, 32, 8, 128, 4096, [4096, 4096]),
+]
+
+
+@pytest.mark.parametrize("case", ALIGNED_CASES, ids=[f"B{c[0]}W{c[4]}" for c in ALIGNED_CASES])
+def test_prefill_chunk_aligned(case):
+    """swa_prefill_chunk_aligned (the rolling buffer read in slot order) against
+    swa_prefill_chunk chunk by chunk: out and LSE byte-identical, with the
+    caches written after each chunk; on the small shapes the oracle too.
+    Sequence 1 starts one window later than sequence 0 (both multiples of W).
+    The caches start as NaN, so a read of a slot not yet written shows."""
+    B, Hq, Hkv, D, W, chunks = case
+    print(f"prefill chunk aligned {case}", flush=True)
+    theta = 10000.0
+    gpu = GpuSide(B, Hq, Hkv, D, W, 0, theta)
+    small = W <= 256
+    orc = OracleSide(range(B), Hkv, D, W, 0, theta) if small else None
+    atol, rrms, latol = tol(torch.bfloat16)
+    offs = [W * b for b in range(B)]
+    t = 0
+    for ci, C in enumerate(chunks):
+        q, k, v = (rnd((B, C, h, D), n, 300 + ci).to(DEV) for h, n in ((Hq, "q"), (Hkv, "k"), (Hkv, "v")))
+        start = [offs[b] + t for b in range(B)]
+        st = torch.tensor(start, dtype=torch.int32, device=DEV)
+        kc = gpu.kc if gpu.has_cache else None
+        vc = gpu.vc if gpu.has_cache else None
+        oa, la = swa.swa_prefill_chunk_aligned(gpu.p, q, k, v, kc, vc, st)
+        og, lg = swa.swa_prefill_chunk(gpu.p, q, k, v, kc, vc, st)
+        torch.cuda.synchronize()
+        assert torch.equal(oa.view(torch.int16), og.view(torch.int16)), f"chunk {ci}: out differs"
+        assert torch.equal(la.view(torch.int32), lg.view(torch.int32)), f"chunk {ci}: lse differs"
+        if orc is not None:
+            ref = orc.prefill(q.cpu(), k.cpu(), v.cpu(), start)
+            for b in range(B):
+                assert_close(oa[b].cpu(), ref[b][0], atol, rrms, f"chunk {ci} seq {b} out")
+                assert_lse(la[b].cpu(), ref[b][1], latol, f"chunk {ci} seq {b} lse")
+            orc.write(k.cpu(), v.cpu(), start)
+        swa.swa_cache_write(gpu.p, k, v, st, gpu.kc, gpu.vc)
+        gpu.has_cache = True
+        t += C
+
+
+def test_prefill_chunk_aligned_rejects_a_misaligned_start():
+    """A start that is not a multiple of W breaks the entry point's promise:
+    that sequence's outputs are all NaN (checked on the device), the other
+    sequence's equal swa_prefill_chunk's."""
+    B, Hq, Hkv, D, W, C = 2, 8, 2, 128, 128, 100
+    print("prefill chunk aligned, misaligned start", flush=True)
+    gpu = GpuSide(B, Hq, Hkv, D, W, 0, 10000.0)
+    kh, vh = (rnd((B, W, Hkv, D), n, 77).to(DEV) for n in ("hist_k", "hist_v"))   # positions 0 .. W-1
+    swa.swa_cache_write(gpu.p, kh, vh, torch.zeros(B, dtype=torch.int32, device=DEV), gpu.kc, gpu.vc)
+    q, k, v = (rnd((B, C, h, D), n, 78).to(DEV) for h, n in ((Hq, "q"), (Hkv, "k"), (Hkv, "v")))
+    st = torch.tensor([W, W + 5], dtype=torch.int32, device=DEV)   # sequence 1: W + 5 is no multiple
+    oa, la = swa.swa_prefill_chunk_aligned(gpu.p, q, k, v, gpu.kc, gpu.vc, st)
+    og, lg = swa.swa_prefill_chunk(gpu.p, q, k, v, gpu.kc, gpu.vc, st)
+    torch.cuda.synchronize()
+    assert torch.equal(oa[0].view(torch.int16), og[0].view(torch.int16))
+    assert torch.equal(la[0].view(torch.int32), lg[0].view(torch.int32))
+    assert torch.isnan(oa[1].float()).all() and torch.isnan(la[1]).all()
+    assert not torch.isnan(og[1].float()).any()
+
+
 @pytest.mark.parametrize("D,S", [(128, 0), (128, 3), (64, 3)])
 def test_prefill_without_cache_at_nonzero_start(D, S):
     """No caches (k_cache = v_cache = NULL) with chunks that start past 0:
