@@ -180,6 +180,7 @@ def test_prefill_chunks(case):
 ALIGNED_CASES = [
     (2, 8, 2, 128, 256, [256, 256, 256, 100]),
     (2, 8, 2, 128, 128, [256, 256, 77]),
+    (2, 8, 2, 128, 100, [100, 100, 200, 37]),   # a window that is no multiple of the 32-key tile
     (1, 32, 8, 128, 4096, [4096, 4096]),
 ]
 
