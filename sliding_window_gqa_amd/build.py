@@ -68,7 +68,29 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_c_check(verbose)
     return LIB
+
+
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "swa_c_check.c")
+C_CHECK = os.path.join(ROOT, "tests", "c_abi", "swa_c_check")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile the plain-C caller of the ABI (tests/c_abi) with gcc against
+    include/swa.h and the freshly linked libswa.so; returns its path."""
+    rocm = os.path.dirname(os.path.dirname(_hipcc()))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.join(rocm, 'include')}", f"-I{os.path.join(ROOT, 'include')}", C_CHECK_SRC,
+           f"-L{PKG}", "-lswa", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../sliding_window_gqa_amd", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}",
+           "-o", C_CHECK]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {C_CHECK_SRC}:\n{r.stdout}\n{r.stderr}")
+    return C_CHECK
 
 
 if __name__ == "__main__":
