@@ -64,7 +64,15 @@ def test_workload3_chunked_prefill_and_full_causal():
     for c in range(N // C):
         s = c * C
         print(f"  chunk {c}", flush=True)
+        # the aligned entry (the loop the benchmark times: chunks of W from 0)
+        # on the caches as they stand, then the general one, which also writes
+        # the chunk into the caches: byte-identical
+        st = torch.tensor([s], dtype=torch.int32, device=DEV)
+        oa, la = swa.swa_prefill_chunk_aligned(gpu.p, *(x[:, s:s + C].to(DEV) for x in (q, k, v)),
+                                               gpu.kc if c else None, gpu.vc if c else None, st)
         out, lse = gpu.prefill(q[:, s:s + C], k[:, s:s + C], v[:, s:s + C], [s])
+        assert torch.equal(oa.view(torch.int16), out.view(torch.int16)), f"chunk {c}: aligned out differs"
+        assert torch.equal(la.view(torch.int32), lse.view(torch.int32)), f"chunk {c}: aligned lse differs"
         rows = sample_rows(C, 12, 30 + c, [0, 1, 2, 63, 64, 2047, 4094, 4095])
         ref = orc.prefill(q[:, s:s + C], k[:, s:s + C], v[:, s:s + C], [s], rows=rows)[0]
         check_rows(out[0].cpu(), lse[0].cpu(), ref, rows, torch.bfloat16, f"chunk {c}")
