@@ -346,7 +346,7 @@ def main():
                          "achieved": round(dec_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(dec_achieved / PEAK_HBM_GBPS, 4),
                          "traffic": profiled_traffic("decode_bf16_d128_g4_kernel.decode_b64_w4096",
-                                                     ["swa_decode.hip", "swa_device.hpp"]),
+                                                     ["swa_decode.hip", "swa_passes.hpp", "swa_device.hpp"]),
                          "algorithmic_bytes": round((dec_bytes + write_bytes) / T),
                          "avg_call_ms": round(dec_ms / T, 4),
                          "median_call_ms": round(dec_times[len(dec_times) // 2], 4),

@@ -102,6 +102,12 @@ __device__ inline void combine_column(const Shape& sh, const float* part, int n_
   const int r = map.n ? map.row[z] : z;   // the token's row in out
   const int D = sh.D;
   const float* src = part + ((long long)z * sh.Hq + h) * n_splits * (D + 2);
+  // up to 8 splits: the partial outputs go out with the maxima and sums,
+  // one wait for memory instead of two
+  float xp[8];
+  const bool few = n_splits <= 8;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) xp[u] = (few && u < n_splits) ? src[u * (D + 2) + d] : 0.f;
   for (int s = d; s < n_splits; s += D) {
     sm_m[s] = src[s * (D + 2) + D];
     sm_l[s] = src[s * (D + 2) + D + 1];
@@ -114,6 +120,12 @@ __device__ inline void combine_column(const Shape& sh, const float* part, int n_
   float L = 0.f, O = 0.f;
   for (int s = 0; s < n_splits; ++s) L += sm_l[s] * sm_f[s];
   int s = 0;
+  if (few) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < n_splits) O += xp[u] * sm_f[u];
+    s = n_splits;
+  }
   for (; s + 8 <= n_splits; s += 8) {
     float x[8];
 #pragma unroll
