@@ -527,12 +527,13 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(Shape sh, const flo
 
 }  // namespace
 
-// Splits: about one work-group per CU (256 CUs).  Longer ranges per
-// work-group beat more, shorter ones: the per-work-group prologue, the merge
-// and the combine pass cost more than the load imbalance (16 sequences with
-// 4096 slots stream at 5.17 TB/s with 2 splits against 5.05 with 4, 8
-// sequences take 31.9 us with 4 splits against 32.3 with 8).  Each range is a
-// multiple of the 128 slots one work-group step covers.
+// Splits: about one work-group per CU (256 CUs), each range at least 256
+// slots.  Longer ranges per work-group beat more, shorter ones: the
+// per-work-group prologue, the merge and the combine pass cost more than the
+// load imbalance (16 sequences with 4096 slots stream at 5.17 TB/s with 2
+// splits against 5.05 with 4, 8 sequences take 31.9 us with 4 splits against
+// 32.3 with 8, one sequence 11.25 us per step with 16 against 11.5 with 32).
+// Each range is a multiple of the 128 slots one work-group step covers.
 // Keys a fast decode streams per (sequence, KV head): the slots, or with a
 // dilated window the sinks and ceil(W/dil) window keys.
 static Shape key_shape(const Shape& sh) {
@@ -546,7 +547,7 @@ int decode_splits_fast(const Shape& sh) { return decode_splits(key_shape(sh)); }
 int decode_splits(const Shape& sh) {
   const int units = sh.B * sh.Hkv;
   int n = (256 + units - 1) / units;
-  const int max_n = (sh.S + 4 * kChunk - 1) / (4 * kChunk);
+  const int max_n = (sh.S + 8 * kChunk - 1) / (8 * kChunk);
   if (n > max_n) n = max_n;
   if (n > kMaxSplits) n = kMaxSplits;   // (the combine's LDS; 256 / units never exceeds it)
   if (n < 1) n = 1;
@@ -560,11 +561,13 @@ static int split_len_of(const Shape& sh, int n_splits) {
 }
 
 // Waves per work-group of the fast kernel (no dilation): 8 when the grid
-// holds at most one work-group per CU and each range gives all 8 waves
-// slots, else 4.  With one work-group per CU the 8-wave form keeps twice the
-// loads in flight per CU: 16 sequences x 8 KV heads x 2 ranges stream at
-// 5.19 against 5.14 TB/s, 8 sequences x 4 ranges take 31.2 against 31.8 us;
-// with two or more work-groups per CU (64 sequences) 4 waves are faster.
+// holds between a half and one work-group per CU and each range gives all 8
+// waves slots, else 4.  With one work-group per CU the 8-wave form keeps
+// twice the loads in flight per CU: 16 sequences x 8 KV heads x 2 ranges
+// stream at 5.19 against 5.14 TB/s, 8 sequences x 4 ranges take 31.2 against
+// 31.8 us; with two or more work-groups per CU (64 sequences) 4 waves are
+// faster, and so with half the CUs or fewer (one sequence x 16 ranges: 11.25
+// against 11.9 us per step).
 static int cu_count() {   // of the current device, 0 if unknown; cached per device
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -579,7 +582,7 @@ static int decode_waves(const Shape& sh, int n_splits) {
   if (sh.dil > 1) return 4;
   const long long wgs = (long long)sh.B * sh.Hkv * n_splits;
   const int cus = cu_count();
-  return (cus > 0 && wgs <= cus && split_len_of(key_shape(sh), n_splits) >= 8 * kChunk) ? 8 : 4;
+  return (cus > 0 && 2 * wgs > cus && wgs <= cus && split_len_of(key_shape(sh), n_splits) >= 8 * kChunk) ? 8 : 4;
 }
 
 hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const void* q,

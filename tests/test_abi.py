@@ -152,8 +152,8 @@ def test_workspace_sizes():
         per_split = B * 32 * (128 + 2) * 4
         assert nbytes % per_split == 0
         n_splits = nbytes // per_split
-        assert 1 <= n_splits <= -(-(W + S) // 128)
-        assert B * 8 * n_splits >= min(256, B * 8 * -(-(W + S) // 128))
+        assert 1 <= n_splits <= -(-(W + S) // 256)
+        assert B * 8 * n_splits >= min(256, B * 8 * -(-(W + S) // 256))
 
 
 def test_status_strings():
@@ -245,8 +245,8 @@ def test_step_varlen_workspace_over_several_decode_launches():
     lib = swa.library()
     p = P(batch=70)
 
-    def splits(b):   # about 256 work-groups, at most one per 128 slots
-        return max(1, min(-(-256 // (b * 8)), -(-4096 // 128)))
+    def splits(b):   # about 256 work-groups, ranges of at least 256 slots
+        return max(1, min(-(-256 // (b * 8)), -(-4096 // 256)))
 
     part = max(b * 32 * splits(b) * 130 * 4 for b in (64, 6))
     keys = -(-(70 * 8 * 128 * 2) // 256) * 256
