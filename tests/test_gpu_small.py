@@ -585,6 +585,9 @@ VARLEN_CASES = [
     (4, 8, 2, 128, 4096, 0, torch.bfloat16, [129, 129, 1, 1], [0, 5000, 70, 4095]),
     (70, 8, 2, 128, 64, 0, torch.bfloat16, [1] * 10 + [70] * 5 + [1] * 49 + [33] * 3 + [1] * 3,
      [int(x) for x in np.random.default_rng(8).integers(0, 200, 70)]),
+    # 16 one-token sequences x 8 KV heads x 2 ranges: the step's decode runs
+    # 8 waves per work-group (one per CU) through the sequence map
+    (17, 32, 8, 128, 4096, 0, torch.bfloat16, [1] * 16 + [100], [4100 + 61 * b for b in range(16)] + [4096]),
 ]
 
 
