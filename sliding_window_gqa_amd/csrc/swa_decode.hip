@@ -560,14 +560,6 @@ static int split_len_of(const Shape& sh, int n_splits) {
   return len;
 }
 
-// Waves per work-group of the fast kernel (no dilation): 8 when the grid
-// holds between a half and one work-group per CU and each range gives all 8
-// waves slots, else 4.  With one work-group per CU the 8-wave form keeps
-// twice the loads in flight per CU: 16 sequences x 8 KV heads x 2 ranges
-// stream at 5.19 against 5.14 TB/s, 8 sequences x 4 ranges take 31.2 against
-// 31.8 us; with two or more work-groups per CU (64 sequences) 4 waves are
-// faster, and so with half the CUs or fewer (one sequence x 16 ranges: 11.25
-// against 11.9 us per step).
 static int cu_count() {   // of the current device, 0 if unknown; cached per device
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -578,6 +570,14 @@ static int cu_count() {   // of the current device, 0 if unknown; cached per dev
   return n;
 }
 
+// Waves per work-group of the fast kernel (no dilation): 8 when the grid
+// holds between a half and one work-group per CU and each range gives all 8
+// waves slots, else 4.  With one work-group per CU the 8-wave form keeps
+// twice the loads in flight per CU: 16 sequences x 8 KV heads x 2 ranges
+// stream at 5.19 against 5.14 TB/s, 8 sequences x 4 ranges take 31.2 against
+// 31.8 us; with two or more work-groups per CU (64 sequences) 4 waves are
+// faster, and so with half the CUs or fewer (one sequence x 16 ranges: 11.25
+// against 11.9 us per step).
 static int decode_waves(const Shape& sh, int n_splits) {
   if (sh.dil > 1) return 4;
   const long long wgs = (long long)sh.B * sh.Hkv * n_splits;
