@@ -64,6 +64,17 @@ bool fast_path(const swa_params* p) {
          seq_cache_bytes < (1LL << 31);
 }
 
+// The fast decode kernel takes any group of 1, 2, 4 or 8 query heads per KV
+// head (a dilated window only with 4).
+bool fast_decode(const swa_params* p) {
+  const long long seq_cache_bytes =
+      (long long)(p->n_sink + p->window) * p->n_kv_heads * p->head_dim * 2;
+  const int g = p->n_kv_heads > 0 ? p->n_q_heads / p->n_kv_heads : 0;
+  const bool group = p->n_q_heads == g * p->n_kv_heads && (g == 1 || g == 2 || g == 4 || g == 8) &&
+                     (g == 4 || p->dilation <= 1);
+  return p->dtype == SWA_BF16 && p->head_dim == 128 && group && seq_cache_bytes < (1LL << 31);
+}
+
 // The fast prefill kernel also addresses one sequence's chunk (Q, K, V, and
 // a few tiles past its end) with 32-bit byte offsets.  A dilated window takes
 // it without sinks and in fixed-length batches (varlen: dilated = false).
@@ -128,7 +139,7 @@ T* rows_at(T* p, long long rows, long long row_elems, size_t es) {
 int decode_launch(const swa_params* params, const Shape& sh, const void* q, const void* k_cache,
                   const void* v_cache, const int32_t* pos, void* out, float* lse,
                   void* workspace, const swa::FusedWrite* fw, hipStream_t stream) {
-  const bool fast = fast_path(params);
+  const bool fast = fast_decode(params);
   const int n = fast ? swa::decode_splits_fast(sh) : swa::decode_splits(sh);
   const RopeTab rt = rope_table(params);
   const bool f32 = params->dtype == SWA_F32;
@@ -366,7 +377,7 @@ int swa_decode_step(const swa_params* params, const void* q, const void* k, cons
   if (!q || !k || !v || !k_cache || !v_cache || !pos || !out) return SWA_ERR_NULL;
   const size_t need = swa_decode_workspace_bytes(params);
   if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
-  if (fast_path(params)) {
+  if (fast_decode(params)) {
     const swa::FusedWrite fw{k, v, k_cache, v_cache};
     return decode_launch(params, sh, q, k_cache, v_cache, pos, out, lse, workspace, &fw, stream);
   }

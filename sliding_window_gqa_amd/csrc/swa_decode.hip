@@ -119,11 +119,15 @@ __device__ inline void ddma2(__amdgpu_buffer_rsrc_t r0, int o0, unsigned l0,
 // position p - k*dil (slot n_sink + (p - k*dil - n_sink) mod W).
 //
 // NW: waves per work-group (4 or 8), two waves per SIMD either way.
-template <bool DIL, int NW>
+// G: query heads per KV head (1, 2, 4 or 8; the kernel's name keeps the
+// group of 4 of the pages' model): the B operand's columns 0 .. G-1 are the
+// group's heads, so every K/V byte read serves all G of them.
+template <bool DIL, int NW, int G>
 __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeArgs a) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   __shared__ __attribute__((aligned(16))) uint8_t kvs[NW * 2 * DTILE];   // [wave][buffer] K
-  __shared__ float sm_m[NW][4], sm_l[NW][4];
-  __shared__ float sm_o[NW][4][HD];
+  __shared__ float sm_m[NW][G], sm_l[NW][G];
+  __shared__ float sm_o[NW][G][HD];
   __shared__ double rope_rev[kMaxPairs];
 
   const Shape& sh = a.sh;
@@ -156,14 +160,14 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
     const int x = sp_w - t;
     return nsink + (x < 0 ? x + W : x);
   };
-  const int h0 = kvh * 4;
+  const int h0 = kvh * G;
 
   const long long row_stride = (long long)sh.Hkv * HD;       // elements between slots
   const uint16_t* kbase = a.kc + ((long long)b * S * sh.Hkv + kvh) * HD;
   const uint16_t* vbase = a.vc + ((long long)b * S * sh.Hkv + kvh) * HD;
   const float c2 = sh.scale_log2;
 
-  // ---- Q: B operand, column i = query head h0+i (i < 4), rotated at p ----
+  // ---- Q: B operand, column i = query head h0+i (i < G), rotated at p ----
   if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
   __syncthreads();
 
@@ -209,10 +213,10 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
     u32x4 wq[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      wq[kk] = *reinterpret_cast<const u32x4*>(a.q + ((long long)r * sh.Hq + h0 + (i & 3)) * HD + 8 * (4 * kk + g));
+      wq[kk] = *reinterpret_cast<const u32x4*>(a.q + ((long long)r * sh.Hq + h0 + (i & (G - 1))) * HD + 8 * (4 * kk + g));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 wv = i < 4 ? wq[kk] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 wv = i < G ? wq[kk] : u32x4{0u, 0u, 0u, 0u};
       u32x4 r;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -383,7 +387,7 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
 
   // ---- merge the NW waves through LDS ----
   const float lt = xg_sum(l_run);
-  if (i < 4) {
+  if (i < G) {
     if (g == 0) {
       sm_m[w][i] = m_run;
       sm_l[w][i] = lt;
@@ -395,7 +399,7 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
       for (int r = 0; r < 4; ++r) sm_o[w][i][8 * (4 * g + r) + db] = o[db][r];
   }
   __syncthreads();
-  for (int idx = tid; idx < 4 * HD; idx += 64 * NW) {
+  for (int idx = tid; idx < G * HD; idx += 64 * NW) {
     const int hh = idx / HD, d = idx - hh * HD;
     float M = -INFINITY;
 #pragma unroll
@@ -579,7 +583,7 @@ static int cu_count() {   // of the current device, 0 if unknown; cached per dev
 // faster, and so with half the CUs or fewer (one sequence x 16 ranges: 11.25
 // against 11.9 us per step).
 static int decode_waves(const Shape& sh, int n_splits) {
-  if (sh.dil > 1) return 4;
+  if (sh.dil > 1 || sh.Hq != 4 * sh.Hkv) return 4;
   const long long wgs = (long long)sh.B * sh.Hkv * n_splits;
   const int cus = cu_count();
   return (cus > 0 && 2 * wgs > cus && wgs <= cus && split_len_of(key_shape(sh), n_splits) >= 8 * kChunk) ? 8 : 4;
@@ -610,13 +614,26 @@ hipError_t launch_decode_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const 
   else
     a.map = DecodeMap{};
   const int nw = decode_waves(sh, n_splits);
+  const int G = sh.Hq / sh.Hkv;
   const dim3 grid(n_splits, sh.Hkv, sh.B);
-  if (sh.dil > 1)
-    decode_bf16_d128_g4_kernel<true, 4><<<grid, dim3(256), 0, st>>>(a);
-  else if (nw == 8)
-    decode_bf16_d128_g4_kernel<false, 8><<<grid, dim3(512), 0, st>>>(a);
-  else
-    decode_bf16_d128_g4_kernel<false, 4><<<grid, dim3(256), 0, st>>>(a);
+  if (G == 4) {
+    if (sh.dil > 1)
+      decode_bf16_d128_g4_kernel<true, 4, 4><<<grid, dim3(256), 0, st>>>(a);
+    else if (nw == 8)
+      decode_bf16_d128_g4_kernel<false, 8, 4><<<grid, dim3(512), 0, st>>>(a);
+    else
+      decode_bf16_d128_g4_kernel<false, 4, 4><<<grid, dim3(256), 0, st>>>(a);
+  } else if (sh.dil > 1 || sh.Hq != G * sh.Hkv) {
+    return hipErrorInvalidValue;   // (the host sends these shapes to the generic kernel)
+  } else if (G == 1) {
+    decode_bf16_d128_g4_kernel<false, 4, 1><<<grid, dim3(256), 0, st>>>(a);
+  } else if (G == 2) {
+    decode_bf16_d128_g4_kernel<false, 4, 2><<<grid, dim3(256), 0, st>>>(a);
+  } else if (G == 8) {
+    decode_bf16_d128_g4_kernel<false, 4, 8><<<grid, dim3(256), 0, st>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

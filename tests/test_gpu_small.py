@@ -429,6 +429,11 @@ DECODE_CASES = [
     # 16 (sequence, KV head) units x 16 ranges of 384 slots: at most one
     # work-group per CU, so the fast kernel runs 8 waves per work-group
     (2, 32, 8, 128, 4096, 2, torch.bfloat16),
+    # other group sizes on the fast kernel: 1 (one query head per KV head),
+    # 2 with sinks, 8 over a full 4096-slot window
+    (3, 2, 2, 128, 100, 0, torch.bfloat16),
+    (2, 4, 2, 128, 300, 3, torch.bfloat16),
+    (2, 16, 2, 128, 4096, 0, torch.bfloat16),
 ]
 
 
