@@ -173,6 +173,32 @@ int swa_prefill_chunk_aligned(const swa_params* params, const void* q, const voi
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * swa_prefill_chunk_aligned_write_prev — one boundary of a chunked prompt:
+ * swa_cache_write of the previous chunk, then swa_prefill_chunk_aligned of
+ * the next, on the same stream, with results byte-identical to those two
+ * calls (essay §4.1 and explainer How It Works 4: each chunk attends to the
+ * cache that the chunks before it filled, then is written into it).  On the
+ * fast shape the previous chunk's write and the next chunk's key rotation
+ * run as one pass, a launch fewer per boundary.
+ *   k_prev, v_prev : [batch][prev_len][n_kv_heads][head_dim] raw keys and
+ *               values of the previous chunk, starting at start_prev[b]
+ *               (device int32[batch]); prev_len >= 1.
+ *   q, k, v, start_pos, chunk_len, out, lse, workspace : the next chunk, as
+ *               swa_prefill_chunk_aligned (every start a multiple of window;
+ *               NaN rows for a sequence whose start is not).
+ *   k_cache, v_cache : the caches, updated in place with the previous chunk
+ *               and then read by the next chunk's attention (not NULL).
+ * The workspace must not overlap k_prev, v_prev or the caches.  With sinks,
+ * dilation, or a shape off the fast kernel it makes the two calls.
+ */
+int swa_prefill_chunk_aligned_write_prev(const swa_params* params, const void* k_prev,
+                                         const void* v_prev, const int32_t* start_prev, int32_t prev_len,
+                                         const void* q, const void* k, const void* v, void* k_cache,
+                                         void* v_cache, const int32_t* start_pos, int32_t chunk_len,
+                                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
  * swa_rope_keys — the key-rotation pass of swa_prefill_chunk on its own:
  * k_rot[b][t] = RoPE(k[b][t], start_pos[b] + t) (digest "Methods": RoPE,
  * theta from the architecture table), same layout as k.  With rope_theta == 0

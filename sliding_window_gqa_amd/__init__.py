@@ -14,6 +14,7 @@ import os
 __all__ = [
     "SwaError", "swa_params", "make_params", "library", "LIB_PATH",
     "swa_cache_write", "swa_prefill_chunk", "swa_prefill_chunk_aligned", "swa_prefill_workspace_bytes",
+    "swa_prefill_chunk_aligned_write_prev",
     "swa_decode", "swa_decode_step", "swa_decode_workspace_bytes", "swa_status_string",
     "swa_rope_keys", "swa_prefill_attention", "swa_rope_keys_cache_write",
     "swa_prefill_varlen_workspace_bytes", "swa_rope_keys_varlen", "swa_prefill_attention_varlen",
@@ -62,6 +63,8 @@ _SIGNATURES = {
     "swa_prefill_workspace_bytes": (_sz, [_P, _i32]),
     "swa_prefill_chunk": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "swa_prefill_chunk_aligned": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "swa_prefill_chunk_aligned_write_prev": (ctypes.c_int, [_P, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                                            _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "swa_rope_keys": (ctypes.c_int, [_P, _vp, _vp, _i32, _vp, _vp]),
     "swa_rope_keys_cache_write": (ctypes.c_int, [_P, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "swa_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
@@ -219,6 +222,37 @@ def swa_prefill_chunk_aligned(params, q, k, v, k_cache, v_cache, start_pos, out=
     not gets NaN outputs.  Same arguments and results as swa_prefill_chunk."""
     return swa_prefill_chunk(params, q, k, v, k_cache, v_cache, start_pos, out, lse, workspace,
                              want_lse, stream, _entry="swa_prefill_chunk_aligned")
+
+
+def swa_prefill_chunk_aligned_write_prev(params, k_prev, v_prev, start_prev, q, k, v, k_cache, v_cache,
+                                         start_pos, out=None, lse=None, workspace=None, want_lse=True,
+                                         stream=None):
+    """swa_cache_write of the previous chunk (k_prev, v_prev from start_prev),
+    then swa_prefill_chunk_aligned of the next (q, k, v from start_pos), with
+    the write and the next chunk's key rotation in one pass; returns (out, lse)."""
+    torch = _torch()
+    dt = _dtype_of(params)
+    C, Cp = q.shape[1], k_prev.shape[1]
+    qshp = (params.batch, C, params.n_q_heads, params.head_dim)
+    kshp = (params.batch, C, params.n_kv_heads, params.head_dim)
+    pshp = (params.batch, Cp, params.n_kv_heads, params.head_dim)
+    cshp = (params.batch, params.n_sink + params.window, params.n_kv_heads, params.head_dim)
+    if out is None:
+        out = torch.empty(qshp, dtype=dt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((params.batch, params.n_q_heads, C), dtype=torch.float32, device=q.device)
+    workspace = _workspace(swa_prefill_workspace_bytes(params, C), q.device, workspace)
+    st = library().swa_prefill_chunk_aligned_write_prev(
+        ctypes.byref(params), _ptr(k_prev, "k_prev", dt, pshp), _ptr(v_prev, "v_prev", dt, pshp),
+        _ptr(start_prev, "start_prev", torch.int32, (params.batch,)), Cp,
+        _ptr(q, "q", dt, qshp), _ptr(k, "k", dt, kshp), _ptr(v, "v", dt, kshp),
+        _ptr(k_cache, "k_cache", dt, cshp), _ptr(v_cache, "v_cache", dt, cshp),
+        _ptr(start_pos, "start_pos", torch.int32, (params.batch,)), C,
+        _ptr(out, "out", dt, qshp),
+        _ptr(lse, "lse", torch.float32, (params.batch, params.n_q_heads, C)),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "swa_prefill_chunk_aligned_write_prev")
+    return out, lse
 
 
 def swa_rope_keys(params, k, start_pos, k_rot=None, stream=None):

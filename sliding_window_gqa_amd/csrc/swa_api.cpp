@@ -349,6 +349,48 @@ int swa_prefill_chunk_aligned(const swa_params* params, const void* q, const voi
   return launched(e);
 }
 
+int swa_prefill_chunk_aligned_write_prev(const swa_params* params, const void* k_prev,
+                                         const void* v_prev, const int32_t* start_prev, int32_t prev_len,
+                                         const void* q, const void* k, const void* v, void* k_cache,
+                                         void* v_cache, const int32_t* start_pos, int32_t chunk_len,
+                                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  Shape sh;
+  int st = check_params(params, &sh);
+  if (st != SWA_OK) return st;
+  if (!k_prev || !v_prev || !start_prev || !q || !k || !v || !k_cache || !v_cache || !start_pos || !out)
+    return SWA_ERR_NULL;
+  if (prev_len < 1 || chunk_len < 1 || chunk_len > (1 << 24)) return SWA_ERR_SHAPE;
+  if ((long long)sh.B * prev_len * sh.Hkv * (sh.D / 8) >= (1LL << 40)) return SWA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < swa_prefill_workspace_bytes(params, chunk_len))
+    return SWA_ERR_WORKSPACE;
+  // the general path: the two calls one after the other (every argument is
+  // checked above, so the write is never left without its chunk)
+  if (!fast_prefill(params, chunk_len) || sh.n_sink != 0 || sh.dil > 1) {
+    st = swa_cache_write(params, k_prev, v_prev, start_prev, prev_len, k_cache, v_cache, stream);
+    if (st != SWA_OK) return st;
+    return swa_prefill_chunk_aligned(params, q, k, v, k_cache, v_cache, start_pos, chunk_len, out, lse,
+                                     workspace, workspace_bytes, stream);
+  }
+  const RopeTab rt = rope_table(params);
+  swa::WriteRotate j{};
+  j.k_prev = k_prev;
+  j.v_prev = v_prev;
+  j.start_prev = start_prev;
+  j.n_prev = prev_len;
+  j.k_cache = k_cache;
+  j.v_cache = v_cache;
+  j.k = k;
+  j.start = start_pos;
+  j.n_tok = chunk_len;
+  j.k_rot = workspace;
+  hipError_t e = swa::launch_write_rotate(sh, rt, j, stream);
+  if (e == hipSuccess)
+    e = swa::launch_prefill_bf16_d128_g4(sh, rt, q, workspace, v, k_cache, v_cache, start_pos, chunk_len,
+                                         out, lse, nullptr, stream, true);
+  return launched(e);
+}
+
 size_t swa_decode_workspace_bytes(const swa_params* params) {
   Shape sh;
   if (check_params(params, &sh) != SWA_OK) return 0;

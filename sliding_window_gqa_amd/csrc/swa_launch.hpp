@@ -40,6 +40,26 @@ hipError_t launch_cache_write(const Shape& sh, const RopeTab& rt, bool f32, cons
                               void* vdst, WriteMode mode, const VarTab* vt, hipStream_t st,
                               void* kcache = nullptr);
 
+// kToCache of a previous chunk and kToDenseAligned of the next one in one
+// launch (bf16, fixed length, both chunks of the same B sequences): the
+// previous chunk's k_prev / v_prev [B][n_prev] from start_prev into the
+// caches, the next chunk's rotated k [B][n_tok] from start into k_rot.  The
+// launcher fills tpb, t_lo and nb_prev.
+struct WriteRotate {
+  const void* k_prev;
+  const void* v_prev;
+  const int32_t* start_prev;
+  int n_prev;
+  void* k_cache;
+  void* v_cache;
+  const void* k;
+  const int32_t* start;
+  int n_tok;
+  void* k_rot;
+  int tpb, t_lo, nb_prev;
+};
+hipError_t launch_write_rotate(const Shape& sh, const RopeTab& rt, WriteRotate j, hipStream_t st);
+
 // LSE of a fixed-length batch [B][Hq][C] into its columns of a packed
 // [Hq][total] array (dst = the batch's first column).
 hipError_t launch_lse_pack(const float* src, float* dst, int B, int Hq, int C, long long total,

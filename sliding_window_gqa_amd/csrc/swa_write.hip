@@ -33,6 +33,24 @@
 namespace swa {
 namespace {
 
+// Rotated keys of a token whose sequence started off a multiple of W in an
+// aligned chunk: NaN, so that every output of the sequence is NaN rather
+// than silently wrong.  Chunks ct0, ct0 + stride, .. of token row `row`.
+template <bool F32>
+__device__ inline void store_nan_keys(int cpt, long long row, int ct0, int stride, void* kdst) {
+  const long long e0 = row * cpt * 8;
+  for (int ct = ct0; ct < cpt; ct += stride) {
+    if (F32) {
+      float4* d = reinterpret_cast<float4*>(static_cast<float*>(kdst) + e0 + 8 * ct);
+      const float qn = __builtin_nanf("");
+      d[0] = d[1] = make_float4(qn, qn, qn, qn);
+    } else {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + e0 + 8 * ct) =
+          u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    }
+  }
+}
+
 template <bool F32, bool VAR>
 __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, const void* __restrict__ k,
                                                          const void* __restrict__ v,
@@ -63,26 +81,48 @@ __global__ void __launch_bounds__(256) cache_write_kernel(Shape sh, RopeTab rt, 
   if (tb >= tok_per_block || t >= len) return;
   const int s0 = start[b];
   if (mode == kToDenseAligned) {
-    if (s0 % sh.W != 0) {
-      // the start breaks the caller's promise: NaN keys, so that every output
-      // of the sequence is NaN rather than silently wrong
-      const long long e0 = (srow + t) * cpt * 8;
-      for (int ct = (int)threadIdx.x - tb * cpt; ct < cpt; ct += (int)blockDim.x) {
-        if (F32) {
-          float4* d = reinterpret_cast<float4*>(static_cast<float*>(kdst) + e0 + 8 * ct);
-          const float qn = __builtin_nanf("");
-          d[0] = d[1] = make_float4(qn, qn, qn, qn);
-        } else {
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(kdst) + e0 + 8 * ct) =
-              u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-        }
-      }
+    if (s0 % sh.W != 0) {   // the start breaks the caller's promise
+      store_nan_keys<F32>(cpt, srow + t, (int)threadIdx.x - tb * cpt, (int)blockDim.x, kdst);
       return;
     }
     mode = kToDense;
   }
   rotate_store_token<F32>(sh, rt, k, v, b, srow, t, s0, s0 + len - 1, (int)threadIdx.x - tb * cpt,
                           (int)blockDim.x, kdst, vdst, mode, kcache);
+}
+
+// A chunk boundary of an aligned chunked prefill in one launch (bf16, fixed
+// length): blocks [0, nb_prev) of grid row b store the previous chunk's
+// surviving tokens into sequence b's rolling buffer (kToCache), the others
+// rotate the next chunk's keys into the dense buffer (kToDenseAligned).  The
+// two jobs write disjoint memory and read only their own inputs, so the
+// result is that of the two passes one after the other.
+__global__ void __launch_bounds__(256) write_rotate_kernel(Shape sh, RopeTab rt, WriteRotate j) {
+  const int cpt = sh.Hkv * (sh.D / 8);
+  const int b = blockIdx.y;
+  const int tb = (int)threadIdx.x / cpt;
+  const int ct0 = (int)threadIdx.x - tb * cpt;
+  if (tb >= j.tpb) return;
+  int blk = blockIdx.x;
+  if (blk < j.nb_prev) {
+    const int t = j.t_lo + blk * j.tpb + tb;
+    if (t >= j.n_prev) return;
+    const int s0 = j.start_prev[b];
+    rotate_store_token<false>(sh, rt, j.k_prev, j.v_prev, b, (long long)b * j.n_prev, t, s0,
+                              s0 + j.n_prev - 1, ct0, (int)blockDim.x, j.k_cache, j.v_cache, kToCache,
+                              nullptr);
+    return;
+  }
+  blk -= j.nb_prev;
+  const int t = blk * j.tpb + tb;
+  if (t >= j.n_tok) return;
+  const int s0 = j.start[b];
+  if (s0 % sh.W != 0) {
+    store_nan_keys<false>(cpt, (long long)b * j.n_tok + t, ct0, (int)blockDim.x, j.k_rot);
+    return;
+  }
+  rotate_store_token<false>(sh, rt, j.k, nullptr, b, (long long)b * j.n_tok, t, s0, s0 + j.n_tok - 1, ct0,
+                            (int)blockDim.x, j.k_rot, nullptr, kToDense, nullptr);
 }
 
 // LSE rows of a fixed-length batch [B][Hq][C] into the columns of a packed
@@ -154,6 +194,20 @@ hipError_t launch_step_tail(StepTail t, hipStream_t st) {
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) return hipErrorInvalidValue;
   step_tail_kernel<<<dim3((unsigned)total), dim3(128), 0, st>>>(t);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_rotate(const Shape& sh, const RopeTab& rt, WriteRotate j, hipStream_t st) {
+  const int threads = 256;
+  const int cpt = sh.Hkv * (sh.D / 8);
+  j.tpb = cpt <= threads ? threads / cpt : 1;
+  // as launch_cache_write: only the previous chunk's last W tokens can survive it
+  j.t_lo = (sh.n_sink == 0 && j.n_prev > sh.W) ? j.n_prev - sh.W : 0;
+  const long long bp = ((long long)(j.n_prev - j.t_lo) + j.tpb - 1) / j.tpb;
+  const long long bn = ((long long)j.n_tok + j.tpb - 1) / j.tpb;
+  if (j.n_prev < 1 || j.n_tok < 1 || bp + bn > INT32_MAX || sh.B > 65535) return hipErrorInvalidValue;
+  j.nb_prev = (int)bp;
+  write_rotate_kernel<<<dim3((unsigned)(bp + bn), (unsigned)sh.B), dim3(threads), 0, st>>>(sh, rt, j);
   return hipGetLastError();
 }
 

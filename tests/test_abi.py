@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
             "swa_cache_write_varlen", "swa_step_varlen",
             "swa_step_varlen_workspace_bytes", "swa_decode_step_noalloc",
             "swa_noalloc_scratch_bytes", "swa_rope_keys_cache_write",
-            "swa_prefill_chunk_aligned"} <= set(names)
+            "swa_prefill_chunk_aligned", "swa_prefill_chunk_aligned_write_prev"} <= set(names)
     lib = ctypes.CDLL(swa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -71,6 +71,8 @@ def test_bad_params_rejected_everywhere(bad, code):
     assert lib.swa_prefill_chunk(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_prefill_chunk_aligned(bp, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, FAKE, 1 << 30,
                                          None) == code
+    assert lib.swa_prefill_chunk_aligned_write_prev(bp, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                    16, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == code
     assert lib.swa_decode_step_noalloc(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
@@ -98,6 +100,13 @@ def test_null_pointers_rejected():
         assert lib.swa_prefill_chunk_aligned(bp, *args, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL, i
     assert lib.swa_prefill_chunk_aligned(bp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, None, FAKE, 1 << 30,
                                          None) == swa.SWA_ERR_NULL
+    for ap in (P(), P(n_sink=4)):   # fused, and the two calls it makes with sinks
+        b2 = ctypes.byref(ap)
+        for i in range(10):   # k_prev, v_prev, start_prev, q, k, v, k_cache, v_cache, start_pos, out
+            args = [FAKE] * 10
+            args[i] = None
+            assert lib.swa_prefill_chunk_aligned_write_prev(b2, *args[:3], 16, *args[3:9], 16, args[9], None, FAKE,
+                                                            1 << 30, None) == swa.SWA_ERR_NULL, i
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == swa.SWA_ERR_NULL
     for i in range(7):   # q, k, v, k_cache, v_cache, pos, out
         args = [FAKE] * 7
@@ -131,6 +140,12 @@ def test_sizes_and_workspace_rejected():
                                              None) == swa.SWA_ERR_WORKSPACE
         assert lib.swa_prefill_chunk_aligned(b2, FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, None, None, need,
                                              None) == swa.SWA_ERR_WORKSPACE
+        wp = lib.swa_prefill_chunk_aligned_write_prev
+        for plen, clen, ws, w_need in ((0, 16, FAKE, need), (16, 0, FAKE, need), (16, 16, FAKE, need - 1),
+                                       (16, 16, None, need)):
+            code = swa.SWA_ERR_SHAPE if plen < 1 or clen < 1 else swa.SWA_ERR_WORKSPACE
+            assert wp(b2, FAKE, FAKE, FAKE, plen, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, clen, FAKE, None, ws, w_need,
+                      None) == code, (plen, clen)
     dneed = lib.swa_decode_workspace_bytes(bp)
     assert lib.swa_decode(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE
     assert lib.swa_decode_step(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dneed - 1, None) == swa.SWA_ERR_WORKSPACE

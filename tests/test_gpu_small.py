@@ -243,6 +243,71 @@ def test_prefill_chunk_aligned_rejects_a_misaligned_start():
     assert not torch.isnan(og[1].float()).any()
 
 
+WRITE_PREV_CASES = [(c, 0) for c in ALIGNED_CASES] + [((2, 8, 2, 128, 100, [100, 100, 37]), 3)]
+
+
+@pytest.mark.parametrize("case,S", WRITE_PREV_CASES, ids=[f"B{c[0]}W{c[4]}S{s}" for c, s in WRITE_PREV_CASES])
+def test_prefill_chunk_aligned_write_prev(case, S):
+    """swa_prefill_chunk_aligned_write_prev (the previous chunk's cache write
+    and the next chunk's prefill, the write and the key rotation in one pass)
+    against the two calls it replaces, chunk by chunk: out and LSE
+    byte-identical, and after the last chunk's own write both caches too.
+    With sinks (S = 3) it makes the two calls itself."""
+    B, Hq, Hkv, D, W, chunks = case
+    print(f"prefill chunk aligned write_prev {case} n_sink={S}", flush=True)
+    theta = 10000.0
+    one = GpuSide(B, Hq, Hkv, D, W, S, theta)    # the fused entry
+    two = GpuSide(B, Hq, Hkv, D, W, S, theta)    # cache write, then the aligned chunk
+    offs = [W * b if S == 0 else 0 for b in range(B)]   # with sinks every sequence starts at 0
+    t = 0
+    prev = None
+    for ci, C in enumerate(chunks):
+        q, k, v = (rnd((B, C, h, D), n, 400 + ci).to(DEV) for h, n in ((Hq, "q"), (Hkv, "k"), (Hkv, "v")))
+        st = torch.tensor([offs[b] + t for b in range(B)], dtype=torch.int32, device=DEV)
+        if prev is None:
+            o1, l1 = swa.swa_prefill_chunk_aligned(one.p, q, k, v, None, None, st)
+            o2, l2 = swa.swa_prefill_chunk_aligned(two.p, q, k, v, None, None, st)
+        else:
+            kp, vp, sp = prev
+            o1, l1 = swa.swa_prefill_chunk_aligned_write_prev(one.p, kp, vp, sp, q, k, v, one.kc, one.vc, st)
+            swa.swa_cache_write(two.p, kp, vp, sp, two.kc, two.vc)
+            o2, l2 = swa.swa_prefill_chunk_aligned(two.p, q, k, v, two.kc, two.vc, st)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"chunk {ci}: out differs"
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), f"chunk {ci}: lse differs"
+        assert not torch.isnan(o1.float()).any(), f"chunk {ci}: NaN (a slot read before it was written)"
+        prev = (k, v, st)
+        t += C
+    for g in (one, two):
+        swa.swa_cache_write(g.p, prev[0], prev[1], prev[2], g.kc, g.vc)
+    torch.cuda.synchronize()
+    assert torch.equal(one.kc.view(torch.int16), two.kc.view(torch.int16))
+    assert torch.equal(one.vc.view(torch.int16), two.vc.view(torch.int16))
+
+
+def test_prefill_chunk_aligned_write_prev_misaligned_start():
+    """The fused entry keeps the aligned promise's check: a sequence whose
+    next start is no multiple of W gets NaN outputs; the other sequence's
+    outputs and both caches equal the two separate calls'."""
+    B, Hq, Hkv, D, W, C = 2, 8, 2, 128, 128, 100
+    print("prefill chunk aligned write_prev, misaligned start", flush=True)
+    one = GpuSide(B, Hq, Hkv, D, W, 0, 10000.0)
+    two = GpuSide(B, Hq, Hkv, D, W, 0, 10000.0)
+    kp, vp = (rnd((B, W, Hkv, D), n, 79).to(DEV) for n in ("hist_k", "hist_v"))   # positions 0 .. W-1
+    sp = torch.zeros(B, dtype=torch.int32, device=DEV)
+    q, k, v = (rnd((B, C, h, D), n, 80).to(DEV) for h, n in ((Hq, "q"), (Hkv, "k"), (Hkv, "v")))
+    st = torch.tensor([W, W + 5], dtype=torch.int32, device=DEV)
+    o1, l1 = swa.swa_prefill_chunk_aligned_write_prev(one.p, kp, vp, sp, q, k, v, one.kc, one.vc, st)
+    swa.swa_cache_write(two.p, kp, vp, sp, two.kc, two.vc)
+    o2, l2 = swa.swa_prefill_chunk(two.p, q, k, v, two.kc, two.vc, st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0].view(torch.int16), o2[0].view(torch.int16))
+    assert torch.equal(l1[0].view(torch.int32), l2[0].view(torch.int32))
+    assert torch.isnan(o1[1].float()).all() and torch.isnan(l1[1]).all()
+    assert torch.equal(one.kc.view(torch.int16), two.kc.view(torch.int16))
+    assert torch.equal(one.vc.view(torch.int16), two.vc.view(torch.int16))
+
+
 @pytest.mark.parametrize("D,S", [(128, 0), (128, 3), (64, 3)])
 def test_prefill_without_cache_at_nonzero_start(D, S):
     """No caches (k_cache = v_cache = NULL) with chunks that start past 0:
