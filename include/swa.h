@@ -165,7 +165,8 @@ int swa_prefill_chunk(const swa_params* params, const void* q, const void* k, co
  *               checks: a sequence whose start is not a multiple gets NaN in
  *               every out row and lse entry.
  * With sinks, dilation, or a shape off the fast kernel (bf16, head_dim 128,
- * 4 query heads per KV head) it runs swa_prefill_chunk (any start).
+ * 1, 2, 4 or 8 query heads per KV head) it runs swa_prefill_chunk (any
+ * start).
  */
 int swa_prefill_chunk_aligned(const swa_params* params, const void* q, const void* k, const void* v,
                               const void* k_cache, const void* v_cache, const int32_t* start_pos,
@@ -278,7 +279,8 @@ int swa_cache_write_varlen(const swa_params* params, const void* k, const void* 
  * into the rolling buffers.  Same arguments and layouts as above; k_cache
  * and v_cache are read and written.  The result is that of
  * swa_prefill_chunk_varlen followed by swa_cache_write_varlen, up to
- * rounding: with bf16, head_dim 128 and 4 query heads per KV head, the
+ * rounding: with bf16, head_dim 128 and 1, 2, 4 or 8 query heads per KV
+ * head (no dilation), the
  * sequences of one token go to the decode kernel after the cache write
  * (the rest to the prefill kernel, before it), so that a decode token costs
  * a decode, not a 64-query prefill tile.

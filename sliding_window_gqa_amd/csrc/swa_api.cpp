@@ -56,17 +56,10 @@ RopeTab rope_table(const swa_params* p) {
   return rt;
 }
 
+// The fast kernels (bf16, head_dim 128) take a group of 1, 2, 4 or 8 query
+// heads per KV head, a dilated window only with 4, and address one
+// sequence's cache with 32-bit byte offsets.
 bool fast_path(const swa_params* p) {
-  // the fast kernels address one sequence's cache with 32-bit byte offsets
-  const long long seq_cache_bytes =
-      (long long)(p->n_sink + p->window) * p->n_kv_heads * p->head_dim * 2;
-  return p->dtype == SWA_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads &&
-         seq_cache_bytes < (1LL << 31);
-}
-
-// The fast decode kernel takes any group of 1, 2, 4 or 8 query heads per KV
-// head (a dilated window only with 4).
-bool fast_decode(const swa_params* p) {
   const long long seq_cache_bytes =
       (long long)(p->n_sink + p->window) * p->n_kv_heads * p->head_dim * 2;
   const int g = p->n_kv_heads > 0 ? p->n_q_heads / p->n_kv_heads : 0;
@@ -74,6 +67,7 @@ bool fast_decode(const swa_params* p) {
                      (g == 4 || p->dilation <= 1);
   return p->dtype == SWA_BF16 && p->head_dim == 128 && group && seq_cache_bytes < (1LL << 31);
 }
+bool fast_decode(const swa_params* p) { return fast_path(p); }
 
 // The fast prefill kernel also addresses one sequence's chunk (Q, K, V, and
 // a few tiles past its end) with 32-bit byte offsets.  A dilated window takes

@@ -8,7 +8,8 @@
 // max and sum (the FlashAttention-2 style block processing the digest page
 // names as the basis of the SWA kernel, "Insights"/"핵심 주장").
 //
-// Fast kernel (bf16, head_dim 128, GQA group 4), MI355X / gfx950:
+// Fast kernel (bf16, head_dim 128; written for the GQA group of 4, and
+// taking groups of 1, 2 and 8 as described at the kernel), MI355X / gfx950:
 //  * One work-group = 64 query positions x the 4 query heads of one KV head
 //    (256 query rows), 8 waves, two per SIMD.  Wave w owns positions
 //    t0+16(w&3) .. +15 for 2 of the 4 heads (32 query columns), so every K or
@@ -194,9 +195,20 @@ struct PrefillArgs {
 // out.  With the scalar registers over-subscribed, the code without that
 // logic places fewer of its spills in the tile loop: 1-1.5% on the
 // 8192-token layer, 3-3.5% on a chunk that reads the cache.
-template <bool VAR, bool DIL, bool NC>
+//
+// GQ, the query heads per KV head (1, 2, 4 or 8; DIL takes 4 only): an item
+// always holds 4 query heads.  With 8, a KV head has two items per query tile
+// (virtual heads 2 kvh and 2 kvh + 1, query heads 8 kvh .. +3 and +4 .. +7),
+// which read the same K/V rows.  With 1 or 2, the item's 4 heads are the
+// group's heads repeated (head h of the item loads query head h mod GQ), and
+// only the first GQ are stored: 4 / GQ times the matrix work of the group.
+template <bool VAR, bool DIL, bool NC, int GQ>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
+  static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group of 1, 2, 4 or 8 query heads");
+  static_assert(GQ == 4 || !DIL, "a dilated window takes groups of 4");
+  constexpr int GH = GQ < 4 ? GQ : 4;    // distinct query heads of an item
+  constexpr int VS = GQ == 8 ? 1 : 0;    // items per (KV head, query tile): 1 << VS
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
   __shared__ __attribute__((aligned(16))) uint8_t qstage[BM * QROWB];
   __shared__ double rope_rev[kMaxPairs];
@@ -298,7 +310,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       it.abs0 = sabs + r0;
       it.s0 = (sabs + r0 - rho) / dil;
     } else {
-      const int per_b = sh.Hkv * a.n_qtiles;
+      const int per_b = (sh.Hkv << VS) * a.n_qtiles;   // items of a query tile: (virtual) heads
       it.b = L / per_b;
       const int rem = L - it.b * per_b;
       it.kvh = rem / a.n_qtiles;
@@ -334,7 +346,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       (unsigned)reinterpret_cast<uintptr_t>((lds_u8*)qstage));
   const int nrec_c = (C - 1) * (int)rowbytes + HD * 2;
   const int nrec_s = a.kc ? (S - 1) * (int)rowbytes + HD * 2 : 0;
-  const int nrec_q = (C - 1) * (int)qrowbytes + QROWB;
+  const int nrec_q = (C - 1) * (int)qrowbytes + GH * ROWB;   // (the item's heads of the last row)
 
   // Cursor of the load stream: the item of round lr_round, its tile lt
   // (tiles past an item's end, once no item follows, load unused rows), and
@@ -379,8 +391,9 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     l_u0 = it.t0 + BN * (it.kmin - it.n_stile);
     l_s0 = it.s0;
     if (DIL) l_a0 = it.abs0;
-    l_ec = (VAR || DIL) ? ((long long)it.row0 * sh.Hkv + it.kvh) * HD : ((long long)it.b * C * sh.Hkv + it.kvh) * HD;
-    l_es = ((long long)it.b * S * sh.Hkv + it.kvh) * HD;
+    const int kvh_ = it.kvh >> VS;   // the item's KV head
+    l_ec = (VAR || DIL) ? ((long long)it.row0 * sh.Hkv + kvh_) * HD : ((long long)it.b * C * sh.Hkv + kvh_) * HD;
+    l_es = ((long long)it.b * S * sh.Hkv + kvh_) * HD;
     l_nrec = (VAR || DIL) ? (it.len - 1) * (int)rbd + HD * 2 : nrec_c;
     l_reg = -1;
     l_cmn = -1;
@@ -489,14 +502,20 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   auto load_q = [&](const Item& it) __attribute__((always_inline)) {
     const long long qrow = (VAR || DIL) ? (long long)it.row0 : (long long)it.b * C;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(a.q + (qrow * sh.Hq + 4 * it.kvh) * HD), (short)0,
-        (VAR || DIL) ? (it.len - 1) * (int)qrbd + QROWB : nrec_q, 0x00020000);
+        uniform_ptr(a.q + (qrow * sh.Hq + GH * it.kvh) * HD), (short)0,
+        (VAR || DIL) ? (it.len - 1) * (int)qrbd + GH * ROWB : nrec_q, 0x00020000);
     int ln_ = lane;   // (computed here, not held in registers across the loop)
     asm volatile("" : "+v"(ln_));
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int q = 8 * w + m;
-      dma16(rq, (it.t0 + q) * (int)qrbd + 16 * (ln_ ^ (q & 15)), lds_q + (unsigned)q * QROWB);
+      if constexpr (GQ < 4) {
+        // the chunk of stage position ln_: head ln_ / 16 mod GQ, swizzled
+        const int src = (((ln_ >> 4) & (GQ - 1)) << 4) | ((ln_ ^ q) & 15);
+        dma16(rq, (it.t0 + q) * (int)qrbd + 16 * src, lds_q + (unsigned)q * QROWB);
+      } else {
+        dma16(rq, (it.t0 + q) * (int)qrbd + 16 * (ln_ ^ (q & 15)), lds_q + (unsigned)q * QROWB);
+      }
     }
   };
 
@@ -573,7 +592,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
     const int tq = q0w + i;                 // this lane's query
     const int I = (DIL ? it.abs0 : s0) + dil * tq;   // its absolute position
-    const int h0 = kvh * 4 + QB * (w >> 2); // first query head of this wave
+    const int h0 = kvh * GH + QB * (w >> 2); // first query head of this wave
     // the next item, whose query rows go to the stage during this item
     const int Ln = item_at(round + 1);
     auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
@@ -897,7 +916,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
                            pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
         *reinterpret_cast<u32x2*>(row + 16 * (c ^ ii)) = val;
       }
-      if (a.lse && g == 0 && tq < it.len) {
+      if (a.lse && g == 0 && tq < it.len && (GQ >= 4 || QB * (w >> 2) + qb < GQ)) {
         const long long lo = VAR ? (long long)(h0 + qb) * a.vt.total + it.row0 + tq
                              : DIL ? ((long long)b * sh.Hq + h0 + qb) * C + (it.row0 - b * C) + dil * tq
                                    : ((long long)b * sh.Hq + h0 + qb) * C + tq;
@@ -908,11 +927,11 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     {
-      uint16_t* orow = a.out + (((VAR || DIL) ? (long long)it.row0 : (long long)b * C) * sh.Hq + 4 * kvh) * HD;
+      uint16_t* orow = a.out + (((VAR || DIL) ? (long long)it.row0 : (long long)b * C) * sh.Hq + GH * kvh) * HD;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int q = 8 * w + m;
-        if (t0 + q < it.len) {
+        if (t0 + q < it.len && (GQ >= 4 || (li_ >> 4) < GQ)) {   // (the repeated heads are not stored)
           const u32x4 v = *reinterpret_cast<const u32x4*>(qstage + q * QROWB + 16 * li_);
           *reinterpret_cast<u32x4*>(orow + (long long)(t0 + q) * dil * sh.Hq * HD + 8 * (li_ ^ (q & 15))) = v;
         }
@@ -1090,15 +1109,19 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.n_qtiles = (rows + BM - 1) / BM;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  long long n_items = (long long)a.n_qtiles * sh.Hkv * sh.B * (dil ? sh.dil : 1);
+  const int gq = sh.Hq / sh.Hkv;
+  if (sh.Hq != gq * sh.Hkv || (gq != 1 && gq != 2 && gq != 4 && gq != 8) || (dil && gq != 4))
+    return hipErrorInvalidValue;
+  const int nvh = gq == 8 ? 2 * sh.Hkv : sh.Hkv;   // items per (sequence, query tile)
+  long long n_items = (long long)a.n_qtiles * nvh * sh.B * (dil ? sh.dil : 1);
   if (vt) {
-    // items of sequence j: Hkv x its own query tiles, numbered after those of 0 .. j-1
+    // items of sequence j: nvh x its own query tiles, numbered after those of 0 .. j-1
     a.vt = *vt;
     a.vt.item_off[0] = 0;
     for (int j = 0; j < vt->n; ++j) {
       const int len = vt->row_off[j + 1] - vt->row_off[j];
       const int qt = (vt->skip_len1 && len == 1) ? 0 : (len + BM - 1) / BM;
-      const long long next = a.vt.item_off[j] + (long long)sh.Hkv * qt;
+      const long long next = a.vt.item_off[j] + (long long)nvh * qt;
       if (next > INT32_MAX) return hipErrorInvalidValue;
       a.vt.item_off[j + 1] = (int)next;
     }
@@ -1112,14 +1135,44 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   // one work-group per CU (a multiple of 8), each looping over its items
   const long long ncu = (long long)(device_cu_count() & ~7);
   const long long nwg = (ncu >= 8 && n_items > ncu) ? ncu : n_items;
-  if (vt)
-    prefill_bf16_d128_g4_kernel<true, false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
-  else if (dil)
-    prefill_bf16_d128_g4_kernel<false, true, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
-  else if ((a.kc == nullptr || aligned) && sh.n_sink == 0)
-    prefill_bf16_d128_g4_kernel<false, false, true><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
-  else
-    prefill_bf16_d128_g4_kernel<false, false, false><<<dim3((unsigned)nwg), dim3(NTHR), 0, st>>>(a);
+  const dim3 grid((unsigned)nwg), block(NTHR);
+  const bool nc = (a.kc == nullptr || aligned) && sh.n_sink == 0;
+  switch (gq) {
+    case 4:
+      if (vt)
+        prefill_bf16_d128_g4_kernel<true, false, false, 4><<<grid, block, 0, st>>>(a);
+      else if (dil)
+        prefill_bf16_d128_g4_kernel<false, true, false, 4><<<grid, block, 0, st>>>(a);
+      else if (nc)
+        prefill_bf16_d128_g4_kernel<false, false, true, 4><<<grid, block, 0, st>>>(a);
+      else
+        prefill_bf16_d128_g4_kernel<false, false, false, 4><<<grid, block, 0, st>>>(a);
+      break;
+    case 8:
+      if (vt)
+        prefill_bf16_d128_g4_kernel<true, false, false, 8><<<grid, block, 0, st>>>(a);
+      else if (nc)
+        prefill_bf16_d128_g4_kernel<false, false, true, 8><<<grid, block, 0, st>>>(a);
+      else
+        prefill_bf16_d128_g4_kernel<false, false, false, 8><<<grid, block, 0, st>>>(a);
+      break;
+    case 2:
+      if (vt)
+        prefill_bf16_d128_g4_kernel<true, false, false, 2><<<grid, block, 0, st>>>(a);
+      else if (nc)
+        prefill_bf16_d128_g4_kernel<false, false, true, 2><<<grid, block, 0, st>>>(a);
+      else
+        prefill_bf16_d128_g4_kernel<false, false, false, 2><<<grid, block, 0, st>>>(a);
+      break;
+    default:
+      if (vt)
+        prefill_bf16_d128_g4_kernel<true, false, false, 1><<<grid, block, 0, st>>>(a);
+      else if (nc)
+        prefill_bf16_d128_g4_kernel<false, false, true, 1><<<grid, block, 0, st>>>(a);
+      else
+        prefill_bf16_d128_g4_kernel<false, false, false, 1><<<grid, block, 0, st>>>(a);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -118,7 +118,7 @@ def test_prefill_tiny_fp32(W):
 
 
 PREFILL_CASES = [
-    # (B, Hq, Hkv, D, W, n_sink, dtype, chunks)  -- fast path: bf16, D=128, G=4
+    # (B, Hq, Hkv, D, W, n_sink, dtype, chunks)  -- fast path: bf16, D=128, groups of 1, 2, 4, 8
     (2, 8, 2, 128, 100, 0, torch.bfloat16, [130, 1, 3, 64, 100, 52]),
     (2, 8, 2, 128, 100, 4, torch.bfloat16, [130, 1, 3, 64, 100, 52]),
     (1, 4, 1, 128, 64, 0, torch.bfloat16, [200, 64, 65]),
@@ -134,6 +134,19 @@ PREFILL_CASES = [
     (2, 32, 8, 128, 16, 3, torch.bfloat16, [4100, 50]),
     # a global prefix longer than the window: 4 sink tiles, the last one ragged
     (2, 8, 2, 128, 64, 100, torch.bfloat16, [300, 77, 130]),
+    # other group sizes on the fast kernel: 8 (two items per KV head and
+    # query tile), 2 and 1 (the item's 4 heads repeat the group's), with and
+    # without sinks; Hq < 4 (a query row shorter than an item's 4 heads);
+    # more items than CUs
+    (2, 16, 2, 128, 100, 0, torch.bfloat16, [130, 1, 3, 64, 100, 52]),
+    (2, 16, 2, 128, 100, 4, torch.bfloat16, [130, 1, 64, 52]),
+    (2, 4, 2, 128, 100, 0, torch.bfloat16, [130, 1, 3, 64, 52]),
+    (2, 4, 2, 128, 100, 3, torch.bfloat16, [130, 1, 64]),
+    (2, 2, 2, 128, 100, 0, torch.bfloat16, [130, 1, 64, 52]),
+    (1, 1, 1, 128, 64, 2, torch.bfloat16, [200, 65]),
+    (1, 2, 1, 128, 64, 0, torch.bfloat16, [200, 65]),
+    (2, 64, 8, 128, 300, 0, torch.bfloat16, [1100, 1030]),
+    (2, 8, 8, 128, 300, 3, torch.bfloat16, [1100, 70]),
     # generic path
     (2, 4, 2, 64, 100, 0, torch.bfloat16, [130, 1, 70]),
     (1, 6, 2, 128, 50, 3, torch.float32, [90, 7, 40]),
@@ -182,10 +195,13 @@ ALIGNED_CASES = [
     (2, 8, 2, 128, 128, [256, 256, 77]),
     (2, 8, 2, 128, 100, [100, 100, 200, 37]),   # a window that is no multiple of the 32-key tile
     (1, 32, 8, 128, 4096, [4096, 4096]),
+    (2, 16, 2, 128, 128, [256, 256, 77]),        # groups of 8, 2 and 1
+    (2, 4, 2, 128, 100, [100, 100, 37]),
+    (2, 2, 2, 128, 128, [128, 128, 50]),
 ]
 
 
-@pytest.mark.parametrize("case", ALIGNED_CASES, ids=[f"B{c[0]}W{c[4]}" for c in ALIGNED_CASES])
+@pytest.mark.parametrize("case", ALIGNED_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}W{c[4]}" for c in ALIGNED_CASES])
 def test_prefill_chunk_aligned(case):
     """swa_prefill_chunk_aligned (the rolling buffer read in slot order) against
     swa_prefill_chunk chunk by chunk: out and LSE byte-identical, with the
@@ -246,7 +262,7 @@ def test_prefill_chunk_aligned_rejects_a_misaligned_start():
 WRITE_PREV_CASES = [(c, 0) for c in ALIGNED_CASES] + [((2, 8, 2, 128, 100, [100, 100, 37]), 3)]
 
 
-@pytest.mark.parametrize("case,S", WRITE_PREV_CASES, ids=[f"B{c[0]}W{c[4]}S{s}" for c, s in WRITE_PREV_CASES])
+@pytest.mark.parametrize("case,S", WRITE_PREV_CASES, ids=[f"B{c[0]}H{c[1]}/{c[2]}W{c[4]}S{s}" for c, s in WRITE_PREV_CASES])
 def test_prefill_chunk_aligned_write_prev(case, S):
     """swa_prefill_chunk_aligned_write_prev (the previous chunk's cache write
     and the next chunk's prefill, the write and the key rotation in one pass)
@@ -332,12 +348,14 @@ def test_prefill_without_cache_at_nonzero_start(D, S):
         assert_lse(lse[b], ref[b][1], latol, f"seq {b} lse")
 
 
-def test_prefill_key_counts_exact():
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (16, 2), (4, 2), (2, 2)])
+def test_prefill_key_counts_exact(Hq, Hkv):
     """A (near) zero softmax scale makes every weight exactly 1, so exp(lse)
     counts the keys each query attended: an end-to-end integer check of the
-    masks, the window edge, the sinks and the cache/chunk split."""
-    print("prefill key counts", flush=True)
-    B, Hq, Hkv, D, W, S = 2, 8, 2, 128, 100, 4
+    masks, the window edge, the sinks and the cache/chunk split, for every
+    query head (groups of 4, 8, 2 and 1)."""
+    print(f"prefill key counts Hq={Hq} Hkv={Hkv}", flush=True)
+    B, D, W, S = 2, 128, 100, 4
     gpu = GpuSide(B, Hq, Hkv, D, W, S, 10000.0, torch.bfloat16, scale=1e-30)
     t = 0
     for ci, C in enumerate([150, 70, 1, 130]):
@@ -383,6 +401,7 @@ DILATED_PREFILL = [
     (1, 8, 2, 128, 64, 100, 4, torch.bfloat16, [300, 77]),
     (2, 4, 2, 64, 90, 2, 5, torch.bfloat16, [140, 9]),
     (1, 6, 2, 128, 50, 3, 2, torch.float32, [90, 7, 40]),
+    (2, 16, 2, 128, 100, 0, 3, torch.bfloat16, [130, 3, 100]),   # a group of 8 (the fast kernel takes 4 dilated)
 ]
 
 
@@ -658,6 +677,11 @@ VARLEN_CASES = [
     # 16 one-token sequences x 8 KV heads x 2 ranges: the step's decode runs
     # 8 waves per work-group (one per CU) through the sequence map
     (17, 32, 8, 128, 4096, 0, torch.bfloat16, [1] * 16 + [100], [4100 + 61 * b for b in range(16)] + [4096]),
+    # other group sizes (8, 2, 1) through the varlen kernels and the mixed step
+    (5, 16, 2, 128, 100, 3, torch.bfloat16, [0, 1, 130, 64, 7], [0, 250, 40, 0, 300]),
+    (4, 4, 2, 128, 4096, 0, torch.bfloat16, [300, 1, 65, 129], [0, 70, 3, 0]),
+    (6, 2, 2, 128, 100, 3, torch.bfloat16, [1, 96, 96, 96, 1, 0], [40, 250, 0, 130, 7, 9]),
+    (4, 16, 2, 128, 4096, 0, torch.bfloat16, [129, 129, 1, 1], [0, 5000, 70, 4095]),
 ]
 
 
