@@ -14,7 +14,7 @@
 // combine pass merges the partials of each (sequence, query head):
 //   m* = max m_s,  l* = sum l_s 2^(m_s - m*),  o = sum o_s 2^(m_s - m*) / l*.
 //
-// Fast kernel (bf16, head_dim 128, GQA group 4; also 1, 2 and 8, see below):
+// Fast kernel (bf16, head_dim 128, GQA group 4):
 //  * A wave takes 32 slots at a time.  K goes global -> LDS directly (buffer
 //    loads with the lds modifier), 16 lanes per whole 256-byte row, into a
 //    per-wave double buffer, and is read back in the A-operand layout of

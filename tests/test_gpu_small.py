@@ -682,6 +682,9 @@ VARLEN_CASES = [
     (4, 4, 2, 128, 4096, 0, torch.bfloat16, [300, 1, 65, 129], [0, 70, 3, 0]),
     (6, 2, 2, 128, 100, 3, torch.bfloat16, [1, 96, 96, 96, 1, 0], [40, 250, 0, 130, 7, 9]),
     (4, 16, 2, 128, 4096, 0, torch.bfloat16, [129, 129, 1, 1], [0, 5000, 70, 4095]),
+    # a run longer than the window (only its last W tokens reach the cache)
+    # whose write rides on the one-split decode launch
+    (5, 8, 2, 128, 64, 0, torch.bfloat16, [1, 100, 100, 1, 1], [30, 200, 0, 64, 7]),
 ]
 
 
