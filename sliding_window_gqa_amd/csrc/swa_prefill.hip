@@ -197,11 +197,15 @@ struct PrefillArgs {
 // 8192-token layer, 3-3.5% on a chunk that reads the cache.
 //
 // GQ, the query heads per KV head (1, 2, 4 or 8; DIL takes 4 only): an item
-// always holds 4 query heads.  With 8, a KV head has two items per query tile
+// always holds 4 query columns of 64 positions (the 4 "heads" of the stage
+// and of the waves).  With 8, a KV head has two items per query tile
 // (virtual heads 2 kvh and 2 kvh + 1, query heads 8 kvh .. +3 and +4 .. +7),
-// which read the same K/V rows.  With 1 or 2, the item's 4 heads are the
-// group's heads repeated (head h of the item loads query head h mod GQ), and
-// only the first GQ are stored: 4 / GQ times the matrix work of the group.
+// which read the same K/V rows.  With 2, an item covers 128 positions of the
+// group's 2 heads: column c is head c & 1 at positions t0 + 64 (c >> 1) ..,
+// so waves 4..7 take the second 64 positions (their masks and band edges
+// follow from their own positions; the item's tiles cover both blocks).
+// With 1, the item's 4 columns are the group's head repeated and only the
+// first is stored: 4 times the matrix work of the head.
 template <bool VAR, bool DIL, bool NC, int GQ>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_d128_g4_kernel(PrefillArgs a) {
@@ -209,6 +213,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   static_assert(GQ == 4 || !DIL, "a dilated window takes groups of 4");
   constexpr int GH = GQ < 4 ? GQ : 4;    // distinct query heads of an item
   constexpr int VS = GQ == 8 ? 1 : 0;    // items per (KV head, query tile): 1 << VS
+  constexpr int PS = GQ == 2 ? 2 : 1;    // blocks of 64 positions per item
+  constexpr int BMI = BM * PS;           // query positions per item
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * RINGB];
   __shared__ __attribute__((aligned(16))) uint8_t qstage[BM * QROWB];
   __shared__ double rope_rev[kMaxPairs];
@@ -289,10 +295,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       it.b = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(io_ <= L)));
       it.row0 = a.vt.row_off[it.b];
       it.len = a.vt.row_off[it.b + 1] - it.row0;
-      const int nqt = (it.len + BM - 1) / BM;
+      const int nqt = (it.len + BMI - 1) / BMI;
       const int rem = L - a.vt.item_off[it.b];
       it.kvh = rem / nqt;
-      it.t0 = (nqt - 1 - (rem - it.kvh * nqt)) * BM;
+      it.t0 = (nqt - 1 - (rem - it.kvh * nqt)) * BMI;
     } else if (DIL) {
       // residue rho of sequence b: chunk rows r0, r0 + dil, ... (positions
       // = rho mod dil), decimated indices from s0 = (s0_abs + r0 - rho) / dil
@@ -314,19 +320,19 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
       it.b = L / per_b;
       const int rem = L - it.b * per_b;
       it.kvh = rem / a.n_qtiles;
-      it.t0 = (a.n_qtiles - 1 - (rem - it.kvh * a.n_qtiles)) * BM;
+      it.t0 = (a.n_qtiles - 1 - (rem - it.kvh * a.n_qtiles)) * BMI;
       it.row0 = it.b * C;
       it.len = C;
     }
     if (!DIL) it.s0 = start_c[it.b];
     it.sa = a.kc ? it.s0 : 0;
-    const int tq_last = min(it.t0 + BM, it.len) - 1;
+    const int tq_last = min(it.t0 + BMI, it.len) - 1;
     // sink tiles: some readable sink lies outside the window of some query
     it.n_stile = (!DIL && nsink > it.s0 - it.sa && tq_last - W + it.sa >= 0) ? (nsink + BN - 1) / BN : 0;
     const int k_lo = -((Wb - 1 + BN - 1) / BN);
     const int k_clip = -((it.sa + it.t0 + BN - 1) / BN);
     it.kmin = max(k_lo, k_clip);
-    it.n_tiles = it.n_stile + (2 - it.kmin);
+    it.n_tiles = it.n_stile + (BMI / BN - it.kmin);
     return it;
   };
 
@@ -509,7 +515,11 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int q = 8 * w + m;
-      if constexpr (GQ < 4) {
+      if constexpr (PS == 2) {
+        // stage column ln_ / 16 = c: head c & 1 at position t0 + q + 64 (c >> 1)
+        const int src = (((ln_ >> 4) & 1) << 4) | ((ln_ ^ q) & 15);
+        dma16(rq, (it.t0 + q + 64 * (ln_ >> 5)) * (int)qrbd + 16 * src, lds_q + (unsigned)q * QROWB);
+      } else if constexpr (GQ < 4) {
         // the chunk of stage position ln_: head ln_ / 16 mod GQ, swizzled
         const int src = (((ln_ >> 4) & (GQ - 1)) << 4) | ((ln_ ^ q) & 15);
         dma16(rq, (it.t0 + q) * (int)qrbd + 16 * src, lds_q + (unsigned)q * QROWB);
@@ -555,7 +565,8 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   // directly.
   bf16x8 qf[QB][4];
   auto load_qf = [&](const Item& it) __attribute__((always_inline)) {
-    const int I = (DIL ? it.abs0 : it.s0) + dil * (it.t0 + 16 * (w & 3) + i);   // the lane's query position
+    // the lane's query position (PS = 2: waves 4..7 take the item's second 64)
+    const int I = (DIL ? it.abs0 : it.s0) + dil * (it.t0 + (PS == 2 ? 64 * (w >> 2) : 0) + 16 * (w & 3) + i);
     // (the asm keeps the table addresses from being computed once for all
     // items and held in registers)
     int gi = g;
@@ -589,10 +600,10 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
   for (int round = 0;; ++round) {
     const int b = it.b, kvh = it.kvh, t0 = it.t0, s0 = it.s0, sa = it.sa;
     const int n_stile = it.n_stile, kmin = it.kmin, n_tiles = it.n_tiles;
-    const int q0w = t0 + 16 * (w & 3);      // first query of this wave (chunk-relative)
+    const int q0w = t0 + (PS == 2 ? 64 * (w >> 2) : 0) + 16 * (w & 3);   // first query of this wave (chunk-relative)
     const int tq = q0w + i;                 // this lane's query
     const int I = (DIL ? it.abs0 : s0) + dil * tq;   // its absolute position
-    const int h0 = kvh * GH + QB * (w >> 2); // first query head of this wave
+    const int h0 = kvh * GH + (PS == 2 ? 0 : QB * (w >> 2)); // first query head of this wave
     // the next item, whose query rows go to the stage during this item
     const int Ln = item_at(round + 1);
     auto band_u0 = [&](int t) __attribute__((always_inline)) { return t0 + BN * (kmin + t - n_stile); };
@@ -916,7 +927,7 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
                            pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv)};
         *reinterpret_cast<u32x2*>(row + 16 * (c ^ ii)) = val;
       }
-      if (a.lse && g == 0 && tq < it.len && (GQ >= 4 || QB * (w >> 2) + qb < GQ)) {
+      if (a.lse && g == 0 && tq < it.len && (GQ >= 4 || PS == 2 || QB * (w >> 2) + qb < GQ)) {
         const long long lo = VAR ? (long long)(h0 + qb) * a.vt.total + it.row0 + tq
                              : DIL ? ((long long)b * sh.Hq + h0 + qb) * C + (it.row0 - b * C) + dil * tq
                                    : ((long long)b * sh.Hq + h0 + qb) * C + tq;
@@ -931,7 +942,15 @@ prefill_bf16_d128_g4_kernel(PrefillArgs a) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int q = 8 * w + m;
-        if (t0 + q < it.len && (GQ >= 4 || (li_ >> 4) < GQ)) {   // (the repeated heads are not stored)
+        if constexpr (PS == 2) {
+          // stage column li_ / 16 = c: head c & 1 at position t0 + q + 64 (c >> 1)
+          const int row = t0 + q + 64 * (li_ >> 5);
+          if (row < it.len) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qstage + q * QROWB + 16 * li_);
+            *reinterpret_cast<u32x4*>(orow + (long long)row * sh.Hq * HD + 128 * ((li_ >> 4) & 1) +
+                                      8 * ((li_ ^ q) & 15)) = v;
+          }
+        } else if (t0 + q < it.len && (GQ >= 4 || (li_ >> 4) < GQ)) {   // (the repeated heads are not stored)
           const u32x4 v = *reinterpret_cast<const u32x4*>(qstage + q * QROWB + 16 * li_);
           *reinterpret_cast<u32x4*>(orow + (long long)(t0 + q) * dil * sh.Hq * HD + 8 * (li_ ^ (q & 15))) = v;
         }
@@ -1106,12 +1125,13 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
   a.C = C;
   const bool dil = sh.dil > 1 && !vt;   // (the API sends dilated varlen batches to the generic kernel)
   const int rows = dil ? (C + sh.dil - 1) / sh.dil : C;   // the longest residue's rows
-  a.n_qtiles = (rows + BM - 1) / BM;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse = lse;
   const int gq = sh.Hq / sh.Hkv;
   if (sh.Hq != gq * sh.Hkv || (gq != 1 && gq != 2 && gq != 4 && gq != 8) || (dil && gq != 4))
     return hipErrorInvalidValue;
+  const int bmi = gq == 2 ? 2 * BM : BM;   // query positions per item (a group of 2: two blocks)
+  a.n_qtiles = (rows + bmi - 1) / bmi;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
   const int nvh = gq == 8 ? 2 * sh.Hkv : sh.Hkv;   // items per (sequence, query tile)
   long long n_items = (long long)a.n_qtiles * nvh * sh.B * (dil ? sh.dil : 1);
   if (vt) {
@@ -1120,7 +1140,7 @@ hipError_t launch_prefill_bf16_d128_g4(const Shape& sh, const RopeTab& rt, const
     a.vt.item_off[0] = 0;
     for (int j = 0; j < vt->n; ++j) {
       const int len = vt->row_off[j + 1] - vt->row_off[j];
-      const int qt = (vt->skip_len1 && len == 1) ? 0 : (len + BM - 1) / BM;
+      const int qt = (vt->skip_len1 && len == 1) ? 0 : (len + bmi - 1) / bmi;
       const long long next = a.vt.item_off[j] + (long long)nvh * qt;
       if (next > INT32_MAX) return hipErrorInvalidValue;
       a.vt.item_off[j + 1] = (int)next;
