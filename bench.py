@@ -382,9 +382,56 @@ def main():
     if not args.no_cpu_baseline and args.only in ("prefill", "all"):
         result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), W, wl.rope_theta, args.cpu_seconds)
 
+    if args.only == "all":
+        result["device"] = device_info(torch, dev)
     result["host"] = {"cpu": cpu_model(), "os_cpu_count": os.cpu_count(),
                       "affinity_cpus": len(os.sched_getaffinity(0))}
     print(json.dumps(result), flush=True)
+
+
+def device_info(torch, dev, nbytes=1 << 30, reps=10):
+    """The GPU as the runtime reports it, the matrix peak its CU count and
+    clock give, and a measured device-to-device copy: the achievable HBM line
+    the decode and write rates can also be read against."""
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "hbm_bytes": props.total_memory}
+    clock_khz = None
+    try:   # hipDeviceAttributeClockRate (kHz) from the HIP runtime torch already loaded
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        attr = 5   # hipDeviceAttributeClockRate
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev.index or 0) == 0 and v.value > 0:
+            clock_khz = v.value
+    except OSError:
+        pass
+    if clock_khz:
+        info["max_clock_mhz"] = clock_khz / 1e3
+        # bf16 dense MFMA: 4096 flops per clock per CU
+        info["bf16_peak_at_max_clock_tflops"] = round(props.multi_processor_count * clock_khz * 1e3 * 4096 / 1e12, 1)
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    med = times[len(times) // 2]
+    info["copy_1gib"] = {"median_ms": round(med, 4), "gbps": round(2 * nbytes / (med * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(2 * nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "note": "device-to-device copy of 1 GiB, bytes read + written; the achievable "
+                                 "streaming rate on this box"}
+    del src, dst
+    return info
 
 
 def decode_layers(swa, synth, torch, dev, n_layers=32, tokens=16):
