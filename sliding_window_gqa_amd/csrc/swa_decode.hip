@@ -171,40 +171,51 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
   if (tid < kMaxPairs) rope_rev[tid] = a.rt.rev[tid];
   __syncthreads();
 
-  // ---- fused step: the range that holds slot(p) first stores the new entry
-  // of this head (key rotated at p, as the cache write does it; value as
-  // is).  No other work-group reads that slot.  The stores complete before
-  // the barrier, so every load of the work-group issued after it sees them.
-  if (a.knew != nullptr) {
-    const int slot = slot_of(p, sh.W, sh.n_sink);
-    const int vp = DIL ? (p < nsink ? p : nsink) : slot;   // the range that holds p
-    if (vp >= sp0 && vp < sp0 + a.split_len) {
-      if (tid < 32) {
-        const int c = tid & 15;   // 16-byte chunk: head-dim elements 8c .. 8c+7
-        const long long src = ((long long)r * sh.Hkv + kvh) * HD + 8 * c;
-        const long long dst = ((long long)b * S + slot) * row_stride + kvh * HD + 8 * c;
-        if (tid < 16) {
-          const u32x4 wk = *reinterpret_cast<const u32x4*>(a.knew + src);
-          u32x4 r;
+  // ---- fused step: the range that holds slot(p) stores the new entry of
+  // this head (key rotated at p, as the cache write does it; value as is).
+  // No other work-group reads that slot.  Without dilation the store is not
+  // waited for: the wave whose chunk holds the slot reads the row from
+  // memory like any other (old or new contents, whichever arrives) and then
+  // overwrites it with the new entry, in LDS (K) and in its V registers,
+  // before the products use it.  Lane (i, g) holds chunk i (head-dim
+  // 8i .. 8i+7) of the new key (rotated) and value.
+  const int vp = DIL ? (p < nsink ? p : nsink) : slot_of(p, sh.W, sh.n_sink);   // the key that is p
+  const bool holder = a.knew != nullptr && vp >= sp0 && vp < sp0 + a.split_len;
+  u32x4 knw = {0u, 0u, 0u, 0u}, vnw = {0u, 0u, 0u, 0u};
+  if (holder) {
+    const long long src = ((long long)r * sh.Hkv + kvh) * HD + 8 * i;
+    knw = *reinterpret_cast<const u32x4*>(a.knew + src);
+    vnw = *reinterpret_cast<const u32x4*>(a.vnew + src);
+  }
+  // Rotate the new key and store the entry: wave 0, lanes g = 0 the key,
+  // g = 1 the value.  Without dilation this runs once the stream's first
+  // loads are out and nothing waits for it.  With dilation the keys past the
+  // live range read the row of the last live key (masked, but their values
+  // must be finite), which can be the new entry: there the store completes
+  // before the first load, as in the separate cache write.
+  auto store_new = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float x0 = bf16_lo(wk[jj]), x1 = bf16_hi(wk[jj]);
-            if (sh.rope) {
-              float cs, sn;
-              rope_cs(p, rope_rev[4 * c + jj], cs, sn);
-              rotate(x0, x1, cs, sn);
-            }
-            r[jj] = pack_bf16(x0, x1);
-          }
-          *reinterpret_cast<u32x4*>(a.kdst + dst) = r;
-        } else {
-          *reinterpret_cast<u32x4*>(a.vdst + dst) =
-              *reinterpret_cast<const u32x4*>(a.vnew + src);
-        }
+    for (int jj = 0; jj < 4; ++jj) {
+      float x0 = bf16_lo(knw[jj]), x1 = bf16_hi(knw[jj]);
+      if (sh.rope) {
+        float cs, sn;
+        rope_cs(p, rope_rev[4 * i + jj], cs, sn);
+        rotate(x0, x1, cs, sn);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      knw[jj] = pack_bf16(x0, x1);
     }
+    if (tid < 32) {
+      const long long dst = ((long long)b * S + slot_of(p, sh.W, sh.n_sink)) * row_stride + kvh * HD + 8 * i;
+      if (tid < 16)
+        *reinterpret_cast<u32x4*>(a.kdst + dst) = knw;
+      else
+        *reinterpret_cast<u32x4*>(a.vdst + dst) = vnw;
+    }
+  };
+  if (DIL && holder) {
+    store_new();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
   bf16x8 qf[4];
   auto load_q = [&]() __attribute__((always_inline)) {
@@ -347,6 +358,18 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[db], 0, 0, 0);
     }
   };
+  // The chunk row rr (0..31) that is the new entry: its K row in this
+  // wave's LDS buffer (chunk i at i ^ dkswz(rr), written by lanes g = 0 once
+  // the chunk's loads have landed) and its V row, which sits in register
+  // e of the lanes g (rows 4g+e, then 16+4g+e-4, as load_v places them).
+  auto put_new = [&](int rr, int buf, u32x4 (&vr)[8]) __attribute__((always_inline)) {
+    if (g == 0)
+      *reinterpret_cast<u32x4*>(kvs + (w * 2 + buf) * DTILE + rr * DROWB + 16 * (i ^ dkswz(rr))) = knw;
+    const int gt = (rr & 15) >> 2, et = (rr & 3) + (rr >= 16 ? 4 : 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e == et && g == gt) vr[e] = vnw;
+  };
   // Each wave takes chunks c0, c0 + 4*kChunk, ... of the range; the next
   // chunk's 16 loads go out before the current chunk is computed (past the
   // range they read zeros).  The buffer a load fills was last read by the
@@ -365,10 +388,12 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
       load_v(c0 + cstep, vB);
     }
     load_q();
+    if (!DIL && holder) store_new();
     int buf = 0;
     while (c0 < vend) {
       dma_chunk(c0 + cstep, buf ^ 1);
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      if (!DIL && holder && (unsigned)(vp - c0) < (unsigned)kChunk) put_new(vp - c0, buf, vA);
       do_chunk(c0, buf, vA);
       load_v(c0 + 2 * cstep, vA);
       c0 += cstep;
@@ -376,6 +401,7 @@ __global__ void __launch_bounds__(64 * NW, 2) decode_bf16_d128_g4_kernel(DecodeA
       if (c0 >= vend) break;
       dma_chunk(c0 + cstep, buf ^ 1);
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      if (!DIL && holder && (unsigned)(vp - c0) < (unsigned)kChunk) put_new(vp - c0, buf, vB);
       do_chunk(c0, buf, vB);
       load_v(c0 + 2 * cstep, vB);
       c0 += cstep;
