@@ -324,9 +324,10 @@ int swa_decode(const swa_params* params, const void* q, const void* k_cache, con
  * swa_decode.  With bf16, head_dim 128 and 1, 2, 4 or 8 query heads per KV
  * head (4 with a dilated window) this is one launch (plus the combine when
  * the slots are split over several ranges): the work-group whose slot range
- * holds slot(pos[b]) stores the entry before it streams its range, and every
- * K/V byte it reads serves all query heads of its KV head.  Other shapes run
- * the two calls.
+ * holds slot(pos[b]) stores the entry and attends to the new key and value
+ * from its own registers rather than to what it reads back from that slot,
+ * and every K/V byte it reads serves all query heads of its KV head.  Other
+ * shapes run the two calls.
  *   q       : [batch][n_q_heads][head_dim] raw queries.
  *   k, v    : [batch][n_kv_heads][head_dim] raw new key / value of the token
  *             at pos[b] (the key is rotated here, the value stored as is).
